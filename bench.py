@@ -1,0 +1,197 @@
+"""Benchmark: one MI355X forward pass through the routed grouped-GEMM MoE layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral]
+
+A step is one moe_layer call (route, permute, persistent expert-FFN + combine)
+over the seeded synthetic Mixtral-shape batch (T=4096, d=4096, f=14336, E=8,
+top-2), inputs resident in HBM.  W untimed steps, then K timed steps between
+two device synchronisations.  Prints one JSON line with the layer throughput
+(tokens/s), the grouped-GEMM TFLOP/s of the persistent kernel, its roofline
+entry and the CPU oracle timed on a bounded sample of the same workload.
+
+--mode copy runs a plain device-to-device copy of known size (used to scale
+the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_kernel_mixtral_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "routed_grouped_gemm_moe_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(os.path.basename(p).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the persistent kernel from the committed counter
+    summary, or None if absent or taken from different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_mode(args) -> None:
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": args.steps}), flush=True)
+
+
+def cpu_baseline(cfg, arrs, n_tokens: int):
+    import numpy as np
+    import oracle
+    toks = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"], arrs["w_up"],
+                        arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi, bias=arrs["bias"])
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_tokens} evenly spaced tokens of the same {cfg.name} batch, each routed "
+                      f"and run through its {cfg.k} selected experts' float64 SwiGLU and combine "
+                      f"({dt:.1f} s)"}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--mode", default="layer", choices=["layer", "copy"])
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.mode == "copy":
+        copy_mode(args)
+        return
+
+    import moe_workloads as W
+    import routed_grouped_gemm_moe_amd as M
+
+    cfg = W.CONFIGS[args.config]
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    arrs = W.generate(cfg)
+    dev = lambda v: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to("cuda").view(
+        torch.bfloat16)
+    x, wr = dev(arrs["x"]), dev(arrs["w_router"])
+    wg, wu, wd = dev(arrs["w_gate"]), dev(arrs["w_up"]), dev(arrs["w_down"])
+    bias = torch.from_numpy(arrs["bias"]).to("cuda") if arrs["bias"] is not None else None
+    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
+                      device="cuda")
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+
+    def step():
+        M.moe_layer(D, x, wr, wg, wu, wd, bias=bias, out=out, out_dtype=dt, topk_ids_out=ids,
+                    topk_w_out=gates, ws=ws)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if M.moe_device_status(D, ws) != 0:
+        raise RuntimeError("device status not OK after warmup")
+
+    # local rows (all T*k for a full-local config)
+    ids_h = ids.cpu().numpy()
+    n_local = int(((ids_h >= cfg.e_lo) & (ids_h < cfg.E_hi)).sum())
+    flops = 6.0 * cfg.d * cfg.f * n_local   # Weave §3.1: 6*H*I per token-expert pair
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    M.moe_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_ev, (route_ms, perm_ms, ffn_ms) = M.moe_timing_read()
+    M.moe_timing_enable(False)
+    if M.moe_device_status(D, ws) != 0:
+        raise RuntimeError("device status not OK after timed steps")
+
+    elapsed = t1 - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = cfg.T * args.steps / elapsed
+    ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12 if ffn_ms > 0 else 0.0
+    layer_tflops = flops / (ms_per_step * 1e-3) / 1e12
+    traffic = read_traffic()
+
+    rec = {
+        "metric": "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA bf16 peak), 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian activations and weights, Gaussian router)",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi],
+                   "parallelism": "none (one GPU)"},
+        "grouped_gemm_tflops": round(ffn_tflops, 2),
+        "grouped_gemm_pct_mfma_peak": round(100 * ffn_tflops / PEAK_BF16_TFLOPS, 2),
+        "layer_tflops": round(layer_tflops, 2),
+        "stages_ms": {"route": round(route_ms, 4), "permute": round(perm_ms, 4),
+                      "expert_ffn_combine_persistent": round(ffn_ms, 4), "events": n_ev},
+        "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "layer_kernel (persistent gate/up, down, combine tiles)",
+                     "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({args.cpu_tokens} tokens)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, arrs, args.cpu_tokens)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed grouped-GEMM MoE layer.
+ *
+ * One GPU's forward pass through an expert-parallel MoE layer, split into the
+ * stages of Weave ("Fine-Grained Dynamic SM Scheduling in an MoE Megakernel",
+ * §2.1 and Figure 3): top-k gating, dispatch into expert-contiguous buffers,
+ * GEMM0 (gate and up projections) with the SiLU-multiply activation, GEMM1
+ * (down projection), and the gate-weighted combine back to token order.
+ * moe_layer runs all of them; its expert GEMMs and combine are one persistent
+ * kernel that claims tiles with atomic counters in dependency order (Weave §4)
+ * and lets combine tiles start as soon as device-side flags say the down
+ * tiles they read are complete (tile-level signaling: Cui et al., "Fine-grained
+ * Computation-Communication Overlap via Tile-level Signaling and Scheduling
+ * for Mixture-of-Experts", abstract).
+ *
+ * Conventions for every call:
+ *  - Data pointers are DEVICE pointers, owned by the caller, and must stay
+ *    valid until the enqueued work completes.  `stream` is a hipStream_t
+ *    (NULL = the default stream).  Calls only enqueue work; none synchronises
+ *    with the host.  The library allocates no device memory per call: callers
+ *    pass a workspace of at least *_workspace_bytes(dims) bytes, 256-byte
+ *    aligned.
+ *  - bf16 tensors are raw bf16 bit patterns (uint16), row-major.  Weights are
+ *    stored [out][in] (each output unit's weights contiguous):
+ *        w_router [E, d], w_gate [E_loc, f, d], w_up [E_loc, f, d],
+ *        w_down [E_loc, d, f].
+ *  - Local experts are [e_lo, e_hi); E_loc = e_hi - e_lo.  Weight tensors
+ *    hold only the local experts.  Rows routed to other experts are skipped
+ *    (their gates still come from the global top-k).
+ *  - Host-side argument checks run before anything is enqueued; a call that
+ *    returns an error has enqueued nothing.  Errors found on the device (a
+ *    bounded flag wait that timed out) are recorded in the workspace and read
+ *    with moe_device_status.
+ *  - Calls on distinct workspaces are independent; calls sharing a workspace
+ *    must be ordered on one stream.
+ *
+ * Routing arithmetic (the pages do not define the gate function; this library
+ * fixes it so that ids are reproducible bit for bit): logit[t,e] is a float32
+ * sum over 16 equal contiguous chunks of the hidden dimension, each chunk
+ * summed sequentially from +0 in ascending index, the 16 chunk sums combined
+ * by a balanced pairwise tree ((s0+s1)+(s2+s3))+..., then the optional bias
+ * added.  The k largest logits are selected (ties to the lower expert id) and
+ * listed by (logit descending, id ascending); the gates are the softmax over
+ * the selected logits.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,    /* null pointer, inconsistent dims */
+    MOE_ERR_UNSUPPORTED = -2,    /* dims outside what the kernels support */
+    MOE_ERR_WORKSPACE = -3,      /* workspace null, misaligned or too small */
+    MOE_ERR_HIP = -4,            /* a HIP runtime call or launch failed */
+    MOE_ERR_DEVICE_TIMEOUT = -5  /* a device-side flag wait exceeded its bound */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* Problem size.  T tokens of hidden size d, expert FFN size f, E experts in
+ * the router, top-k, local experts [e_lo, e_hi).
+ * Supported: T >= 0, 1 <= k <= E <= 1024, 0 <= e_lo < e_hi <= E,
+ * d % 256 == 0, f % 128 == 0, T*k < 2^31. */
+typedef struct {
+    int64_t T, d, f, E, k, e_lo, e_hi;
+} moe_dims;
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_string(moe_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int moe_version(void);
+
+/* ---- moe_route: top-k gating (Weave §2.1: each token selects its experts
+ * through a learned gate; Figure 3 shows top-k routing).
+ *   x        bf16 [T, d]       activations
+ *   w_router bf16 [E, d]       router weight
+ *   bias     f32  [E] or NULL  added to every logit (after the dot product)
+ *   topk_ids i32  [T, k]  out  selected expert ids, by (logit desc, id asc)
+ *   topk_w   f32  [T, k]  out  renormalised softmax gates of those experts
+ *   logits   f32  [T, E]  out, optional (NULL to skip)
+ */
+moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
+                     int32_t *topk_ids, float *topk_w, float *logits, void *stream);
+
+/* ---- moe_permute: dispatch into expert-contiguous rows (Weave §2.1 stage
+ * 1, Figure 3; on one GPU the "send" is a gather; each source row is read
+ * once, as with Weave's dispatch-side deduplication, §4).
+ *   x         bf16 [T, d]          activations
+ *   topk_ids  i32  [T, k]          from moe_route (global expert ids)
+ *   counts    i32  [E_loc]    out  rows per local expert
+ *   offsets   i32  [E_loc+1]  out  exclusive prefix of counts; offsets[E_loc] = N
+ *   perm_src  i32  [T*k]      out  source token of each row (first N valid)
+ *   inv_perm  i32  [T, k]     out  row of each (token, slot); -1 if not local
+ *   x_perm    bf16 [T*k, d]   out  x_perm[r] = x[perm_src[r]] (first N valid)
+ * Rows inside an expert segment are in ascending source-token order.
+ */
+size_t moe_permute_workspace_bytes(const moe_dims *dims);
+moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_ids,
+                       int32_t *counts, int32_t *offsets, int32_t *perm_src, int32_t *inv_perm,
+                       void *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- moe_expert_ffn: grouped SwiGLU expert FFN over expert-contiguous rows
+ * (Weave §2.1 stages 2-4: GEMM0 up+gate, SiLU followed by element-wise
+ * multiplication, GEMM1 down; FLOP count 6*d*f per row, Weave §3.1).
+ *   x_perm  bf16 [T*k, d]      rows, expert-contiguous (first offsets[E_loc])
+ *   offsets i32  [E_loc+1]     device-resident segment offsets
+ *   w_gate, w_up bf16 [E_loc, f, d];  w_down bf16 [E_loc, d, f]
+ *   y_perm  bf16 [T*k, d] out  y = (silu(x Wg^T) * (x Wu^T)) Wd^T per row
+ * The intermediate h is rounded to bf16; accumulation is float32.
+ */
+size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims);
+moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                          const void *w_gate, const void *w_up, const void *w_down, void *y_perm,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* ---- moe_combine: gate-weighted sum back to token order (Weave §2.1 stage 5).
+ *   y_perm   bf16 [T*k, d]  expert outputs by row
+ *   inv_perm i32  [T, k]    row of each (token, slot), -1 = skip
+ *   topk_w   f32  [T, k]    gates
+ *   out      [T, d]   out   bf16 (round to nearest even) or f32 per out_dtype;
+ *                           out[t] = sum over slots j ascending with
+ *                           inv_perm >= 0 of topk_w[t,j] * y_perm[row], in f32;
+ *                           tokens with no local slot get 0.
+ */
+moe_status moe_combine(const moe_dims *dims, const void *y_perm, const int32_t *inv_perm,
+                       const float *topk_w, void *out, moe_dtype out_dtype, void *stream);
+
+/* ---- moe_layer: the whole forward pass.  Route, permute, then one
+ * persistent kernel whose workgroups claim gate/up tiles, then down tiles,
+ * then combine tiles from per-XCD atomic queues (Weave §4: tiles claimed by
+ * atomicAdd in the pipeline's dependency order).  A down tile waits on a
+ * per-row-block counter of finished gate/up tiles; each finished down tile
+ * releases a flag that the combine tiles reading it acquire.
+ *   out          [T, d] bf16 or f32 (f32 for an expert-parallel partial)
+ *   topk_ids_out i32 [T,k], topk_w_out f32 [T,k]: optional copies of routing
+ */
+size_t moe_layer_workspace_bytes(const moe_dims *dims);
+moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
+                     const void *w_gate, const void *w_up, const void *w_down, void *out,
+                     moe_dtype out_dtype, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Synchronises `stream`, then reads the device status word that moe_layer
+ * keeps in `ws` (MOE_OK, or MOE_ERR_DEVICE_TIMEOUT if a flag wait gave up). */
+moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_bytes, void *stream);
+
+/* ---- Stage timing (measurement aid).  When enabled, moe_layer records HIP
+ * events on its stream around each of its launches; moe_timing_read
+ * synchronises and returns the average milliseconds per call of each stage
+ * since the last enable: [0] route, [1] permute (all its kernels), [2] the
+ * persistent expert-FFN + combine kernel.  Returns the number of calls
+ * averaged.  Not thread-safe; for benchmarking only. */
+void moe_timing_enable(int on);
+int moe_timing_read(float *stage_ms, int n_stages);
+
+/* Timeout of each device-side flag wait of moe_layer, in microseconds
+ * (default 2 s; values < 1 restore the default).  A wait that times out
+ * records MOE_ERR_DEVICE_TIMEOUT and makes every other wait of that launch
+ * return at once, so the launch still drains.  Used by tests to exercise the
+ * timeout path. */
+void moe_set_wait_timeout_us(int64_t us);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -67,12 +67,18 @@ def _load():
         lib.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         lib.oracle_layer_tokens.argtypes = [i64, vp, i64, i64, i64, i64, i64, i64, i64, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_num_threads.restype = C.c_int
         for name in ("oracle_router_logits", "oracle_router_logits_f64", "oracle_topk_gates",
                      "oracle_route", "oracle_permute", "oracle_expert_rows", "oracle_combine",
                      "oracle_layer_tokens"):
             getattr(lib, name).restype = C.c_int
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return int(_load().oracle_num_threads())
 
 
 def _p(a: Optional[np.ndarray]):

@@ -54,6 +54,13 @@ static inline float bf(uint16_t h) {
 
 int oracle_version(void) { return 1; }
 
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif
+
 /* ---------------------------------------------------------------- routing */
 
 /* One router logit in the defined float32 order (see header). d % 16 == 0. */

@@ -1,0 +1,288 @@
+"""Python binding of the MI355X routed grouped-GEMM MoE library (gfx950 HIP).
+
+Thin ctypes marshalling over the C ABI in include/moe.h: the functions below
+carry the same names as the C entry points, take torch tensors that already
+live on the GPU, pass their data pointers and the current HIP stream, and
+raise on a non-OK status.  Every step of the computation runs in the HIP
+kernels of libmoe_mi355x.so; torch only provides device memory and streams.
+Output tensors that are not passed in are allocated here with torch.
+
+If the shared library has not been built, every call raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Optional, Tuple
+
+__all__ = [
+    "MoEDims", "lib_path", "load", "exported_abi_names", "header_abi_names",
+    "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+    "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
+    "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
+    "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "MoEError",
+    "MOE_BF16", "MOE_F32",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
+
+MOE_BF16, MOE_F32 = 0, 1
+_STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_TIMEOUT"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({status})")
+
+
+class MoEDims(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("T", "d", "f", "E", "k", "e_lo", "e_hi")]
+
+    @classmethod
+    def make(cls, T, d, f, E, k, e_lo=0, e_hi=None) -> "MoEDims":
+        return cls(int(T), int(d), int(f), int(E), int(k), int(e_lo),
+                   int(E if e_hi is None else e_hi))
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+_lib = None
+
+
+def load():
+    """Load the shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        raise ImportError(f"{_LIB} is missing: build it with "
+                          "`python -m routed_grouped_gemm_moe_amd.build` (no fallback exists)")
+    lib = C.CDLL(_LIB)
+    vp, i32, i64, sz, dp = C.c_void_p, C.c_int, C.c_int64, C.c_size_t, C.POINTER(MoEDims)
+    sig = {
+        "moe_status_string": ([i32], C.c_char_p),
+        "moe_version": ([], i32),
+        "moe_route": ([dp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "moe_permute_workspace_bytes": ([dp], sz),
+        "moe_permute": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_expert_ffn_workspace_bytes": ([dp], sz),
+        "moe_expert_ffn": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_combine": ([dp, vp, vp, vp, vp, i32, vp], i32),
+        "moe_layer_workspace_bytes": ([dp], sz),
+        "moe_layer": ([dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
+        "moe_device_status": ([dp, vp, sz, vp], i32),
+        "moe_timing_enable": ([i32], None),
+        "moe_timing_read": ([C.POINTER(C.c_float), i32], i32),
+        "moe_set_wait_timeout_us": ([i64], None),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def header_abi_names():
+    """Function names declared in include/moe.h."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def exported_abi_names():
+    lib = load()
+    return [n for n in header_abi_names() if hasattr(lib, n)]
+
+
+# ------------------------------------------------------------------ helpers
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise MoEError(rc, what)
+
+
+def _dims(dims) -> MoEDims:
+    if isinstance(dims, MoEDims):
+        return dims
+    if isinstance(dims, dict):
+        return MoEDims.make(**dims)
+    return MoEDims.make(dims.T, dims.d, dims.f, dims.E, dims.k, dims.e_lo, dims.E_hi)
+
+
+def _require(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: want contiguous cuda {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ ABI calls
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def moe_permute_workspace_bytes(dims) -> int:
+    return int(load().moe_permute_workspace_bytes(C.byref(_dims(dims))))
+
+
+def moe_expert_ffn_workspace_bytes(dims) -> int:
+    return int(load().moe_expert_ffn_workspace_bytes(C.byref(_dims(dims))))
+
+
+def moe_layer_workspace_bytes(dims) -> int:
+    return int(load().moe_layer_workspace_bytes(C.byref(_dims(dims))))
+
+
+def moe_route(dims, x, w_router, bias=None, topk_ids=None, topk_w=None, logits=None,
+              want_logits: bool = False, stream=None):
+    """Top-k gating.  Returns (topk_ids int32 [T,k], topk_w f32 [T,k], logits or None)."""
+    import torch
+    D = _dims(dims)
+    dev = x.device
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(w_router, torch.bfloat16, (D.E, D.d), "w_router")
+    if bias is not None:
+        _require(bias, torch.float32, (D.E,), "bias")
+    if topk_ids is None:
+        topk_ids = torch.empty((D.T, D.k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((D.T, D.k), dtype=torch.float32, device=dev)
+    if logits is None and want_logits:
+        logits = torch.empty((D.T, D.E), dtype=torch.float32, device=dev)
+    rc = load().moe_route(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
+                          _ptr(topk_w), _ptr(logits), _stream(stream))
+    _check(rc, "moe_route")
+    return topk_ids, topk_w, logits
+
+
+def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv_perm=None,
+                x_perm=None, ws=None, stream=None):
+    """Dispatch.  Returns (counts, offsets, perm_src, inv_perm, x_perm) device tensors
+    (perm_src and x_perm sized for T*k rows; the first offsets[-1] are valid)."""
+    import torch
+    D = _dims(dims)
+    dev = x.device
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(topk_ids, torch.int32, (D.T, D.k), "topk_ids")
+    counts = torch.empty(EL, dtype=torch.int32, device=dev) if counts is None else counts
+    offsets = torch.empty(EL + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm_src = torch.empty(max(cap, 1), dtype=torch.int32, device=dev) if perm_src is None else perm_src
+    inv_perm = torch.empty((D.T, D.k), dtype=torch.int32, device=dev) if inv_perm is None else inv_perm
+    x_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if x_perm is None else x_perm
+    need = moe_permute_workspace_bytes(D)
+    ws = _workspace(need, dev) if ws is None else ws
+    rc = load().moe_permute(C.byref(D), _ptr(x), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                            _ptr(perm_src), _ptr(inv_perm), _ptr(x_perm), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_permute")
+    return counts, offsets, perm_src, inv_perm, x_perm
+
+
+def moe_expert_ffn(dims, x_perm, offsets, w_gate, w_up, w_down, y_perm=None, ws=None,
+                   stream=None):
+    """Grouped SwiGLU FFN over expert-contiguous rows.  Returns y_perm bf16 [T*k, d]."""
+    import torch
+    D = _dims(dims)
+    dev = x_perm.device
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(w_gate, torch.bfloat16, (EL, D.f, D.d), "w_gate")
+    _require(w_up, torch.bfloat16, (EL, D.f, D.d), "w_up")
+    _require(w_down, torch.bfloat16, (EL, D.d, D.f), "w_down")
+    _require(offsets, torch.int32, (EL + 1,), "offsets")
+    if x_perm.shape[0] < cap or x_perm.shape[1] != D.d:
+        raise ValueError("x_perm must have at least T*k rows of d")
+    y_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if y_perm is None else y_perm
+    need = moe_expert_ffn_workspace_bytes(D)
+    ws = _workspace(need, dev) if ws is None else ws
+    rc = load().moe_expert_ffn(C.byref(D), _ptr(x_perm), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
+                               _ptr(w_down), _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(rc, "moe_expert_ffn")
+    return y_perm
+
+
+def moe_combine(dims, y_perm, inv_perm, topk_w, out=None, out_dtype: int = MOE_BF16, stream=None):
+    """Gate-weighted combine.  Returns out [T, d] (bf16 or f32)."""
+    import torch
+    D = _dims(dims)
+    dev = y_perm.device
+    _require(inv_perm, torch.int32, (D.T, D.k), "inv_perm")
+    _require(topk_w, torch.float32, (D.T, D.k), "topk_w")
+    dt = torch.float32 if out_dtype == MOE_F32 else torch.bfloat16
+    out = torch.empty((D.T, D.d), dtype=dt, device=dev) if out is None else out
+    rc = load().moe_combine(C.byref(D), _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(out),
+                            int(out_dtype), _stream(stream))
+    _check(rc, "moe_combine")
+    return out
+
+
+def moe_layer(dims, x, w_router, w_gate, w_up, w_down, bias=None, out=None,
+              out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None, ws=None,
+              stream=None):
+    """Whole layer forward.  Returns out [T, d]."""
+    import torch
+    D = _dims(dims)
+    dev = x.device
+    EL = D.e_hi - D.e_lo
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(w_router, torch.bfloat16, (D.E, D.d), "w_router")
+    _require(w_gate, torch.bfloat16, (EL, D.f, D.d), "w_gate")
+    _require(w_up, torch.bfloat16, (EL, D.f, D.d), "w_up")
+    _require(w_down, torch.bfloat16, (EL, D.d, D.f), "w_down")
+    if bias is not None:
+        _require(bias, torch.float32, (D.E,), "bias")
+    dt = torch.float32 if out_dtype == MOE_F32 else torch.bfloat16
+    out = torch.empty((D.T, D.d), dtype=dt, device=dev) if out is None else out
+    need = moe_layer_workspace_bytes(D)
+    ws = _workspace(need, dev) if ws is None else ws
+    rc = load().moe_layer(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
+                          _ptr(w_up), _ptr(w_down), _ptr(out), int(out_dtype), _ptr(topk_ids_out),
+                          _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(stream))
+    _check(rc, "moe_layer")
+    return out
+
+
+def moe_device_status(dims, ws, stream=None) -> int:
+    return int(load().moe_device_status(C.byref(_dims(dims)), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_timing_enable(on: bool = True) -> None:
+    load().moe_timing_enable(1 if on else 0)
+
+
+def moe_timing_read() -> Tuple[int, Tuple[float, float, float]]:
+    arr = (C.c_float * 3)()
+    n = load().moe_timing_read(arr, 3)
+    return int(n), (arr[0], arr[1], arr[2])
+
+
+def moe_set_wait_timeout_us(us: int) -> None:
+    load().moe_set_wait_timeout_us(int(us))

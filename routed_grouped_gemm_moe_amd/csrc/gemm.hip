@@ -1,0 +1,122 @@
+// Standalone grouped expert GEMMs (the moe_expert_ffn path) and the m-tile
+// table builder.  The tile table is built on the device from the segment
+// offsets that the permute produced, so no count ever returns to the host
+// (Weave §3: the workload is fixed once routing completes; §4: the routing
+// result reaches the kernel as a parameter).
+//
+// Launch shape: one workgroup per (m-tile, n-tile), grid sized for the worst
+// case and surplus workgroups exit at once.  Tiles are numbered n-tile-major
+// (consecutive tiles share one weight tile across the m-tiles of an expert)
+// and each of the 8 XCDs takes one contiguous eighth of that order: workgroup
+// b runs on XCD b % 8 (round-robin dispatch), so the workgroups sharing a
+// weight tile meet in one XCD's L2.
+#include "gemm_tile.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(1024) void build_mtiles_kernel(int64_t EL,
+                                                            const int32_t *__restrict__ offsets,
+                                                            MTile *__restrict__ mtiles,
+                                                            int32_t *__restrict__ n_mtiles,
+                                                            int32_t *__restrict__ mtile_base) {
+    extern __shared__ int32_t s_mt[];  // [EL + 1]
+    for (int64_t e = threadIdx.x; e < EL; e += 1024)
+        s_mt[e] = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t run = 0;
+        for (int64_t e = 0; e < EL; ++e) {
+            int32_t m = s_mt[e];
+            s_mt[e] = run;
+            run += m;
+        }
+        s_mt[EL] = run;
+        *n_mtiles = run;
+    }
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < EL; e += 1024) {
+        const int32_t base = s_mt[e], n = s_mt[e + 1] - base;
+        const int32_t row0 = offsets[e], cnt = offsets[e + 1] - row0;
+        mtile_base[e] = base;
+        for (int32_t m = 0; m < n; ++m) {
+            MTile t;
+            t.e = (int32_t)e;
+            t.row0 = row0 + m * BM;
+            t.rows = min(BM, cnt - m * BM);
+            t.pad = 0;
+            mtiles[base + m] = t;
+        }
+    }
+}
+
+// Map workgroup b to tile L in [0, n): XCD x = b % 8 takes [x*per, x*per+per).
+__device__ __forceinline__ int xcd_tile(int n) {
+    const int b = blockIdx.x;
+    const int per = (n + NUM_XCD - 1) / NUM_XCD;
+    const int j = b / NUM_XCD;
+    if (j >= per) return -1;
+    const int L = (b % NUM_XCD) * per + j;
+    return L < n ? L : -1;
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
+    int64_t d, int64_t f, const bf16_t *__restrict__ A, const MTile *__restrict__ mtiles,
+    const int32_t *__restrict__ n_mtiles, const bf16_t *__restrict__ W0,
+    const bf16_t *__restrict__ W1, bf16_t *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+    const int MT = *n_mtiles;
+    const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
+    const int L = xcd_tile(MT * NT);
+    if (L < 0) return;
+    const int nt = L / MT;
+    const MTile t = mtiles[L % MT];
+    if (GATE_UP) {
+        const bf16_t *wg = W0 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
+        const bf16_t *wu = W1 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
+        gemm_tile<true>(A, d, t.row0, t.rows, wg, wu, d, (int)d, out, f, (int64_t)nt * BN_GU, lds);
+    } else {
+        const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
+        gemm_tile<false>(A, f, t.row0, t.rows, wd, nullptr, f, (int)f, out, d, (int64_t)nt * BN_DN,
+                         lds);
+    }
+}
+
+template <bool GATE_UP>
+hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, const int32_t *n_mtiles,
+                       const bf16_t *W0, const bf16_t *W1, bf16_t *out, hipStream_t s) {
+    const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
+    int64_t grid = D.max_mtiles() * NT;
+    grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    if (grid == 0) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_kernel<GATE_UP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
+                       GEMM_LDS_BYTES, s, D.d, D.f, A, mtiles, n_mtiles, W0, W1, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
+                               int32_t *n_mtiles, int32_t *mtile_base, hipStream_t s) {
+    hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024), (D.EL() + 1) * sizeof(int32_t), s,
+                       D.EL(), offsets, mtiles, n_mtiles, mtile_base);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *x_perm, const MTile *mtiles,
+                               const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
+                               bf16_t *h, hipStream_t s) {
+    return launch_gemm<true>(D, x_perm, mtiles, n_mtiles, w_gate, w_up, h, s);
+}
+
+hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
+                            const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
+                            hipStream_t s) {
+    return launch_gemm<false>(D, h, mtiles, n_mtiles, w_down, nullptr, y, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,239 @@
+// Persistent expert-FFN + combine kernel of moe_layer.
+//
+// One workgroup per CU stays resident and claims tiles until none are left
+// (Weave, §4: a persistent kernel in which each SM "claims its next tile via
+// atomicAdd on a global counter following the chunk pipeline DAG order").
+// Three tile kinds, claimed in dependency order:
+//   1. gate/up tiles (m-tile, 128 h columns): GEMM0 + SiLU-mul epilogue;
+//      each finished tile bumps gu_done[m-tile].
+//   2. down tiles (m-tile, 256 y columns): wait until gu_done[m-tile] counts
+//      every gate/up tile of that row block, then GEMM1; a finished tile sets
+//      dn_flag[m-tile, column block].
+//   3. combine tiles (32 tokens, 256 columns): wait for the dn_flag of every
+//      (m-tile, column block) their rows live in, then the gated sum.
+// A finished down tile thus hands its rows to the combine through a device-
+// side flag as soon as it is written (the producer-consumer tile signaling of
+// Cui et al., abstract), not at a kernel boundary.
+//
+// Queues: each kind is numbered n-tile-major and split into 8 contiguous
+// ranges, one per XCD (workgroup b runs on XCD b % 8), so the m-tiles that
+// share a weight tile run in one XCD's L2.  A workgroup first drains its own
+// XCD's range, then steals from the others, and moves to the next kind only
+// when every range of the current kind is claimed.  Deadlock freedom: a tile
+// waits only on tiles of an earlier kind, all of which were claimed earlier by
+// running workgroups whose own waits are, inductively, satisfiable.
+//
+// Memory ordering: producers fence (release, agent scope) before a barrier and
+// a release-add/store of the counter; consumers poll with relaxed loads, then
+// a barrier and an acquire fence at agent scope in every wave, which makes the
+// data written on another XCD visible.  Polling is bounded in time: a wait
+// that exceeds the timeout records MOE_ERR_DEVICE_TIMEOUT in the status word
+// and carries on (the result is then invalid, but the kernel drains).
+#include "combine_tile.h"
+#include "gemm_tile.h"
+
+namespace moe {
+namespace {
+
+// Synchronisation helpers.  Every branch and loop exit next to a barrier is
+// wave-uniform: work that one agent must do (claim a tile, bump a counter,
+// poll a flag) is done by all 64 lanes of wave 0 with uniform values
+// (readfirstlane, wave votes), never inside an `if (threadIdx.x == 0)`.  With
+// a lane-divergent region at the edge of a loop that contains barriers, the
+// compiler may rotate the loop so that lane 0 runs that region while the
+// other lanes already re-enter the body and wait at a barrier with stale
+// state -- the waves then never meet and the workgroup hangs.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Claim one tile of [0, n) for the calling wave.  Queue y covers
+// [y*per, y*per + per); the own XCD's queue first, then the others.
+__device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd) {
+    const int per = (n + NUM_XCD - 1) / NUM_XCD;
+    for (int r = 0; r < NUM_XCD; ++r) {
+        const int y = (xcd + r) & (NUM_XCD - 1);
+        const int lo = y * per;
+        const int len = min(n, lo + per) - lo;
+        if (len <= 0) continue;
+        int32_t *c = q + y * QSTRIDE;
+        if (uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= len)
+            continue;
+        // lane 0 adds 1, the others 0: lane 0's pre-op value is the claim
+        const int old = uniform(__hip_atomic_fetch_add(c, lane_id() == 0 ? 1 : 0,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (old < len) return lo + old;
+    }
+    return -1;
+}
+
+__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim) {
+    if (wave_id() == 0) *s_claim = claim_tile(q, n, xcd);  // all lanes store the same value
+    __syncthreads();
+    const int L = uniform(*s_claim);
+    __syncthreads();
+    return L;
+}
+
+// Wave-uniform wait until every lane's flag satisfies *p >= target (lanes with
+// need == false do not wait).  Bounded in wall-clock time (wall_clock64
+// ticks): past wait_ticks the status word records MOE_ERR_DEVICE_TIMEOUT, and
+// once any wait has timed out every other wait of the launch returns at once,
+// so a launch never outlives one timeout plus its own compute.
+__device__ __forceinline__ void wave_wait_geq(const int32_t *p, int32_t target, bool need,
+                                              int64_t wait_ticks, int32_t *status) {
+    const int64_t t0 = (int64_t)wall_clock64();
+    for (;;) {
+        const bool ok = !need || __hip_atomic_load(p, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (__all(ok)) return;
+        if (uniform(__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+            return;
+        if ((int64_t)wall_clock64() - t0 > wait_ticks) {
+            __hip_atomic_store(status, (int32_t)MOE_ERR_DEVICE_TIMEOUT, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+__device__ __forceinline__ void acquire_all() {
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// All stores of the workgroup become visible at agent scope, then wave 0
+// bumps (add) or sets (store 1) the counter with release semantics.
+__device__ __forceinline__ void release_then(int32_t *p, bool add) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (wave_id() == 0) {
+        if (add)
+            __hip_atomic_fetch_add(p, lane_id() == 0 ? 1 : 0, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
+    extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+    __shared__ int s_claim;
+    const Dims &D = a.D;
+    const int xcd = blockIdx.x % NUM_XCD;
+    const int MT = *a.n_mtiles;
+    const int NT1 = (int)D.nt_gu();
+    const int NT2 = (int)D.nt_dn();
+    const int64_t d = D.d, f = D.f, k = D.k;
+
+    // 1. gate/up tiles
+    const int n1 = MT * NT1;
+    if (n1 > 0)
+        for (;;) {
+            const int L = next_tile(a.queues, n1, xcd, &s_claim);
+            if (L < 0) break;
+            const int nt = L / MT, mt = L % MT;
+            const MTile t = a.mtiles[mt];
+            const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
+            gemm_tile<true>(a.x_perm, d, t.row0, t.rows, a.w_gate + wo, a.w_up + wo, d, (int)d,
+                            a.h, f, (int64_t)nt * BN_GU, lds);
+            release_then(a.gu_done + mt, true);
+        }
+
+    // 2. down tiles
+    const int n2 = MT * NT2;
+    if (n2 > 0)
+        for (;;) {
+            const int L = next_tile(a.queues + NUM_XCD * QSTRIDE, n2, xcd, &s_claim);
+            if (L < 0) break;
+            const int nt = L / MT, mt = L % MT;
+            const MTile t = a.mtiles[mt];
+            if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
+            acquire_all();
+            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
+            gemm_tile<false>(a.h, f, t.row0, t.rows, a.w_down + wo, nullptr, f, (int)f, a.y, d,
+                             (int64_t)nt * BN_DN, lds);
+            release_then(a.dn_flag + (int64_t)mt * NT2 + nt, false);
+        }
+
+    // 3. combine tiles
+    const int NTB = (int)D.comb_blocks();
+    const int n3 = NTB * NT2;
+    if (n3 > 0)
+        for (;;) {
+            const int L = next_tile(a.queues + 2 * NUM_XCD * QSTRIDE, n3, xcd, &s_claim);
+            if (L < 0) break;
+            const int nt = L / NTB, tb = L % NTB;
+            // every (token, slot) of the tile waits for the down tile holding its row
+            for (int base = 0; base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
+                const int i = base + (int)threadIdx.x;
+                const int64_t t = (int64_t)tb * COMB_TOK + i / k;
+                const int64_t j = i % k;
+                bool need = false;
+                const int32_t *flag = a.dn_flag;
+                if (i < COMB_TOK * k && t < D.T) {
+                    const int32_t p = a.inv_perm[t * k + j];
+                    if (p >= 0) {
+                        const int32_t e = a.ids[t * k + j] - (int32_t)D.e_lo;
+                        const int32_t mt = a.mtile_base[e] + (p - a.offsets[e]) / BM;
+                        flag = a.dn_flag + (int64_t)mt * NT2 + nt;
+                        need = true;
+                    }
+                }
+                wave_wait_geq(flag, 1, need, a.wait_ticks, a.status);
+            }
+            acquire_all();
+            for (int i = threadIdx.x; i < COMB_TOK * (BN_DN / 8); i += GEMM_THREADS) {
+                const int64_t t = (int64_t)tb * COMB_TOK + i / (BN_DN / 8);
+                if (t >= D.T) continue;
+                const int64_t v = (int64_t)nt * (BN_DN / 8) + i % (BN_DN / 8);
+                combine_vec<OUT_F32>(t, v, d, k, a.y, a.inv_perm, a.gates, a.out);
+            }
+        }
+}
+
+}  // namespace
+
+int layer_grid_size() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipFuncSetAttribute((const void *)layer_kernel<false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) != hipSuccess ||
+        hipFuncSetAttribute((const void *)layer_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)layer_kernel<false>,
+                                                     GEMM_THREADS, GEMM_LDS_BYTES) != hipSuccess ||
+        occ < 1)
+        occ = 1;
+    cached = cus * occ;
+    return cached;
+}
+
+int64_t wall_clock_hz() {
+    static int64_t cached = 0;
+    if (cached) return cached;
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        khz = 100000;  // 100 MHz, the documented constant rate
+    cached = (int64_t)khz * 1000;
+    return cached;
+}
+
+hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s) {
+    if (a.out_f32)
+        hipLaunchKernelGGL(layer_kernel<true>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s, a);
+    else
+        hipLaunchKernelGGL(layer_kernel<false>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
+                           a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,347 @@
+// Host runtime of the C ABI declared in include/moe.h: argument checks (run
+// before any HIP call, so they also work on a machine without a GPU),
+// workspace layout, the launch sequences of every entry point, and the
+// optional stage timing used by the benchmark.
+#include <mutex>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout make_layout(const Dims &D, LayoutKind kind) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t Tk = (size_t)(D.T * D.k), EL = (size_t)D.EL(), cap = (size_t)D.cap();
+    const size_t MT = (size_t)D.max_mtiles();
+    const bool layer = kind == LAYOUT_LAYER;
+    const bool ffn = kind == LAYOUT_FFN || layer;
+    const bool perm = kind == LAYOUT_PERMUTE || layer;
+    // scheduler state first and contiguous (cleared by one kernel)
+    L.status = take(layer ? 256 : 0);
+    L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
+    L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
+    L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
+    L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
+    L.gates = take(layer ? Tk * sizeof(float) : 0);
+    L.blk_counts = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
+    L.blk_base = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
+    L.counts = take(layer ? EL * sizeof(int32_t) : 0);
+    L.offsets = take(layer ? (EL + 1) * sizeof(int32_t) : 0);
+    L.perm_src = take(layer ? cap * sizeof(int32_t) : 0);
+    L.inv_perm = take(layer ? Tk * sizeof(int32_t) : 0);
+    L.mtiles = take(ffn ? MT * sizeof(MTile) : 0);
+    L.n_mtiles = take(ffn ? sizeof(int32_t) : 0);
+    L.mtile_base = take(ffn ? EL * sizeof(int32_t) : 0);
+    L.x_perm = take(layer ? cap * (size_t)D.d * 2 : 0);
+    L.h = take(ffn ? cap * (size_t)D.f * 2 : 0);
+    L.y = take(layer ? cap * (size_t)D.d * 2 : 0);
+    L.total = off;
+    return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+std::mutex g_mu;
+int64_t g_wait_us = 2000000;  // device flag-wait timeout
+bool g_timing = false;
+struct CallEvents {
+    hipEvent_t ev[4];
+};
+std::vector<CallEvents> g_events;   // recorded, not yet read
+std::vector<hipEvent_t> g_pool;     // free events
+
+hipEvent_t pool_event() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_dims(const moe_dims *dm, Dims *out) {
+    if (!dm) return MOE_ERR_INVALID_ARG;
+    Dims D{dm->T, dm->d, dm->f, dm->E, dm->k, dm->e_lo, dm->e_hi};
+    if (D.T < 0 || D.d <= 0 || D.f <= 0 || D.E <= 0 || D.k <= 0 || D.k > D.E || D.e_lo < 0 ||
+        D.e_hi > D.E || D.e_lo >= D.e_hi)
+        return MOE_ERR_INVALID_ARG;
+    if (D.E > 1024 || D.k > 64 || D.d % 256 != 0 || D.f % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (D.T * D.k >= (int64_t(1) << 31) || D.cap() * D.d >= (int64_t(1) << 40) ||
+        D.d >= (1 << 20) || D.f >= (1 << 20))
+        return MOE_ERR_UNSUPPORTED;
+    *out = D;
+    return MOE_OK;
+}
+
+moe_status check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return MOE_OK;
+    if (!ws || ((uintptr_t)ws & 255u) != 0 || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported dimensions";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_DEVICE_TIMEOUT: return "device-side flag wait timed out";
+    }
+    return "unknown status";
+}
+
+int moe_version(void) { return 100; }
+
+moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
+                     int32_t *topk_ids, float *topk_w, float *logits, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (D.T == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, topk_ids,
+                                   topk_w, logits, (hipStream_t)stream));
+}
+
+size_t moe_permute_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims(dims, &D) != MOE_OK) return 0;
+    return make_layout(D, LAYOUT_PERMUTE).total;
+}
+
+moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_ids,
+                       int32_t *counts, int32_t *offsets, int32_t *perm_src, int32_t *inv_perm,
+                       void *x_perm, void *ws, size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+    if (D.T > 0 && (!x || !topk_ids || !perm_src || !inv_perm || !x_perm))
+        return MOE_ERR_INVALID_ARG;
+    if (D.T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(D, LAYOUT_PERMUTE);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    return hip_status(launch_permute(D, (const bf16_t *)x, topk_ids, counts, offsets, perm_src,
+                                     inv_perm, (bf16_t *)x_perm, at<int32_t>(ws, L.blk_counts),
+                                     at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr,
+                                     nullptr, 0, (hipStream_t)stream));
+}
+
+size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims(dims, &D) != MOE_OK) return 0;
+    return make_layout(D, LAYOUT_FFN).total;
+}
+
+moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                          const void *w_gate, const void *w_up, const void *w_down, void *y_perm,
+                          void *ws, size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (D.T == 0) return MOE_OK;
+    if (!x_perm || !offsets || !w_gate || !w_up || !w_down || !y_perm) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned16(y_perm))
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(D, LAYOUT_FFN);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    bf16_t *h = at<bf16_t>(ws, L.h);
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), s);
+    if (e == hipSuccess)
+        e = launch_gemm_gate_up(D, (const bf16_t *)x_perm, mt, nmt, (const bf16_t *)w_gate,
+                                (const bf16_t *)w_up, h, s);
+    if (e == hipSuccess)
+        e = launch_gemm_down(D, h, mt, nmt, (const bf16_t *)w_down, (bf16_t *)y_perm, s);
+    return hip_status(e);
+}
+
+moe_status moe_combine(const moe_dims *dims, const void *y_perm, const int32_t *inv_perm,
+                       const float *topk_w, void *out, moe_dtype out_dtype, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+    if (D.T == 0) return MOE_OK;
+    if (!y_perm || !inv_perm || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_combine(D, (const bf16_t *)y_perm, inv_perm, topk_w, out,
+                                     out_dtype == MOE_F32, (hipStream_t)stream));
+}
+
+size_t moe_layer_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims(dims, &D) != MOE_OK) return 0;
+    return make_layout(D, LAYOUT_LAYER).total;
+}
+
+moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
+                     const void *w_gate, const void *w_up, const void *w_down, void *out,
+                     moe_dtype out_dtype, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                     size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+    if (D.T == 0) return MOE_OK;
+    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
+        !aligned16(w_down) || !aligned16(out))
+        return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(D, LAYOUT_LAYER);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    const int grid = layer_grid_size();
+    if (grid <= 0) return MOE_ERR_HIP;
+    int64_t wait_us;
+    CallEvents ce{};
+    bool timing;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        wait_us = g_wait_us;
+        timing = g_timing;
+        if (timing)
+            for (int i = 0; i < 4; ++i) ce.ev[i] = pool_event();
+    }
+    auto mark = [&](int i) {
+        if (timing && ce.ev[i]) (void)hipEventRecord(ce.ev[i], s);
+    };
+
+    int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
+    int32_t *offsets = at<int32_t>(ws, L.offsets);
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    int32_t *mtile_base = at<int32_t>(ws, L.mtile_base);
+    int32_t *inv_perm = at<int32_t>(ws, L.inv_perm);
+    bf16_t *x_perm = at<bf16_t>(ws, L.x_perm);
+    const int64_t sched_ints = (int64_t)((L.dn_flag - L.status) / 4) +
+                               D.max_mtiles() * D.nt_dn();
+
+    mark(0);
+    hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
+                                nullptr, s);
+    mark(1);
+    if (e == hipSuccess)
+        e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
+                           at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
+                           at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), mt, nmt,
+                           mtile_base, at<int32_t>(ws, L.status), sched_ints, s);
+    mark(2);
+    if (e == hipSuccess) {
+        LayerArgs a;
+        a.D = D;
+        a.x_perm = x_perm;
+        a.w_gate = (const bf16_t *)w_gate;
+        a.w_up = (const bf16_t *)w_up;
+        a.w_down = (const bf16_t *)w_down;
+        a.h = at<bf16_t>(ws, L.h);
+        a.y = at<bf16_t>(ws, L.y);
+        a.ids = ids;
+        a.inv_perm = inv_perm;
+        a.offsets = offsets;
+        a.mtile_base = mtile_base;
+        a.n_mtiles = nmt;
+        a.gates = gates;
+        a.mtiles = mt;
+        a.queues = at<int32_t>(ws, L.queues);
+        a.gu_done = at<int32_t>(ws, L.gu_done);
+        a.dn_flag = at<int32_t>(ws, L.dn_flag);
+        a.status = at<int32_t>(ws, L.status);
+        a.out = out;
+        a.out_f32 = out_dtype == MOE_F32;
+        a.wait_ticks = wait_us * (wall_clock_hz() / 1000000);
+        e = launch_layer_persistent(a, grid, s);
+    }
+    mark(3);
+    if (timing) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_events.push_back(ce);
+    }
+    return hip_status(e);
+}
+
+moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    const Layout L = make_layout(D, LAYOUT_LAYER);
+    if ((st = check_ws((void *)ws, ws_bytes, L.total)) != MOE_OK) return st;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
+    int32_t v = 0;
+    if (hipMemcpy(&v, at<int32_t>((void *)ws, L.status), sizeof v, hipMemcpyDeviceToHost) !=
+        hipSuccess)
+        return MOE_ERR_HIP;
+    return v == 0 ? MOE_OK : (moe_status)v;
+}
+
+void moe_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_timing = on != 0;
+    for (auto &ce : g_events)
+        for (auto ev : ce.ev)
+            if (ev) {
+                (void)hipEventSynchronize(ev);
+                g_pool.push_back(ev);
+            }
+    g_events.clear();
+}
+
+int moe_timing_read(float *stage_ms, int n_stages) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    double sum[3] = {0, 0, 0};
+    int n = 0;
+    for (auto &ce : g_events) {
+        bool ok = true;
+        float ms[3] = {0, 0, 0};
+        for (int i = 0; i < 3 && ok; ++i) {
+            if (!ce.ev[i] || !ce.ev[i + 1] || hipEventSynchronize(ce.ev[i + 1]) != hipSuccess ||
+                hipEventElapsedTime(&ms[i], ce.ev[i], ce.ev[i + 1]) != hipSuccess)
+                ok = false;
+        }
+        if (ok) {
+            for (int i = 0; i < 3; ++i) sum[i] += ms[i];
+            ++n;
+        }
+        for (auto ev : ce.ev)
+            if (ev) g_pool.push_back(ev);
+    }
+    g_events.clear();
+    for (int i = 0; i < n_stages && i < 3; ++i) stage_ms[i] = n ? (float)(sum[i] / n) : 0.0f;
+    return n;
+}
+
+void moe_set_wait_timeout_us(int64_t us) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_wait_us = us < 1 ? 2000000 : us;
+}
+
+}  // extern "C"

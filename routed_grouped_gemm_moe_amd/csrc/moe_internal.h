@@ -1,0 +1,131 @@
+// Internal declarations of the gfx950 MoE library: tile constants, bf16
+// helpers, the workspace layout and the kernel launchers.  Not part of the
+// C ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- tiles
+// Grouped GEMM tile: BM rows x BN_TILE output columns x BK per LDS stage,
+// 256 threads = 4 waves in a 2x2 grid, each wave 128x128 with 32x32x16 MFMAs.
+constexpr int BM = 256;
+constexpr int BK = 64;
+constexpr int BN_TILE = 256;          // B rows staged per tile
+constexpr int BN_GU = 128;            // gate (and up) columns per gate/up tile
+constexpr int BN_DN = 256;            // down columns per down tile
+constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_LDS_BYTES = 2 * (BM * BK + BN_TILE * BK) * 2;  // 128 KiB, double buffered
+
+// Permute: tokens per block of the histogram / rank kernels.
+constexpr int PERM_TB = 256;
+// Combine tile of the persistent kernel: tokens x BN_DN columns.
+constexpr int COMB_TOK = 32;
+
+constexpr int NUM_XCD = 8;            // MI355X: 8 accelerator complex dies
+constexpr int QSTRIDE = 32;           // ints between queue counters (128 B apart)
+
+// ---------------------------------------------------------------- bf16
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Native 16-byte vector (HIP's uint4 is a union-based struct, which keeps
+// arrays of it out of registers).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 element q (0..7) of a 16-byte vector, widened exactly to float.
+__device__ __forceinline__ float bf16x8_elem(const u32x4_t &v, int q) {
+    const uint32_t w = v[q >> 1];
+    return __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+__device__ __forceinline__ float bf2f(bf16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+// float -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- sizes
+struct Dims {
+    int64_t T, d, f, E, k, e_lo, e_hi;
+    __host__ __device__ int64_t EL() const { return e_hi - e_lo; }
+    __host__ __device__ int64_t cap() const { return T * k; }                       // worst-case local rows
+    __host__ __device__ int64_t max_mtiles() const { return (cap() + EL() * (BM - 1)) / BM; }
+    __host__ __device__ int64_t nt_gu() const { return f / BN_GU; }
+    __host__ __device__ int64_t nt_dn() const { return d / BN_DN; }
+    __host__ __device__ int64_t perm_blocks() const { return (T + PERM_TB - 1) / PERM_TB; }
+    __host__ __device__ int64_t comb_blocks() const { return (T + COMB_TOK - 1) / COMB_TOK; }
+};
+
+// An m-tile of the grouped GEMM: rows [row0, row0 + rows) of expert e.
+struct MTile {
+    int32_t e, row0, rows, pad;
+};
+
+// Byte offsets of every region in a workspace (each 256-byte aligned).
+struct Layout {
+    size_t status, queues, gu_done, dn_flag, ids, gates, blk_counts, blk_base, counts, offsets,
+        perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm, h, y, total;
+};
+
+enum LayoutKind { LAYOUT_PERMUTE = 0, LAYOUT_FFN = 1, LAYOUT_LAYER = 2 };
+Layout make_layout(const Dims &D, LayoutKind kind);
+
+template <typename T>
+__host__ __device__ inline T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(ws) + off);
+}
+
+// ---------------------------------------------------------------- launches
+// All return hipSuccess or the launch error.
+hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
+                        int32_t *ids, float *gates, float *logits, hipStream_t s);
+
+hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
+                          int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
+                          int32_t *blk_counts, int32_t *blk_base,
+                          // optional: also build the GEMM m-tile table and clear the
+                          // scheduler state of the persistent kernel (NULL to skip)
+                          MTile *mtiles, int32_t *n_mtiles, int32_t *mtile_base,
+                          int32_t *sched_state, int64_t sched_state_ints, hipStream_t s);
+
+hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
+                               int32_t *n_mtiles, int32_t *mtile_base, hipStream_t s);
+
+hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *x_perm, const MTile *mtiles,
+                               const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
+                               bf16_t *h, hipStream_t s);
+hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
+                            const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
+                            hipStream_t s);
+
+hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *inv_perm,
+                          const float *gates, void *out, bool out_f32, hipStream_t s);
+
+struct LayerArgs {
+    Dims D;
+    const bf16_t *x_perm, *w_gate, *w_up, *w_down;
+    bf16_t *h, *y;
+    const int32_t *ids, *inv_perm, *offsets, *mtile_base, *n_mtiles;
+    const float *gates;
+    const MTile *mtiles;
+    int32_t *queues, *gu_done, *dn_flag, *status;
+    void *out;
+    int out_f32;
+    int64_t wait_ticks;  // flag-wait timeout in wall_clock64 ticks
+};
+hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s);
+int layer_grid_size();  // resident workgroups of the persistent kernel (cached)
+int64_t wall_clock_hz(); // frequency of wall_clock64 on the current device (cached)
+
+}  // namespace moe

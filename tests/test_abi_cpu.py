@@ -1,0 +1,108 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/moe.h declares, sizes workspaces, and rejects bad arguments on
+the host before anything is enqueued (no compute call is made here)."""
+import ctypes as C
+import os
+
+import pytest
+
+import routed_grouped_gemm_moe_amd as M
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.lib_path()),
+                                reason="library not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = C.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_WS = C.c_void_p(0x100000)   # 256-byte aligned, for workspace-size checks
+
+
+def dims(**kw):
+    base = dict(T=256, d=512, f=1024, E=8, k=2)
+    base.update(kw)
+    return M.MoEDims.make(**base)
+
+
+def test_every_header_function_is_exported():
+    names = M.header_abi_names()
+    for want in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+                 "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string"):
+        assert want in names
+    lib = M.load()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert missing == []
+
+
+def test_status_strings():
+    assert M.moe_status_string(0) == "ok"
+    assert "workspace" in M.moe_status_string(WORKSPACE)
+    assert "timed out" in M.moe_status_string(-5)
+    assert M.load().moe_version() >= 100
+
+
+def test_workspace_sizes_scale_with_problem():
+    small = M.moe_layer_workspace_bytes(dims())
+    big = M.moe_layer_workspace_bytes(dims(T=4096, d=4096, f=14336))
+    assert 0 < small < big
+    # layer workspace holds x_perm, h and y for T*k rows at least
+    D = dims(T=4096, d=4096, f=14336)
+    assert big >= 4096 * 2 * (4096 + 14336 + 4096) * 2
+    assert M.moe_permute_workspace_bytes(dims()) > 0
+    assert M.moe_expert_ffn_workspace_bytes(dims()) > 256 * 2 * 1024 * 2
+    # invalid dims size to 0
+    assert M.moe_layer_workspace_bytes(dims(k=9)) == 0
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(k=0), INVALID), (dict(k=9), INVALID), (dict(e_lo=4, e_hi=4), INVALID),
+    (dict(e_hi=9), INVALID), (dict(T=-1), INVALID), (dict(d=0), INVALID),
+    (dict(d=384), UNSUPPORTED), (dict(f=1000), UNSUPPORTED), (dict(E=2000, k=2), UNSUPPORTED),
+    (dict(E=128, k=65), UNSUPPORTED),
+])
+def test_bad_dims_rejected_by_every_entry_point(bad, status):
+    lib = M.load()
+    D = dims(**bad)
+    assert lib.moe_route(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, None, None) == status
+    assert lib.moe_permute(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, 1 << 40,
+                           None) == status
+    assert lib.moe_expert_ffn(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, 1 << 40,
+                              None) == status
+    assert lib.moe_combine(C.byref(D), FAKE, FAKE, FAKE, FAKE, 0, None) == status
+    assert lib.moe_layer(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None, None,
+                         FAKE_WS, 1 << 40, None) == status
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = M.load()
+    D = dims()
+    assert lib.moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, None) == INVALID
+    assert lib.moe_route(C.byref(D), None, FAKE, None, FAKE, FAKE, None, None) == INVALID
+    assert lib.moe_route(C.byref(D), C.c_void_p(0x10002), FAKE, None, FAKE, FAKE, None,
+                         None) == INVALID
+    assert lib.moe_combine(C.byref(D), FAKE, FAKE, FAKE, FAKE, 7, None) == INVALID
+    assert lib.moe_layer(C.byref(D), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, None, None,
+                         FAKE_WS, 1 << 40, None) == INVALID
+
+
+def test_workspace_checks():
+    lib = M.load()
+    D = dims()
+    need = M.moe_layer_workspace_bytes(D)
+    args = (C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None, None)
+    assert lib.moe_layer(*args, None, need, None) == WORKSPACE
+    assert lib.moe_layer(*args, FAKE_WS, need - 1, None) == WORKSPACE
+    assert lib.moe_layer(*args, C.c_void_p(0x100010), need, None) == WORKSPACE
+    pneed = M.moe_permute_workspace_bytes(D)
+    assert lib.moe_permute(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS,
+                           pneed - 1, None) == WORKSPACE
+    fneed = M.moe_expert_ffn_workspace_bytes(D)
+    assert lib.moe_expert_ffn(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, fneed - 1,
+                              None) == WORKSPACE
+
+
+def test_empty_batch_is_a_no_op():
+    lib = M.load()
+    D = dims(T=0)
+    assert lib.moe_route(C.byref(D), None, None, None, None, None, None, None) == OK
+    assert lib.moe_combine(C.byref(D), None, None, None, None, 0, None) == OK
+    assert lib.moe_layer(C.byref(D), None, None, None, None, None, None, None, 0, None, None, None,
+                         0, None) == OK

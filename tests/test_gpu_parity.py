@@ -1,0 +1,236 @@
+"""GPU parity: every C-ABI call against the CPU oracle.
+
+Small and ragged cases are compared element by element; the five workload
+shapes at full size are compared bit-exactly on routing and dispatch and on
+sampled tokens/rows for the FFN and layer outputs.  The fused moe_layer must
+also equal the staged route -> permute -> expert_ffn -> combine path bit for
+bit: both run the same tiles, so any difference is a scheduling or signaling
+error in the persistent kernel.
+"""
+import numpy as np
+import pytest
+
+import moe_workloads as W
+import oracle
+from gpu_util import (TOL_GATE, TOL_LAYER, dev, dev_bf16, host_bits, host_f32, rel_err, say,
+                      sample_tokens, upload)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import routed_grouped_gemm_moe_amd as M
+
+
+def _dims(cfg):
+    return M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+
+
+SMALL = {
+    "tiny": W.CONFIGS["tiny"],
+    "ragged_T300": W.CONFIGS["tiny"].scaled(T=300, d=256, f=384, seed=3),
+    "local_subset_e16k4": W.CONFIGS["tiny"].scaled(T=200, d=512, f=256, E=16, k=4, e_lo=3,
+                                                   e_hi=11, out_fp32=True, seed=4),
+    "k_equals_E": W.CONFIGS["tiny"].scaled(T=64, d=256, f=128, E=4, k=4, seed=5),
+    "k1": W.CONFIGS["tiny"].scaled(T=130, d=256, f=256, E=6, k=1, seed=6),
+    "e128k8": W.CONFIGS["tiny"].scaled(T=160, d=256, f=128, E=128, k=8, seed=7),
+    "single_expert": W.CONFIGS["tiny"].scaled(T=77, d=256, f=128, E=1, k=1, seed=8),
+    "one_token": W.CONFIGS["tiny"].scaled(T=1, d=256, f=128, E=8, k=2, seed=9),
+    "multi_tile_rows": W.CONFIGS["tiny"].scaled(T=1000, d=256, f=256, E=4, k=2, seed=10),
+}
+
+
+def _bias_all_to_one(E, e):
+    b = np.zeros(E, np.float32)
+    b[e] = 1000.0
+    return b
+
+
+def _check_route(cfg, t, arrs):
+    D = _dims(cfg)
+    say(f"moe_route {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k}")
+    ids, gates, logits = M.moe_route(D, t["x"], t["w_router"], t["bias"], want_logits=True)
+    torch.cuda.synchronize()
+    r_ids, r_g, r_l = oracle.route(arrs["x"], arrs["w_router"], cfg.k, bias=arrs["bias"],
+                                   want_logits=True)
+    assert np.array_equal(logits.cpu().numpy().view(np.uint32), r_l.view(np.uint32)), "logits"
+    assert np.array_equal(ids.cpu().numpy(), r_ids), "topk ids"
+    assert np.abs(gates.cpu().numpy() - r_g).max() <= TOL_GATE, "gates"
+    return ids, gates, r_ids, r_g
+
+
+def _check_permute(cfg, t, arrs, ids_dev, r_ids):
+    D = _dims(cfg)
+    say(f"moe_permute {cfg.name}")
+    counts, offsets, perm, inv, xp = M.moe_permute(D, t["x"], ids_dev)
+    torch.cuda.synchronize()
+    rc, ro, rp, ri = oracle.permute(r_ids, cfg.E, cfg.e_lo, cfg.E_hi)
+    N = int(ro[-1])
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy()[:N], rp)
+    assert np.array_equal(inv.cpu().numpy(), ri)
+    assert np.array_equal(host_bits(xp[:N]), arrs["x"][rp]), "x_perm rows"
+    return offsets, inv, xp, ro, rp, ri, N
+
+
+def _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N, rows=None):
+    D = _dims(cfg)
+    say(f"moe_expert_ffn {cfg.name} N={N}")
+    y = M.moe_expert_ffn(D, xp, offsets, t["w_gate"], t["w_up"], t["w_down"])
+    torch.cuda.synchronize()
+    if N == 0:
+        return y
+    rows = np.arange(N) if rows is None else rows
+    expert_of_row = (np.searchsorted(ro, rows, side="right") - 1).astype(np.int32)
+    ref = oracle.expert_rows(arrs["x"][rp[rows]], expert_of_row, arrs["w_gate"], arrs["w_up"],
+                             arrs["w_down"])
+    got = host_f32(y[torch.as_tensor(rows, device="cuda")])
+    err = rel_err(got, ref)
+    say(f"  ffn rel err {err:.3e}")
+    assert err <= TOL_LAYER
+    return y
+
+
+def _check_combine(cfg, t, y, inv, gates_dev, ri, r_g, N):
+    D = _dims(cfg)
+    yy = host_f32(y[:max(N, 1)]).astype(np.float64)
+    ref = oracle.combine(yy, ri, gates_dev.cpu().numpy())
+    for dt, tol in ((M.MOE_BF16, 2.0 ** -8), (M.MOE_F32, 1e-5)):
+        say(f"moe_combine {cfg.name} dtype={dt}")
+        out = M.moe_combine(D, y, inv, gates_dev, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert rel_err(host_f32(out), ref) <= tol
+
+
+def _check_layer(cfg, t, arrs, staged_out=None, tokens=None):
+    D = _dims(cfg)
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    say(f"moe_layer {cfg.name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} "
+        f"local=[{cfg.e_lo},{cfg.E_hi})")
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
+                      out_dtype=dt, topk_ids_out=ids, topk_w_out=gates, ws=ws)
+    assert M.moe_device_status(D, ws) == 0
+    tokens = np.arange(cfg.T) if tokens is None else tokens
+    ref, r_ids, r_g = oracle.layer_tokens(tokens, arrs["x"], arrs["w_router"], arrs["w_gate"],
+                                          arrs["w_up"], arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi,
+                                          bias=arrs["bias"])
+    assert np.array_equal(ids.cpu().numpy()[tokens], r_ids)
+    assert np.abs(gates.cpu().numpy()[tokens] - r_g).max() <= TOL_GATE
+    got = host_f32(out[torch.as_tensor(tokens, device="cuda")])
+    err = rel_err(got, ref)
+    say(f"  layer rel err {err:.3e} over {len(tokens)} tokens")
+    assert err <= TOL_LAYER
+    if staged_out is not None:
+        assert torch.equal(out.view(torch.int32) if dt == M.MOE_F32 else out.view(torch.int16),
+                           staged_out.view(torch.int32) if dt == M.MOE_F32
+                           else staged_out.view(torch.int16)), "fused != staged"
+    return out
+
+
+def _staged(cfg, t, y, inv, gates_dev):
+    D = _dims(cfg)
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    return M.moe_combine(D, y, inv, gates_dev, out_dtype=dt)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_case_all_stages(name):
+    cfg = SMALL[name].scaled(name=name)
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N)
+    _check_combine(cfg, t, y, inv, gates, ri, r_g, N)
+    staged = _staged(cfg, t, y, inv, gates)
+    _check_layer(cfg, t, arrs, staged_out=staged)
+
+
+@pytest.mark.parametrize("hot,k", [(5, 1), (2, 2)])
+def test_degenerate_one_expert_takes_everything(hot, k):
+    cfg = W.CONFIGS["tiny"].scaled(name=f"hot{hot}k{k}", T=260, d=256, f=256, E=8, k=k, seed=11)
+    arrs = W.generate(cfg, bias_override=_bias_all_to_one(8, hot))
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    assert np.all(r_ids[:, 0] == hot)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    assert np.diff(ro)[hot] == cfg.T
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N)
+    staged = _staged(cfg, t, y, inv, gates)
+    _check_layer(cfg, t, arrs, staged_out=staged)
+
+
+def test_no_local_rows_gives_zero_output():
+    # every token routes only to experts outside the local range
+    cfg = W.CONFIGS["tiny"].scaled(name="nolocal", T=50, d=256, f=128, E=8, k=1, e_lo=0, e_hi=2,
+                                   out_fp32=True, seed=12)
+    arrs = W.generate(cfg, bias_override=_bias_all_to_one(8, 6))
+    t = upload(cfg, arrs)
+    out = _check_layer(cfg, t, arrs)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_repeated_calls_reuse_workspace_and_stay_identical():
+    cfg = SMALL["multi_tile_rows"]
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    D = _dims(cfg)
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    say("moe_layer repeated x5 on one workspace")
+    outs = [M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws)
+            for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert M.moe_device_status(D, ws) == 0
+
+
+def test_bounded_wait_reports_timeout_then_recovers():
+    cfg = SMALL["multi_tile_rows"]
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    D = _dims(cfg)
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    say("moe_layer with a 1 us flag-wait timeout")
+    try:
+        M.moe_set_wait_timeout_us(1)
+        M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws)
+        st = M.moe_device_status(D, ws)
+        assert st in (0, -5)
+    finally:
+        M.moe_set_wait_timeout_us(0)
+    say("moe_layer with the default timeout")
+    M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws)
+    assert M.moe_device_status(D, ws) == 0
+
+
+# ------------------------------------------------------------ full-size shapes
+
+FULL = ["tiny", "mixtral", "fine", "skewed", "dsv3_share"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(name):
+    cfg = W.CONFIGS[name]
+    say(f"generate {name}")
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    # FFN rows: first and last row of a few experts plus random rows
+    rng = np.random.default_rng(1)
+    edges = np.concatenate([ro[:-1][np.diff(ro) > 0][:6], (ro[1:] - 1)[np.diff(ro) > 0][-6:]])
+    rows = np.unique(np.concatenate([edges, rng.choice(N, size=min(N, 12), replace=False)]))
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N, rows=rows)
+    staged = _staged(cfg, t, y, inv, gates)
+    local_tok = np.nonzero((ri >= 0).any(1))[0]
+    must = local_tok[:3].tolist() + local_tok[-3:].tolist()
+    if cfg.E_loc < cfg.E:
+        must += np.nonzero(~(ri >= 0).any(1))[0][:2].tolist()
+    toks = sample_tokens(cfg.T, 16, seed=2, must=must)
+    _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
+    del t, xp, y, staged
+    torch.cuda.empty_cache()
