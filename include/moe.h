@@ -161,6 +161,19 @@ moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_byt
 void moe_timing_enable(int on);
 int moe_timing_read(float *stage_ms, int n_stages);
 
+/* ---- Per-tile trace (measurement aid, after the per-tile clock traces that
+ * X-Stage, §5.1, takes of its fused kernel).  With a buffer set, every
+ * moe_layer launch appends one record per tile of its persistent kernel:
+ *   int64 buf[1 + 4*n_records], buf[0] = records written (the caller zeroes it;
+ *   it can exceed n_records, extra records are dropped), then per record
+ *   {kind << 32 | tile index, workgroup << 8 | XCD, start tick, end tick},
+ *   kind 1 = gate/up, 2 = down, 3 = combine; ticks of the device's constant
+ *   wall clock, moe_wall_clock_hz() per second.
+ * buf is device memory owned by the caller; NULL (or n_records < 1) turns the
+ * trace off.  Not thread-safe; for profiling only. */
+void moe_set_trace(void *buf, int64_t n_records);
+int64_t moe_wall_clock_hz(void);
+
 /* Timeout of each device-side flag wait of moe_layer, in microseconds
  * (default 2 s; values < 1 restore the default).  A wait that times out
  * records MOE_ERR_DEVICE_TIMEOUT and makes every other wait of that launch

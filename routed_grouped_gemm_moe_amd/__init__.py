@@ -22,7 +22,8 @@ __all__ = [
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
-    "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "MoEError",
+    "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "moe_set_trace",
+    "moe_wall_clock_hz", "MoEError",
     "MOE_BF16", "MOE_F32",
 ]
 
@@ -82,6 +83,8 @@ def load():
         "moe_timing_enable": ([i32], None),
         "moe_timing_read": ([C.POINTER(C.c_float), i32], i32),
         "moe_set_wait_timeout_us": ([i64], None),
+        "moe_set_trace": ([vp, i64], None),
+        "moe_wall_clock_hz": ([], i64),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -286,3 +289,13 @@ def moe_timing_read() -> Tuple[int, Tuple[float, float, float]]:
 
 def moe_set_wait_timeout_us(us: int) -> None:
     load().moe_set_wait_timeout_us(int(us))
+
+
+def moe_set_trace(buf=None, n_records: int = 0) -> None:
+    """Per-tile trace of moe_layer into an int64 device tensor of 1 + 4*n_records
+    elements (element 0 = record count, zero it first); None turns it off."""
+    load().moe_set_trace(_ptr(buf), int(n_records) if buf is not None else 0)
+
+
+def moe_wall_clock_hz() -> int:
+    return int(load().moe_wall_clock_hz())

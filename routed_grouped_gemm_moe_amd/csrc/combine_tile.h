@@ -8,7 +8,9 @@ namespace moe {
 
 // out[t, 8v .. 8v+8) = sum over slots j ascending (inv_perm >= 0) of
 // gates[t,j] * y[inv_perm[t,j], 8v .. 8v+8), float32 accumulation.
-template <bool OUT_F32>
+// COHERENT: read y with device-coherent loads (two 8-byte agent-scope atomic
+// loads), for y rows written moments ago by another XCD.
+template <bool OUT_F32, bool COHERENT = false>
 __device__ __forceinline__ void combine_vec(int64_t t, int64_t v, int64_t d, int64_t k,
                                             const bf16_t *__restrict__ y,
                                             const int32_t *__restrict__ inv_perm,
@@ -20,7 +22,15 @@ __device__ __forceinline__ void combine_vec(int64_t t, int64_t v, int64_t d, int
         const int32_t p = inv_perm[t * k + j];
         if (p < 0) continue;
         const float w = gates[t * k + j];
-        const u32x4_t yv = reinterpret_cast<const u32x4_t *>(y + (int64_t)p * d)[v];
+        u32x4_t yv;
+        if (COHERENT) {
+            const uint64_t *q = reinterpret_cast<const uint64_t *>(y + (int64_t)p * d) + 2 * v;
+            const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            yv = u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+        } else {
+            yv = reinterpret_cast<const u32x4_t *>(y + (int64_t)p * d)[v];
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w, bf16x8_elem(yv, q), acc[q]);
     }

@@ -5,11 +5,11 @@
 // result reaches the kernel as a parameter).
 //
 // Launch shape: one workgroup per (m-tile, n-tile), grid sized for the worst
-// case and surplus workgroups exit at once.  Tiles are numbered n-tile-major
-// (consecutive tiles share one weight tile across the m-tiles of an expert)
-// and each of the 8 XCDs takes one contiguous eighth of that order: workgroup
-// b runs on XCD b % 8 (round-robin dispatch), so the workgroups sharing a
-// weight tile meet in one XCD's L2.
+// case and surplus workgroups exit at once.  Tiles follow the blocked order
+// of gemm_tile.h (groups of 4 m-tiles swept n-tile-major, so the tiles in
+// flight share weight and activation tiles) and each of the 8 XCDs takes one
+// contiguous eighth of that order: workgroup b runs on XCD b % 8 (round-robin
+// dispatch), so the workgroups sharing a tile meet in one XCD's L2.
 #include "gemm_tile.h"
 
 namespace moe {
@@ -65,13 +65,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     int64_t d, int64_t f, const bf16_t *__restrict__ A, const MTile *__restrict__ mtiles,
     const int32_t *__restrict__ n_mtiles, const bf16_t *__restrict__ W0,
     const bf16_t *__restrict__ W1, bf16_t *__restrict__ out) {
-    extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+    extern __shared__ __attribute__((aligned(16))) char lds[];
     const int MT = *n_mtiles;
     const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
     const int L = xcd_tile(MT * NT);
     if (L < 0) return;
-    const int nt = L / MT;
-    const MTile t = mtiles[L % MT];
+    int mt, nt;
+    blocked_tile(L, MT, NT, &mt, &nt);
+    const MTile t = mtiles[mt];
     if (GATE_UP) {
         const bf16_t *wg = W0 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
         const bf16_t *wu = W1 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;

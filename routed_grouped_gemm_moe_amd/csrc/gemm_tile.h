@@ -3,99 +3,92 @@
 // followed by element-wise multiplication", GEMM1 = down projection).
 //
 // Tile: BM = 256 rows (one expert's rows, clamped at the segment end) by
-// BN_TILE = 256 B rows, stepping K by BK = 64 through double-buffered LDS.
-// 256 threads = 4 waves in a 2x2 grid; each wave owns a 128x128 block made of
-// 4x4 v_mfma_f32_32x32x16_bf16 tiles (256 float accumulators per lane).
+// BN_TILE = 256 B rows.  256 threads = 4 waves in a 2x2 grid; each wave owns a
+// 128x128 block made of 4x4 v_mfma_f32_32x32x16_bf16 tiles (256 float
+// accumulators per lane, held in AGPRs).
+//
+// Staging: K advances by BK = 32 per stage through a ring of NSTAGE = 4 LDS
+// stages (32 KiB each).  Operands go global -> LDS directly (buffer loads with
+// the LDS-DMA bit, 16 bytes per lane), without passing through VGPRs, and the
+// loads of stage s+3 are issued while stage s is multiplied, so three stages
+// (~3000 MFMA cycles) of latency are covered.  Each lane of a DMA instruction
+// writes 16 bytes at LDS base + 16*lane; the lane's global source is chosen so
+// that the 16-byte chunk c of staged row r lands at chunk c ^ swz(r),
+// swz(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the MFMA fragment reads (32
+// consecutive rows, one chunk) free of bank conflicts whether the LDS serves
+// 8 or 16 lanes per cycle.  The buffer descriptors span exactly the tile's
+// rows, so a stray offset reads zeros instead of faulting.
 //
 // Operands are K-contiguous in memory (activations [rows][K], weights
-// [out][K]), so A and B stage identically: every 16-byte chunk c of a 128-byte
-// LDS row r is stored at chunk position c ^ (r & 7).  A lane's MFMA fragment is
-// one 16-byte chunk (8 consecutive k) of one row; the xor spreads the 8 lanes
-// that read the same chunk index of 8 consecutive rows over distinct banks.
+// [out][K]).  GATE_UP (GEMM0): B rows 0..127 are gate rows n0..n0+127 of
+// expert e and rows 128..255 the matching up rows, so every wave holds gate
+// and up accumulators for the same (row, column) and the epilogue writes
+// h = silu(g) * u as bf16 without touching memory in between.  Otherwise
+// (GEMM1) the 256 B rows are 256 down-projection columns and the epilogue
+// writes y as bf16.
 //
-// GATE_UP (GEMM0): B rows 0..127 are gate rows n0..n0+127 of expert e and rows
-// 128..255 the matching up rows, so every wave holds gate and up accumulators
-// for the same (row, column) and the epilogue writes h = silu(g) * u as bf16
-// without touching memory in between.  Otherwise (GEMM1) the 256 B rows are
-// 256 down-projection columns and the epilogue writes y as bf16.
+// The MFMA sequence (k-steps of 16 in ascending k, accumulator by
+// accumulator) fixes the float32 result; the staging only changes when data
+// arrive, so every schedule of tiles gives bit-identical outputs.
 #pragma once
+
+#include <type_traits>
 
 #include "moe_internal.h"
 
 namespace moe {
 
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// global -> registers: chunk (tid & 7) of rows (tid >> 3) + 32*i, i < 8
-template <bool GATE_UP>
-__device__ __forceinline__ void tile_gload(u32x4_t (&ra)[8], u32x4_t (&rb)[8], const bf16_t *gA,
-                                           const bf16_t *B0, const bf16_t *B1,
-                                           const int32_t (&offA)[8], const int32_t (&offB)[8],
-                                           int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4_t *>(gA + offA[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bf16_t *Bp = (GATE_UP && i >= 4) ? B1 : B0;
-        rb[i] = *reinterpret_cast<const u32x4_t *>(Bp + offB[i] + k0);
-    }
+// LLVM intrinsic: raw buffer load whose data go to LDS (M0 = LDS base).
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void *lds,
+                                    int size, int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer descriptor over [p, p + bytes): raw (stride 0); lanes whose offset
+// is out of range read zeros.
+__device__ __forceinline__ i32x4_t make_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    i32x4_t r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)(uint32_t)(a >> 32);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
 }
 
-// registers -> one LDS stage (A tile then B tile)
-__device__ __forceinline__ void tile_lstore(bf16_t *stage, int st_off, const u32x4_t (&ra)[8],
-                                            const u32x4_t (&rb)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4_t *>(stage + st_off + i * 32 * BK) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4_t *>(stage + BM * BK + st_off + i * 32 * BK) = rb[i];
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// fragments of k-step s (16 k values) for the 4 A and 4 B row blocks of a wave
-__device__ __forceinline__ void tile_frags(bf16x8_t (&a)[4], bf16x8_t (&b)[4], const bf16_t *stage,
-                                           const int (&arow)[4], const int (&brow)[4], int khalf,
-                                           int s) {
-    const bf16_t *sA = stage;
-    const bf16_t *sB = stage + BM * BK;
-    const int c = 2 * s + khalf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t *>(sA + swz(arow[i], c));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t *>(sB + swz(brow[j], c));
-}
-
+// 16 MFMAs of one k-step.  Row block i is skipped when it holds no valid row
+// of the tile (nblk = valid 32-row blocks of this wave, wave-uniform), so a
+// ragged m-tile with few rows costs a fraction of a full tile.
 __device__ __forceinline__ void tile_mfma(f32x16_t (&acc)[4][4], const bf16x8_t (&a)[4],
-                                          const bf16x8_t (&b)[4]) {
+                                          const bf16x8_t (&b)[4], int nblk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
+        if (i < nblk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// 4 k-steps of 16 over one LDS stage; the fragments of step s+1 are read
-// while the 16 MFMAs of step s run.
-__device__ __forceinline__ void tile_compute(f32x16_t (&acc)[4][4], const bf16_t *stage,
-                                             const int (&arow)[4], const int (&brow)[4],
-                                             int khalf) {
-    // sched_barrier(0) keeps the scheduler from sinking the next reads below
-    // the current MFMAs (it would otherwise do so to save registers).
-    bf16x8_t a0[4], b0[4], a1[4], b1[4];
-    tile_frags(a0, b0, stage, arow, brow, khalf, 0);
-    tile_frags(a1, b1, stage, arow, brow, khalf, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_mfma(acc, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_frags(a0, b0, stage, arow, brow, khalf, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_mfma(acc, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_frags(a1, b1, stage, arow, brow, khalf, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_mfma(acc, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    tile_mfma(acc, a1, b1);
+// Blocked tile order shared by the grouped GEMM launches: m-tiles in groups of
+// GM_GROUP, each group swept n-tile-major, so GM_GROUP m-tiles x a run of
+// n-tiles are in flight together and share their weight and activation tiles
+// in L2.  L in [0, MT*NT) -> (m-tile, n-tile).
+constexpr int GM_GROUP = 4;
+__host__ __device__ __forceinline__ void blocked_tile(int L, int MT, int NT, int *mt, int *nt) {
+    const int g = L / (GM_GROUP * NT);
+    const int r = L - g * (GM_GROUP * NT);
+    const int s = min(GM_GROUP, MT - g * GM_GROUP);
+    *nt = r / s;
+    *mt = g * GM_GROUP + (r - *nt * s);
 }
 
 template <bool GATE_UP>
@@ -103,43 +96,75 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
                                           int a_rows, const bf16_t *__restrict__ B0,
                                           const bf16_t *__restrict__ B1, int64_t ldb, int K,
                                           bf16_t *__restrict__ out, int64_t ldo, int64_t out_col0,
-                                          bf16_t *lds) {
+                                          char *lds) {
     // An opaque copy of the thread index: inside a persistent tile loop this
     // keeps the compiler from hoisting every lane-dependent address out of the
     // loop (which would hold them live across the accumulators and spill).
     int tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    constexpr int STAGE = (BM + BN_TILE) * BK;  // elements per LDS stage
 
-    const int lr0 = tid >> 3;
-    const int lc = tid & 7;
-    const bf16_t *gA = A + a_row0 * lda;
-    int32_t offA[8], offB[8];
+    // DMA sources: instruction i of this wave stages rows (wave*4 + i)*16 +
+    // lane/4, physical chunk lane%4 of each.
+    const int pc = lane & 3;
+    int voffA[4], voffB[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = lr0 + 32 * i;
-        offA[i] = min(r, a_rows - 1) * (int32_t)lda + lc * 8;
+    for (int i = 0; i < 4; ++i) {
+        const int r = (wave * 4 + i) * 16 + (lane >> 2);
+        const int c = pc ^ swz(r);
+        voffA[i] = min(r, a_rows - 1) * (int)lda * 2 + c * 16;
         const int br = GATE_UP ? (r & 127) : r;
-        offB[i] = br * (int32_t)ldb + lc * 8;
+        voffB[i] = br * (int)ldb * 2 + c * 16;
     }
-    const int st_off = swz(lr0, lc);  // row lr0 + 32*i adds i*32*BK (same xor)
+    const i32x4_t rsA = make_rsrc(A + a_row0 * lda, (uint32_t)(a_rows * lda * 2));
+    const bf16_t *Bw = (GATE_UP && wave >= 2) ? B1 : B0;  // waves 2,3 stage the up rows
+    const i32x4_t rsB = make_rsrc(Bw, (uint32_t)((GATE_UP ? 128 : 256) * ldb * 2));
+    const int ldsA_w = wave * 4 * 1024;
+    const int ldsB_w = STAGE_A_BYTES + wave * 4 * 1024;
 
+    auto issue = [&](int s) {
+        const int kb = s * BK * 2;  // byte offset along K
+        char *st = lds + (s & (NSTAGE - 1)) * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            raw_buffer_load_lds(
+                rsA, (__attribute__((address_space(3))) void *)(uintptr_t)(st + ldsA_w + i * 1024),
+                16, voffA[i], kb, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            raw_buffer_load_lds(
+                rsB, (__attribute__((address_space(3))) void *)(uintptr_t)(st + ldsB_w + i * 1024),
+                16, voffB[i], kb, 0, 0);
+    };
+
+    // Fragment of a 32x32x16 MFMA: lane l reads row l%32 of its 32-row block,
+    // logical chunk 2*kstep + l/32.  swz(blk*32 + l%32) == swz(l%32).
     const int l32 = lane & 31;
     const int khalf = lane >> 5;
+    const int sw = swz(l32);
+    const int fo0 = l32 * STAGE_ROW_BYTES + (((0 + khalf) ^ sw) << 4);
+    const int fo1 = l32 * STAGE_ROW_BYTES + (((2 + khalf) ^ sw) << 4);
     int arow[4], brow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) arow[i] = wm * 128 + i * 32 + l32;
+    for (int i = 0; i < 4; ++i) arow[i] = (wm * 128 + i * 32) * STAGE_ROW_BYTES;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (GATE_UP)
-            brow[j] = (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32) + l32;
+            brow[j] = STAGE_A_BYTES +
+                      (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32) * STAGE_ROW_BYTES;
         else
-            brow[j] = wn * 128 + j * 32 + l32;
+            brow[j] = STAGE_A_BYTES + (wn * 128 + j * 32) * STAGE_ROW_BYTES;
     }
+    auto frags = [&](bf16x8_t (&a)[4], bf16x8_t (&b)[4], int s, int fo) {
+        const char *st = lds + (s & (NSTAGE - 1)) * STAGE_BYTES + fo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t *>(st + arow[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8_t *>(st + brow[j]);
+    };
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -149,22 +174,51 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    u32x4_t ra[8], rb[8];
-    const int KT = K / BK;
-    tile_gload<GATE_UP>(ra, rb, gA, B0, B1, offA, offB, 0);
-    tile_lstore(lds, st_off, ra, rb);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
-        bf16_t *cur = lds + (kt & 1) * STAGE;
-        bf16_t *nxt = lds + ((kt + 1) & 1) * STAGE;
-        if (more) tile_gload<GATE_UP>(ra, rb, gA, B0, B1, offA, offB, (kt + 1) * BK);
-        tile_compute(acc, cur, arow, brow, khalf);
-        if (more) tile_lstore(nxt, st_off, ra, rb);
-        __syncthreads();
-    }
+    // valid 32-row blocks of this wave (wave-uniform)
+    const int nblk = __builtin_amdgcn_readfirstlane(max(0, min(4, (a_rows - wm * 128 + 31) >> 5)));
 
-    // epilogue.  Accumulator v of lane l in a 32x32 tile sits at
+    // Pipeline.  Stage s lives in LDS slot s % 4.  Before stage s+1 is read,
+    // each wave waits for its own DMA of that stage (the later stage may stay
+    // in flight) and the barrier publishes every wave's part; the same barrier
+    // certifies that all waves are done with slot (s-1) % 4, which the DMA of
+    // stage s+3 then overwrites.  The last three steps are peeled so the loop
+    // body has no branch: at a join of paths with different outstanding LDS
+    // reads the compiler would wait for the prefetched fragments before the
+    // second k-step's MFMAs instead of letting them overlap.
+    const int KT = K / BK;  // >= 4 for every supported shape (K % 128 == 0)
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vmcnt<16>();
+    __syncthreads();
+    bf16x8_t a0[4], b0[4], a1[4], b1[4];
+    frags(a0, b0, 0, fo0);
+    auto step = [&](int s, auto wait_all, auto do_issue, auto has_next) {
+        frags(a1, b1, s, fo1);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_mfma(acc, a0, b0, nblk);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(has_next)::value) {
+            if constexpr (decltype(wait_all)::value)
+                wait_vmcnt<0>();
+            else
+                wait_vmcnt<8>();
+            __syncthreads();
+            if constexpr (decltype(do_issue)::value) issue(s + 3);
+            frags(a0, b0, s + 1, fo0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        tile_mfma(acc, a1, b1, nblk);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    for (int s = 0; s < KT - 3; ++s) step(s, no{}, yes{}, yes{});
+    step(KT - 3, no{}, no{}, yes{});
+    step(KT - 2, yes{}, no{}, yes{});
+    step(KT - 1, yes{}, no{}, no{});
+
+    // Epilogue.  Accumulator v of lane l in a 32x32 tile sits at
     // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
     bf16_t *o = out + a_row0 * ldo + out_col0;
 #pragma unroll

@@ -1,9 +1,9 @@
 // Persistent expert-FFN + combine kernel of moe_layer.
 //
 // One workgroup per CU stays resident and claims tiles until none are left
-// (Weave, §4: a persistent kernel in which each SM "claims its next tile via
-// atomicAdd on a global counter following the chunk pipeline DAG order").
-// Three tile kinds, claimed in dependency order:
+// (Weave, §4: a persistent kernel in which each SM claims its next tile with
+// an atomicAdd on a global counter, in the order of the chunk pipeline's
+// dependency graph).  Three tile kinds, claimed in dependency order:
 //   1. gate/up tiles (m-tile, 128 h columns): GEMM0 + SiLU-mul epilogue;
 //      each finished tile bumps gu_done[m-tile].
 //   2. down tiles (m-tile, 256 y columns): wait until gu_done[m-tile] counts
@@ -15,20 +15,29 @@
 // side flag as soon as it is written (the producer-consumer tile signaling of
 // Cui et al., abstract), not at a kernel boundary.
 //
-// Queues: each kind is numbered n-tile-major and split into 8 contiguous
-// ranges, one per XCD (workgroup b runs on XCD b % 8), so the m-tiles that
-// share a weight tile run in one XCD's L2.  A workgroup first drains its own
-// XCD's range, then steals from the others, and moves to the next kind only
-// when every range of the current kind is claimed.  Deadlock freedom: a tile
-// waits only on tiles of an earlier kind, all of which were claimed earlier by
-// running workgroups whose own waits are, inductively, satisfiable.
+// Queues: gate/up and down tiles follow the blocked order of gemm_tile.h and
+// each kind is split into 8 contiguous ranges, one per XCD.  A workgroup reads
+// the XCD it runs on from the hardware (XCC_ID), drains that XCD's range
+// first (so the tiles sharing weight and activation tiles meet in one L2),
+// then steals from the others, and moves to the next kind only when every
+// range of the current kind is claimed.  Deadlock freedom: a tile waits only
+// on tiles of an earlier kind, all of which were claimed earlier by running
+// workgroups whose own waits are, inductively, satisfiable.
 //
-// Memory ordering: producers fence (release, agent scope) before a barrier and
-// a release-add/store of the counter; consumers poll with relaxed loads, then
-// a barrier and an acquire fence at agent scope in every wave, which makes the
-// data written on another XCD visible.  Polling is bounded in time: a wait
-// that exceeds the timeout records MOE_ERR_DEVICE_TIMEOUT in the status word
-// and carries on (the result is then invalid, but the kernel drains).
+// Memory ordering (MI355X: one L2 per XCD; an agent-scope release writes the
+// issuing XCD's L2 back, an agent-scope acquire invalidates it):
+//  - producers: each wave waits for its stores, the workgroup meets at a
+//    barrier, then one wave publishes with a single agent-scope release RMW;
+//  - gate/up producers also OR their XCD into gu_xcd[m-tile].  A down tile
+//    whose producers all ran on its own XCD reads h through the shared L2 and
+//    only invalidates the CU's L1; otherwise it takes the agent-scope acquire.
+//    The blocked queues keep most chains inside one XCD, so most down tiles
+//    leave the other workgroups' L2 contents alone;
+//  - combine tiles read y with device-coherent (agent-scope atomic) loads, so
+//    they never invalidate L2 either.
+// Polling is bounded in time: a wait that exceeds the timeout records
+// MOE_ERR_DEVICE_TIMEOUT in the status word and carries on (the result is
+// then invalid, but the kernel drains).
 #include "combine_tile.h"
 #include "gemm_tile.h"
 
@@ -46,6 +55,13 @@ namespace {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The XCD this wave runs on (hardware register XCC_ID).
+__device__ __forceinline__ int hw_xcd() {
+    int id;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(id));
+    return id & (NUM_XCD - 1);
+}
 
 // Claim one tile of [0, n) for the calling wave.  Queue y covers
 // [y*per, y*per + per); the own XCD's queue first, then the others.
@@ -98,31 +114,54 @@ __device__ __forceinline__ void wave_wait_geq(const int32_t *p, int32_t target, 
     }
 }
 
-__device__ __forceinline__ void acquire_all() {
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-// All stores of the workgroup become visible at agent scope, then wave 0
-// bumps (add) or sets (store 1) the counter with release semantics.
-__device__ __forceinline__ void release_then(int32_t *p, bool add) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Publish a finished tile: every wave's stores have completed (reached L2)
+// before the barrier; then wave 0 optionally records its XCD in *xmask and
+// bumps (add) or sets (store 1) the counter with one agent-scope release,
+// which writes this XCD's L2 back first.
+__device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, int xcd) {
+    wait_vmcnt<0>();
     __syncthreads();
     if (wave_id() == 0) {
+        const bool l0 = lane_id() == 0;
+        if (xmask)
+            __hip_atomic_fetch_or(xmask, l0 ? (1 << xcd) : 0, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
         if (add)
-            __hip_atomic_fetch_add(p, lane_id() == 0 ? 1 : 0, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(p, l0 ? 1 : 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         else
             __hip_atomic_store(p, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+__device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// Optional per-tile trace (measurement aid): one 4 x int64 record per tile,
+// {kind << 32 | tile, workgroup << 8 | xcd, start, end}, times in
+// wall_clock64 ticks.  Written by lane 0 of wave 0; slots come from an atomic
+// counter at trace[0]; records past the capacity are dropped.
+__device__ __forceinline__ void trace_tile(const LayerArgs &a, int kind, int L, int xcd,
+                                           int64_t t0) {
+    if (!a.trace) return;
+    const int64_t t1 = (int64_t)wall_clock64();
+    if (wave_id() == 0 && lane_id() == 0) {
+        const int64_t i = __hip_atomic_fetch_add(a.trace, (int64_t)1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        if (i < a.trace_cap) {
+            int64_t *r = a.trace + 1 + 4 * i;
+            r[0] = ((int64_t)kind << 32) | (int64_t)L;
+            r[1] = ((int64_t)blockIdx.x << 8) | xcd;
+            r[2] = t0;
+            r[3] = t1;
+        }
+    }
+}
+
 template <bool OUT_F32>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
-    extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+    extern __shared__ __attribute__((aligned(16))) char lds[];
     __shared__ int s_claim;
     const Dims &D = a.D;
-    const int xcd = blockIdx.x % NUM_XCD;
+    const int xcd = hw_xcd();
     const int MT = *a.n_mtiles;
     const int NT1 = (int)D.nt_gu();
     const int NT2 = (int)D.nt_dn();
@@ -134,12 +173,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
         for (;;) {
             const int L = next_tile(a.queues, n1, xcd, &s_claim);
             if (L < 0) break;
-            const int nt = L / MT, mt = L % MT;
+            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+            int mt, nt;
+            blocked_tile(L, MT, NT1, &mt, &nt);
             const MTile t = a.mtiles[mt];
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
             gemm_tile<true>(a.x_perm, d, t.row0, t.rows, a.w_gate + wo, a.w_up + wo, d, (int)d,
                             a.h, f, (int64_t)nt * BN_GU, lds);
-            release_then(a.gu_done + mt, true);
+            publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
+            trace_tile(a, 1, L, xcd, t0);
         }
 
     // 2. down tiles
@@ -148,14 +190,23 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
         for (;;) {
             const int L = next_tile(a.queues + NUM_XCD * QSTRIDE, n2, xcd, &s_claim);
             if (L < 0) break;
-            const int nt = L / MT, mt = L % MT;
+            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+            int mt, nt;
+            blocked_tile(L, MT, NT2, &mt, &nt);
             const MTile t = a.mtiles[mt];
             if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
-            acquire_all();
+            __syncthreads();
+            const int producers =
+                uniform(__hip_atomic_load(a.gu_xcd + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if (producers & ~(1 << xcd))
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            else
+                invalidate_l1();
             const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
             gemm_tile<false>(a.h, f, t.row0, t.rows, a.w_down + wo, nullptr, f, (int)f, a.y, d,
                              (int64_t)nt * BN_DN, lds);
-            release_then(a.dn_flag + (int64_t)mt * NT2 + nt, false);
+            publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
+            trace_tile(a, 2, L, xcd, t0);
         }
 
     // 3. combine tiles
@@ -165,6 +216,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
         for (;;) {
             const int L = next_tile(a.queues + 2 * NUM_XCD * QSTRIDE, n3, xcd, &s_claim);
             if (L < 0) break;
+            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             const int nt = L / NTB, tb = L % NTB;
             // every (token, slot) of the tile waits for the down tile holding its row
             for (int base = 0; base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
@@ -184,13 +236,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 }
                 wave_wait_geq(flag, 1, need, a.wait_ticks, a.status);
             }
-            acquire_all();
+            __syncthreads();
             for (int i = threadIdx.x; i < COMB_TOK * (BN_DN / 8); i += GEMM_THREADS) {
                 const int64_t t = (int64_t)tb * COMB_TOK + i / (BN_DN / 8);
                 if (t >= D.T) continue;
                 const int64_t v = (int64_t)nt * (BN_DN / 8) + i % (BN_DN / 8);
-                combine_vec<OUT_F32>(t, v, d, k, a.y, a.inv_perm, a.gates, a.out);
+                combine_vec<OUT_F32, true>(t, v, d, k, a.y, a.inv_perm, a.gates, a.out);
             }
+            trace_tile(a, 3, L, xcd, t0);
         }
 }
 

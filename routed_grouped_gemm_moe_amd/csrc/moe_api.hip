@@ -28,6 +28,7 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.status = take(layer ? 256 : 0);
     L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
+    L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
@@ -55,6 +56,8 @@ namespace {
 
 std::mutex g_mu;
 int64_t g_wait_us = 2000000;  // device flag-wait timeout
+int64_t *g_trace = nullptr;   // per-tile trace buffer of moe_layer (device), or null
+int64_t g_trace_cap = 0;
 bool g_timing = false;
 struct CallEvents {
     hipEvent_t ev[4];
@@ -224,10 +227,14 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     int64_t wait_us;
     CallEvents ce{};
     bool timing;
+    int64_t *trace;
+    int64_t trace_cap;
     {
         std::lock_guard<std::mutex> lk(g_mu);
         wait_us = g_wait_us;
         timing = g_timing;
+        trace = g_trace;
+        trace_cap = g_trace_cap;
         if (timing)
             for (int i = 0; i < 4; ++i) ce.ev[i] = pool_event();
     }
@@ -274,11 +281,14 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.mtiles = mt;
         a.queues = at<int32_t>(ws, L.queues);
         a.gu_done = at<int32_t>(ws, L.gu_done);
+        a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
         a.dn_flag = at<int32_t>(ws, L.dn_flag);
         a.status = at<int32_t>(ws, L.status);
         a.out = out;
         a.out_f32 = out_dtype == MOE_F32;
         a.wait_ticks = wait_us * (wall_clock_hz() / 1000000);
+        a.trace = trace;
+        a.trace_cap = trace_cap;
         e = launch_layer_persistent(a, grid, s);
     }
     mark(3);
@@ -338,6 +348,14 @@ int moe_timing_read(float *stage_ms, int n_stages) {
     for (int i = 0; i < n_stages && i < 3; ++i) stage_ms[i] = n ? (float)(sum[i] / n) : 0.0f;
     return n;
 }
+
+void moe_set_trace(void *buf, int64_t n_records) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_trace = (buf && n_records > 0) ? (int64_t *)buf : nullptr;
+    g_trace_cap = g_trace ? n_records : 0;
+}
+
+int64_t moe_wall_clock_hz(void) { return wall_clock_hz(); }
 
 void moe_set_wait_timeout_us(int64_t us) {
     std::lock_guard<std::mutex> lk(g_mu);

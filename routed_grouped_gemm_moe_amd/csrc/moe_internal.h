@@ -12,15 +12,20 @@
 namespace moe {
 
 // ---------------------------------------------------------------- tiles
-// Grouped GEMM tile: BM rows x BN_TILE output columns x BK per LDS stage,
-// 256 threads = 4 waves in a 2x2 grid, each wave 128x128 with 32x32x16 MFMAs.
+// Grouped GEMM tile: BM rows x BN_TILE output columns, K staged BK at a time
+// through an NSTAGE-deep LDS ring; 256 threads = 4 waves in a 2x2 grid, each
+// wave 128x128 with 32x32x16 MFMAs.
 constexpr int BM = 256;
-constexpr int BK = 64;
+constexpr int BK = 32;
+constexpr int NSTAGE = 4;
 constexpr int BN_TILE = 256;          // B rows staged per tile
 constexpr int BN_GU = 128;            // gate (and up) columns per gate/up tile
 constexpr int BN_DN = 256;            // down columns per down tile
 constexpr int GEMM_THREADS = 256;
-constexpr int GEMM_LDS_BYTES = 2 * (BM * BK + BN_TILE * BK) * 2;  // 128 KiB, double buffered
+constexpr int STAGE_ROW_BYTES = BK * 2;                 // 64
+constexpr int STAGE_A_BYTES = BM * STAGE_ROW_BYTES;     // 16 KiB
+constexpr int STAGE_BYTES = STAGE_A_BYTES + BN_TILE * STAGE_ROW_BYTES;  // 32 KiB
+constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;    // 128 KiB
 
 // Permute: tokens per block of the histogram / rank kernels.
 constexpr int PERM_TB = 256;
@@ -74,7 +79,7 @@ struct MTile {
 
 // Byte offsets of every region in a workspace (each 256-byte aligned).
 struct Layout {
-    size_t status, queues, gu_done, dn_flag, ids, gates, blk_counts, blk_base, counts, offsets,
+    size_t status, queues, gu_done, gu_xcd, dn_flag, ids, gates, blk_counts, blk_base, counts, offsets,
         perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm, h, y, total;
 };
 
@@ -119,10 +124,12 @@ struct LayerArgs {
     const int32_t *ids, *inv_perm, *offsets, *mtile_base, *n_mtiles;
     const float *gates;
     const MTile *mtiles;
-    int32_t *queues, *gu_done, *dn_flag, *status;
+    int32_t *queues, *gu_done, *gu_xcd, *dn_flag, *status;
     void *out;
     int out_f32;
     int64_t wait_ticks;  // flag-wait timeout in wall_clock64 ticks
+    int64_t *trace;      // optional per-tile trace: [0] = record count, then records
+    int64_t trace_cap;   // records that fit after the count
 };
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s);
 int layer_grid_size();  // resident workgroups of the persistent kernel (cached)

@@ -234,3 +234,31 @@ def test_full_size_workload(name):
     _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
     del t, xp, y, staged
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,hot", [("spread", None), ("one_hot_expert", 3)])
+def test_fused_visibility_poisoned_workspace_alternating_inputs(name, hot):
+    # Two different inputs through one workspace whose scratch regions start
+    # as NaN bytes: a tile that read a row before its producer's write was
+    # visible would carry NaNs or the previous input's values into the output,
+    # so fused must equal staged bit for bit on both calls.
+    base = W.CONFIGS["tiny"].scaled(name=name, T=2048, d=512, f=512, E=8, k=2)
+    D = _dims(base)
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    for seed in (21, 22):
+        cfg = base.scaled(seed=seed)
+        bias = _bias_all_to_one(8, hot) if hot is not None else None
+        arrs = W.generate(cfg, bias_override=bias)
+        t = upload(cfg, arrs)
+        say(f"moe_layer poisoned ws {name} seed={seed}")
+        out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
+                          ws=ws)
+        assert M.moe_device_status(D, ws) == 0
+        ids, gates, _ = M.moe_route(D, t["x"], t["w_router"], t["bias"], want_logits=True)
+        counts, offsets, perm, inv, xp = M.moe_permute(D, t["x"], ids)
+        y = M.moe_expert_ffn(D, xp, offsets, t["w_gate"], t["w_up"], t["w_down"])
+        staged = M.moe_combine(D, y, inv, gates)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out.float()).any()
+        assert torch.equal(out.view(torch.int16), staged.view(torch.int16)), "fused != staged"
