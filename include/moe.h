@@ -86,9 +86,19 @@ int moe_version(void);
  *   topk_ids i32  [T, k]  out  selected expert ids, by (logit desc, id asc)
  *   topk_w   f32  [T, k]  out  renormalised softmax gates of those experts
  *   logits   f32  [T, E]  out, optional (NULL to skip)
+ *   ws, ws_bytes               workspace of moe_route_workspace_bytes(dims)
+ *                              bytes (256-byte aligned), or NULL
+ * For E > 16 a workspace enables the fast path: MFMA logits with a rigorous
+ * rounding-error bound pick the candidate experts, whose logits are then
+ * evaluated in the defined order; ids and gates are the same as when every
+ * logit is evaluated in that order, which is what happens with logits != NULL
+ * or without a workspace (slower).  moe_route_workspace_bytes returns 0 when
+ * no workspace is used.
  */
+size_t moe_route_workspace_bytes(const moe_dims *dims);
 moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
-                     int32_t *topk_ids, float *topk_w, float *logits, void *stream);
+                     int32_t *topk_ids, float *topk_w, float *logits, void *ws, size_t ws_bytes,
+                     void *stream);
 
 /* ---- moe_permute: dispatch into expert-contiguous rows (Weave §2.1 stage
  * 1, Figure 3; on one GPU the "send" is a gather; each source row is read

@@ -20,6 +20,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MoEDims", "lib_path", "load", "exported_abi_names", "header_abi_names",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+    "moe_route_workspace_bytes",
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
     "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "moe_set_trace",
@@ -71,7 +72,8 @@ def load():
     sig = {
         "moe_status_string": ([i32], C.c_char_p),
         "moe_version": ([], i32),
-        "moe_route": ([dp, vp, vp, vp, vp, vp, vp, vp], i32),
+        "moe_route_workspace_bytes": ([dp], sz),
+        "moe_route": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_permute_workspace_bytes": ([dp], sz),
         "moe_permute": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_expert_ffn_workspace_bytes": ([dp], sz),
@@ -149,6 +151,10 @@ def moe_status_string(status: int) -> str:
     return load().moe_status_string(int(status)).decode()
 
 
+def moe_route_workspace_bytes(dims) -> int:
+    return int(load().moe_route_workspace_bytes(C.byref(_dims(dims))))
+
+
 def moe_permute_workspace_bytes(dims) -> int:
     return int(load().moe_permute_workspace_bytes(C.byref(_dims(dims))))
 
@@ -162,8 +168,12 @@ def moe_layer_workspace_bytes(dims) -> int:
 
 
 def moe_route(dims, x, w_router, bias=None, topk_ids=None, topk_w=None, logits=None,
-              want_logits: bool = False, stream=None):
-    """Top-k gating.  Returns (topk_ids int32 [T,k], topk_w f32 [T,k], logits or None)."""
+              want_logits: bool = False, ws=None, use_workspace: bool = True, stream=None):
+    """Top-k gating.  Returns (topk_ids int32 [T,k], topk_w f32 [T,k], logits or None).
+
+    A workspace (allocated here when not given and use_workspace is true)
+    enables the fast path for E > 16; without one every logit is evaluated in
+    the defined order.  Both give the same ids and gates."""
     import torch
     D = _dims(dims)
     dev = x.device
@@ -177,8 +187,12 @@ def moe_route(dims, x, w_router, bias=None, topk_ids=None, topk_w=None, logits=N
         topk_w = torch.empty((D.T, D.k), dtype=torch.float32, device=dev)
     if logits is None and want_logits:
         logits = torch.empty((D.T, D.E), dtype=torch.float32, device=dev)
+    if ws is None and use_workspace:
+        nb = moe_route_workspace_bytes(D)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
     rc = load().moe_route(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
-                          _ptr(topk_w), _ptr(logits), _stream(stream))
+                          _ptr(topk_w), _ptr(logits), _ptr(ws),
+                          ws.numel() if ws is not None else 0, _stream(stream))
     _check(rc, "moe_route")
     return topk_ids, topk_w, logits
 

@@ -15,24 +15,43 @@ __device__ __forceinline__ void combine_vec(int64_t t, int64_t v, int64_t d, int
                                             const bf16_t *__restrict__ y,
                                             const int32_t *__restrict__ inv_perm,
                                             const float *__restrict__ gates, void *__restrict__ out) {
+    // Slots are taken in batches of 8: the indices, gates and rows of a batch
+    // are all loaded before the first is used, so up to 8 row loads per lane
+    // are in flight; the float32 sum still runs over j ascending.
+    constexpr int SB = 8;
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int64_t j = 0; j < k; ++j) {
-        const int32_t p = inv_perm[t * k + j];
-        if (p < 0) continue;
-        const float w = gates[t * k + j];
-        u32x4_t yv;
-        if (COHERENT) {
-            const uint64_t *q = reinterpret_cast<const uint64_t *>(y + (int64_t)p * d) + 2 * v;
-            const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            yv = u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-        } else {
-            yv = reinterpret_cast<const u32x4_t *>(y + (int64_t)p * d)[v];
+    for (int64_t j0 = 0; j0 < k; j0 += SB) {
+        int32_t p[SB];
+        float w[SB];
+        u32x4_t yv[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int64_t j = j0 + u;
+            p[u] = j < k ? inv_perm[t * k + j] : -1;
+            w[u] = p[u] >= 0 ? gates[t * k + j] : 0.0f;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w, bf16x8_elem(yv, q), acc[q]);
+        for (int u = 0; u < SB; ++u) {
+            yv[u] = u32x4_t{0u, 0u, 0u, 0u};
+            if (p[u] < 0) continue;
+            if (COHERENT) {
+                const uint64_t *q = reinterpret_cast<const uint64_t *>(y + (int64_t)p[u] * d) + 2 * v;
+                const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t hi =
+                    __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                yv[u] = u32x4_t{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+            } else {
+                yv[u] = reinterpret_cast<const u32x4_t *>(y + (int64_t)p[u] * d)[v];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            if (p[u] < 0) continue;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(w[u], bf16x8_elem(yv[u], q), acc[q]);
+        }
     }
     if (OUT_F32) {
         typedef float f32x4v __attribute__((ext_vector_type(4)));

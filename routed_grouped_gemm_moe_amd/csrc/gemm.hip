@@ -76,11 +76,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     if (GATE_UP) {
         const bf16_t *wg = W0 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
         const bf16_t *wu = W1 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
-        gemm_tile<true>(A, d, t.row0, t.rows, wg, wu, d, (int)d, out, f, (int64_t)nt * BN_GU, lds);
+        gemm_tile<EPI_SILU_BF16>(A, d, t.row0, t.rows, wg, wu, d, BN_GU, (int)d, out, f,
+                                 (int64_t)nt * BN_GU, BN_GU, lds);
     } else {
         const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
-        gemm_tile<false>(A, f, t.row0, t.rows, wd, nullptr, f, (int)f, out, d, (int64_t)nt * BN_DN,
-                         lds);
+        gemm_tile<EPI_BF16>(A, f, t.row0, t.rows, wd, nullptr, f, BN_DN, (int)f, out, d,
+                            (int64_t)nt * BN_DN, BN_DN, lds);
     }
 }
 

@@ -91,12 +91,21 @@ __host__ __device__ __forceinline__ void blocked_tile(int L, int MT, int NT, int
     *mt = g * GM_GROUP + (r - *nt * s);
 }
 
-template <bool GATE_UP>
+// Epilogues: h = silu(g) * u as bf16 (gate/up, dual B), y as bf16 (down),
+// or the raw float32 accumulators (router logit partials; columns >= out_cols
+// are not stored).
+enum { EPI_SILU_BF16 = 0, EPI_BF16 = 1, EPI_F32 = 2 };
+
+// A: a_rows rows from a_row0, stride lda; B0 (and B1 for the dual-B tile):
+// b_rows valid rows each, stride ldb; K columns of both are used.  The buffer
+// descriptors cover exactly the bytes those rows and columns span.
+template <int EPI>
 __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t lda, int64_t a_row0,
                                           int a_rows, const bf16_t *__restrict__ B0,
-                                          const bf16_t *__restrict__ B1, int64_t ldb, int K,
-                                          bf16_t *__restrict__ out, int64_t ldo, int64_t out_col0,
-                                          char *lds) {
+                                          const bf16_t *__restrict__ B1, int64_t ldb, int b_rows,
+                                          int K, void *__restrict__ out, int64_t ldo,
+                                          int64_t out_col0, int out_cols, char *lds) {
+    constexpr bool GATE_UP = EPI == EPI_SILU_BF16;
     // An opaque copy of the thread index: inside a persistent tile loop this
     // keeps the compiler from hoisting every lane-dependent address out of the
     // loop (which would hold them live across the accumulators and spill).
@@ -117,11 +126,12 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
         const int c = pc ^ swz(r);
         voffA[i] = min(r, a_rows - 1) * (int)lda * 2 + c * 16;
         const int br = GATE_UP ? (r & 127) : r;
-        voffB[i] = br * (int)ldb * 2 + c * 16;
+        voffB[i] = min(br, b_rows - 1) * (int)ldb * 2 + c * 16;
     }
-    const i32x4_t rsA = make_rsrc(A + a_row0 * lda, (uint32_t)(a_rows * lda * 2));
+    const i32x4_t rsA =
+        make_rsrc(A + a_row0 * lda, (uint32_t)(((int64_t)(a_rows - 1) * lda + K) * 2));
     const bf16_t *Bw = (GATE_UP && wave >= 2) ? B1 : B0;  // waves 2,3 stage the up rows
-    const i32x4_t rsB = make_rsrc(Bw, (uint32_t)((GATE_UP ? 128 : 256) * ldb * 2));
+    const i32x4_t rsB = make_rsrc(Bw, (uint32_t)(((int64_t)(b_rows - 1) * ldb + K) * 2));
     const int ldsA_w = wave * 4 * 1024;
     const int ldsB_w = STAGE_A_BYTES + wave * 4 * 1024;
 
@@ -220,25 +230,33 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
 
     // Epilogue.  Accumulator v of lane l in a 32x32 tile sits at
     // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
-    bf16_t *o = out + a_row0 * ldo + out_col0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * khalf + (v & 3);
             if (r >= a_rows) continue;
-            if (GATE_UP) {
+            const int64_t orow = (a_row0 + r) * ldo + out_col0;
+            if (EPI == EPI_SILU_BF16) {
+                bf16_t *o = reinterpret_cast<bf16_t *>(out) + orow;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float g = acc[i][j][v];
                     const float u = acc[i][j + 2][v];
                     const float h = g / (1.0f + __expf(-g)) * u;
-                    o[(int64_t)r * ldo + wn * 64 + j * 32 + l32] = f2bf(h);
+                    o[wn * 64 + j * 32 + l32] = f2bf(h);
                 }
-            } else {
+            } else if (EPI == EPI_BF16) {
+                bf16_t *o = reinterpret_cast<bf16_t *>(out) + orow;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    o[(int64_t)r * ldo + wn * 128 + j * 32 + l32] = f2bf(acc[i][j][v]);
+                for (int j = 0; j < 4; ++j) o[wn * 128 + j * 32 + l32] = f2bf(acc[i][j][v]);
+            } else {
+                float *o = reinterpret_cast<float *>(out) + orow;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int col = wn * 128 + j * 32 + l32;
+                    if (col < out_cols) o[col] = acc[i][j][v];
+                }
             }
         }
     }

@@ -178,8 +178,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             blocked_tile(L, MT, NT1, &mt, &nt);
             const MTile t = a.mtiles[mt];
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
-            gemm_tile<true>(a.x_perm, d, t.row0, t.rows, a.w_gate + wo, a.w_up + wo, d, (int)d,
-                            a.h, f, (int64_t)nt * BN_GU, lds);
+            gemm_tile<EPI_SILU_BF16>(a.x_perm, d, t.row0, t.rows, a.w_gate + wo, a.w_up + wo, d,
+                                     BN_GU, (int)d, a.h, f, (int64_t)nt * BN_GU, BN_GU, lds);
             publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
             trace_tile(a, 1, L, xcd, t0);
         }
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             else
                 invalidate_l1();
             const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
-            gemm_tile<false>(a.h, f, t.row0, t.rows, a.w_down + wo, nullptr, f, (int)f, a.y, d,
-                             (int64_t)nt * BN_DN, lds);
+            gemm_tile<EPI_BF16>(a.h, f, t.row0, t.rows, a.w_down + wo, nullptr, f, BN_DN, (int)f,
+                                a.y, d, (int64_t)nt * BN_DN, BN_DN, lds);
             publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
             trace_tile(a, 2, L, xcd, t0);
         }

@@ -30,6 +30,7 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
+    L.route = take(layer ? route_workspace_bytes(D) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
     L.blk_counts = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
@@ -118,16 +119,24 @@ const char *moe_status_string(moe_status s) {
 
 int moe_version(void) { return 100; }
 
+size_t moe_route_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims(dims, &D) != MOE_OK) return 0;
+    return route_workspace_bytes(D);
+}
+
 moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
-                     int32_t *topk_ids, float *topk_w, float *logits, void *stream) {
+                     int32_t *topk_ids, float *topk_w, float *logits, void *ws, size_t ws_bytes,
+                     void *stream) {
     Dims D;
     moe_status st = check_dims(dims, &D);
     if (st != MOE_OK) return st;
     if (D.T == 0) return MOE_OK;
     if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (ws && ((uintptr_t)ws & 255u) != 0) return MOE_ERR_WORKSPACE;
     return hip_status(launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, topk_ids,
-                                   topk_w, logits, (hipStream_t)stream));
+                                   topk_w, logits, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_bytes(const moe_dims *dims) {
@@ -255,7 +264,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
 
     mark(0);
     hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
-                                nullptr, s);
+                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s);
     mark(1);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,

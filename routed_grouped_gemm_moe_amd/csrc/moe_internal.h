@@ -79,7 +79,7 @@ struct MTile {
 
 // Byte offsets of every region in a workspace (each 256-byte aligned).
 struct Layout {
-    size_t status, queues, gu_done, gu_xcd, dn_flag, ids, gates, blk_counts, blk_base, counts, offsets,
+    size_t status, queues, gu_done, gu_xcd, dn_flag, route, ids, gates, blk_counts, blk_base, counts, offsets,
         perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm, h, y, total;
 };
 
@@ -93,8 +93,16 @@ __host__ __device__ inline T *at(void *ws, size_t off) {
 
 // ---------------------------------------------------------------- launches
 // All return hipSuccess or the launch error.
+// Router.  With logits != NULL, or without a large enough workspace when the
+// fast path applies, every logit is evaluated in the defined order; otherwise
+// E <= 16 uses the LDS-staged exact kernel and E > 16 the MFMA + exact-refine
+// fast path (same ids and gates).
+size_t route_workspace_bytes(const Dims &D);
+bool route_uses_fast_path(const Dims &D);
+int route_splits(const Dims &D);
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
-                        int32_t *ids, float *gates, float *logits, hipStream_t s);
+                        int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
+                        hipStream_t s);
 
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,

@@ -1,26 +1,96 @@
 // Router: top-k gating (Weave, §2.1: a learned gate sends each token to k
-// experts; Figure 3 shows top-k routing).  One workgroup handles 16 tokens.
+// experts; Figure 3 shows top-k routing).
 //
 // Logit arithmetic (fixed by this library so ids are reproducible bit for
-// bit): a 256-thread workgroup is 16 chunk lanes x 16 slots.  Lane c of a slot
-// sums its chunk [c*d/16, (c+1)*d/16) of the hidden dimension sequentially in
-// float32 (each bf16*bf16 product is exact, so the fma equals multiply-then-
-// add), and the 16 chunk sums are folded with xor-shuffles 1, 2, 4, 8 -- the
-// balanced pairwise tree ((s0+s1)+(s2+s3))+... -- before the bias is added.
-// Selection is k rounds of a wave-wide argmax (ties to the lower expert id);
-// gates are the float32 softmax over the selected logits.
-#include "moe_internal.h"
+// bit): logit[t,e] is a float32 sum over 16 equal contiguous chunks of the
+// hidden dimension, each chunk summed sequentially from +0 in ascending index
+// (each bf16*bf16 product is exact, so the fma equals multiply-then-add), the
+// 16 chunk sums folded by the balanced pairwise tree ((s0+s1)+(s2+s3))+...,
+// which is what xor-shuffles 1, 2, 4, 8 over the 16 chunk lanes produce, then
+// the bias added.  Selection is k rounds of a wave-wide argmax over
+// (logit desc, id asc); gates are the float32 softmax over the selected
+// logits.
+//
+// Three implementations of that one definition:
+//  - route_exact_kernel: every logit in the defined order (also the optional
+//    logits output).  Used for the logits output and when no workspace is given.
+//  - route_small_kernel (E <= 16): the same, with W_r staged in LDS and the
+//    activations prefetched, so it runs at memory speed.
+//  - fast path (E > 16, with a workspace): bf16 MFMA logits (split-K float32
+//    partials) are an approximation l~ with |l~ - l| <= eps, eps bounded from
+//    ||x_t||, ||w_e|| and the float32 unit roundoff (any summation order of d
+//    products errs by at most d*u*sum|x_i w_i| <= d*u*||x||*||w||).  An expert
+//    whose upper bound l~ + eps is below the k-th largest lower bound l~ - eps
+//    has at least k experts strictly above it and cannot be selected; the
+//    remaining candidates (typically k plus a few) get their logits evaluated
+//    in the defined order, and the selection and gates are taken from those
+//    exact values.  Ids and gates are therefore identical to the exact path.
+#include "gemm_tile.h"
 
 namespace moe {
 namespace {
 
-constexpr int RT_TOK = 16;       // tokens per workgroup
-constexpr int RT_THREADS = 256;  // 16 chunks x 16 slots
+constexpr int RT_TOK = 16;       // tokens per workgroup of the exact kernels
+constexpr int RT_THREADS = 256;  // 16 chunk lanes x 16 slots
 
+// Top-k by (value desc, id asc) over n entries vals[0..n) with expert ids
+// idmap[i] (identity when null), then the renormalised-softmax gates; one wave,
+// results written by lanes 0..k-1.  n <= 1024, k <= 64.
+__device__ __forceinline__ void wave_topk_gates(const float *vals, const int32_t *idmap, int n,
+                                                int64_t k, int lane, int32_t *ids_row,
+                                                float *gates_row) {
+    uint32_t taken = 0;  // bit r2: entry r2*64 + lane already selected
+    float first = 0.0f, denom = 0.0f;
+    float my_sel = 0.0f;
+    int32_t my_id = 0;
+    for (int64_t j = 0; j < k; ++j) {
+        float bv = -__builtin_inff();
+        int32_t bi = 0x7FFFFFFF;
+        int32_t bs = -1;
+        for (int r2 = 0; r2 * 64 + lane < n; ++r2) {
+            if (taken & (1u << r2)) continue;
+            const int i = r2 * 64 + lane;
+            const float v = vals[i];
+            const int32_t e = idmap ? idmap[i] : i;
+            if (v > bv || (v == bv && e < bi)) {
+                bv = v;
+                bi = e;
+                bs = i;
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 64);
+            const int32_t oi = __shfl_xor(bi, m, 64);
+            const int32_t os = __shfl_xor(bs, m, 64);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+                bs = os;
+            }
+        }
+        if (bs >= 0 && (bs & 63) == lane) taken |= 1u << (bs >> 6);
+        if (lane == (int)j) {
+            my_sel = bv;
+            my_id = bi;
+        }
+        if (j == 0) first = bv;
+    }
+    // softmax over the k selected logits, float32; the denominator is a
+    // sequential sum over j = 0..k-1 (each term broadcast from lane j)
+    const float ej = (lane < k) ? expf(my_sel - first) : 0.0f;
+    for (int64_t j = 0; j < k; ++j) denom += __shfl(ej, (int)j, 64);
+    if (lane < k) {
+        ids_row[lane] = my_id;
+        gates_row[lane] = ej / denom;
+    }
+}
+
+// ------------------------------------------------------------ exact, any E
 // TPT tokens x EPT experts of accumulators per thread.  TG = 16/TPT token
 // groups, EG = 16/TG expert groups, EB = EG*EPT experts per pass.
 template <int TPT, int EPT>
-__global__ __launch_bounds__(RT_THREADS) void route_kernel(
+__global__ __launch_bounds__(RT_THREADS) void route_exact_kernel(
     int64_t T, int64_t d, int64_t E, int64_t k, const bf16_t *__restrict__ x,
     const bf16_t *__restrict__ w, const float *__restrict__ bias, int32_t *__restrict__ ids,
     float *__restrict__ gates, float *__restrict__ logits_out) {
@@ -30,20 +100,18 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     extern __shared__ float s_logit[];  // [RT_TOK][E]
 
     const int tid = threadIdx.x;
-    const int c = tid & 15;       // chunk lane
-    const int slot = tid >> 4;    // 0..15
+    const int c = tid & 15;     // chunk lane
+    const int slot = tid >> 4;  // 0..15
     const int tg = slot % TG;
     const int eg = slot / TG;
     const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
     const int64_t dc = d / 16;
 
     const bf16_t *xrow[TPT];
-    bool tok_ok[TPT];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-        int64_t t = t0 + tg * TPT + u;
-        tok_ok[u] = t < T;
-        xrow[u] = x + (tok_ok[u] ? t : 0) * d + c * dc;
+        const int64_t t = t0 + tg * TPT + u;
+        xrow[u] = x + (t < T ? t : 0) * d + c * dc;
     }
 
     for (int64_t e0 = 0; e0 < E; e0 += EB) {
@@ -52,7 +120,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
         bool e_ok[EPT];
 #pragma unroll
         for (int v = 0; v < EPT; ++v) {
-            int64_t e = e0 + eg * EPT + v;
+            const int64_t e = e0 + eg * EPT + v;
             e_ok[v] = e < E;
             wrow[v] = w + (e_ok[v] ? e : 0) * d + c * dc;
 #pragma unroll
@@ -77,7 +145,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
                     for (int v = 0; v < EPT; ++v) acc[u][v] = __builtin_fmaf(xf[u], wf[v], acc[u][v]);
             }
         }
-        // balanced pairwise tree over the 16 chunk lanes (low 4 lane bits)
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
@@ -90,7 +157,7 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
 #pragma unroll
                 for (int v = 0; v < EPT; ++v)
                     if (e_ok[v]) {
-                        int64_t e = e0 + eg * EPT + v;
+                        const int64_t e = e0 + eg * EPT + v;
                         float l = acc[u][v];
                         if (bias) l = l + bias[e];
                         s_logit[(tg * TPT + u) * E + e] = l;
@@ -99,7 +166,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
     }
     __syncthreads();
 
-    // top-k per token: each wave takes 4 tokens
     const int lane = tid & 63;
     const int wave = tid >> 6;
     for (int r = 0; r < RT_TOK / 4; ++r) {
@@ -109,66 +175,386 @@ __global__ __launch_bounds__(RT_THREADS) void route_kernel(
         const float *lt = s_logit + tl * E;
         if (logits_out)
             for (int64_t e = lane; e < E; e += 64) logits_out[t * E + e] = lt[e];
-        // each lane owns experts lane, lane+64, ...; taken[] as a bitmask (E <= 1024)
-        uint32_t taken = 0;
-        float first = 0.0f, denom = 0.0f;
-        // gates need all k selected logits; keep them in lane j of the wave
-        float my_sel = 0.0f;
-        int32_t my_id = 0;
-        for (int64_t j = 0; j < k; ++j) {
-            float bv = -__builtin_inff();
-            int32_t bi = 0x7FFFFFFF;
-            for (int r2 = 0; r2 * 64 + lane < E; ++r2) {
-                if (taken & (1u << r2)) continue;
-                int32_t e = r2 * 64 + lane;
-                float v = lt[e];
-                if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
-            }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                float ov = __shfl_xor(bv, m, 64);
-                int32_t oi = __shfl_xor(bi, m, 64);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            if (lane == (int)j) { my_sel = bv; my_id = bi; }
-            if (j == 0) first = bv;
-        }
-        // softmax over the k selected logits, float32, j ascending
-        float ej = (lane < k) ? expf(my_sel - first) : 0.0f;
-        // sequential sum over j = 0..k-1 (broadcast each term from lane j)
-        for (int64_t j = 0; j < k; ++j) denom += __shfl(ej, (int)j, 64);
-        if (lane < k) {
-            ids[t * k + lane] = my_id;
-            gates[t * k + lane] = ej / denom;
-        }
+        wave_topk_gates(lt, nullptr, (int)E, k, lane, ids + t * k, gates + t * k);
     }
 }
 
+// ------------------------------------------------------------ exact, E <= 16
+// Chunk c of a staged row starts at c * (chunk bytes + 16): the 16-byte
+// stagger puts the 16 chunk lanes' reads of one step in distinct banks.
+__host__ __device__ __forceinline__ int64_t stag_pitch(int64_t d) { return 16 * (d / 16 * 2 + 16); }
+
+template <int EP>
+__global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
+    int64_t T, int64_t d, int64_t E, int64_t k, const bf16_t *__restrict__ x,
+    const bf16_t *__restrict__ w, const float *__restrict__ bias, int32_t *__restrict__ ids,
+    float *__restrict__ gates) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int64_t dc = d / 16;
+    const int64_t cbs = dc * 2 + 16;  // staged chunk stride, bytes
+    const int64_t wp = 16 * cbs;      // staged row pitch
+    float *s_logit = reinterpret_cast<float *>(smem + E * wp);  // [RT_TOK][E]
+
+    // stage W_r: 16-byte piece p of row e (elements 8p..8p+7) -> chunk p / (dc/8)
+    const int64_t ppr = d / 8, ppc = dc / 8;
+    for (int64_t p = threadIdx.x; p < E * ppr; p += RT_THREADS) {
+        const int64_t e = p / ppr, q = p % ppr;
+        const u32x4_t v = reinterpret_cast<const u32x4_t *>(w + e * d)[q];
+        *reinterpret_cast<u32x4_t *>(smem + e * wp + (q / ppc) * cbs + (q % ppc) * 16) = v;
+    }
+    __syncthreads();
+
+    const int tid = threadIdx.x;
+    const int c = tid & 15;
+    const int slot = tid >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * RT_TOK;
+    const int64_t t = t0 + slot;
+    const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (t < T ? t : 0) * d + c * dc);
+    const char *wc = smem + c * cbs;
+    const int nvec = (int)ppc;  // 16-byte vectors per chunk (even)
+
+    float acc[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
+    auto load = [&](u32x4_t (&r)[4], int b) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = (b + u < nvec) ? xp[b + u] : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    auto compute = [&](const u32x4_t (&r)[4], int b) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (b + u >= nvec) break;
+            u32x4_t wv[EP];
+#pragma unroll
+            for (int e = 0; e < EP; ++e)
+                wv[e] = e < E ? *reinterpret_cast<const u32x4_t *>(wc + e * wp + (b + u) * 16)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float xf = bf16x8_elem(r[u], q);
+#pragma unroll
+                for (int e = 0; e < EP; ++e) acc[e] = __builtin_fmaf(xf, bf16x8_elem(wv[e], q), acc[e]);
+            }
+        }
+    };
+    // activations prefetched one block of 4 vectors ahead
+    u32x4_t xa[4], xb[4];
+    load(xa, 0);
+    for (int b = 0; b < nvec; b += 8) {
+        if (b + 4 < nvec) load(xb, b + 4);
+        compute(xa, b);
+        if (b + 8 < nvec) load(xa, b + 8);
+        if (b + 4 < nvec) compute(xb, b + 4);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[e] = acc[e] + __shfl_xor(acc[e], m, 64);
+    if (c == 0 && t < T) {
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+            if (e < E) {
+                float l = acc[e];
+                if (bias) l = l + bias[e];
+                s_logit[slot * E + e] = l;
+            }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    for (int r = 0; r < RT_TOK / 4; ++r) {
+        const int tl = wave * (RT_TOK / 4) + r;
+        const int64_t tt = t0 + tl;
+        if (tt >= T) break;
+        wave_topk_gates(s_logit + tl * E, nullptr, (int)E, k, lane, ids + tt * k, gates + tt * k);
+    }
+}
+
+// ------------------------------------------------------------ fast path
+// W_r re-laid out so the 16 chunk pieces of one step are contiguous:
+// piece (e, step i, chunk c) at ((e * (dc/8) + i) * 16 + c) * 16 bytes; and
+// ||w_e|| (float32, rounded up by a relative 2^-10 to cover its own rounding).
+__global__ __launch_bounds__(256) void route_wprep_kernel(int64_t d, const bf16_t *__restrict__ w,
+                                                          bf16_t *__restrict__ wt,
+                                                          float *__restrict__ wnorm) {
+    __shared__ float s_red[256];
+    const int64_t e = blockIdx.x;
+    const int64_t ppr = d / 8, ppc = d / 16 / 8;
+    float ss = 0.0f;
+    for (int64_t p = threadIdx.x; p < ppr; p += 256) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t *>(w + e * d)[p];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float f = bf16x8_elem(v, q);
+            ss = __builtin_fmaf(f, f, ss);
+        }
+        const int64_t c = p / ppc, i = p % ppc;
+        reinterpret_cast<u32x4_t *>(wt + e * d)[i * 16 + c] = v;
+    }
+    s_red[threadIdx.x] = ss;
+    __syncthreads();
+    for (int m = 128; m >= 1; m >>= 1) {
+        if ((int)threadIdx.x < m) s_red[threadIdx.x] += s_red[threadIdx.x + m];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) wnorm[e] = sqrtf(s_red[0]) * (1.0f + 0x1p-10f);
+}
+
+// Approximate logits: float32 partial sums of x . w over K split S ways,
+// part[s][t][e], one 256 x 256 MFMA tile (token block x expert block) per
+// workgroup.
+__global__ __launch_bounds__(GEMM_THREADS, 1) void route_gemm_kernel(
+    int64_t T, int64_t d, int64_t E, int S, const bf16_t *__restrict__ x,
+    const bf16_t *__restrict__ w, float *__restrict__ part) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int MT = (int)((T + BM - 1) / BM);
+    const int NT = (int)((E + BN_TILE - 1) / BN_TILE);
+    const int L = blockIdx.x;
+    const int s = L / (MT * NT);
+    const int mt = (L % (MT * NT)) % MT;
+    const int nt = (L % (MT * NT)) / MT;
+    const int64_t Ks = d / S, k0 = (int64_t)s * Ks;
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN_TILE;
+    const int a_rows = (int)min((int64_t)BM, T - m0);
+    const int b_rows = (int)min((int64_t)BN_TILE, E - n0);
+    gemm_tile<EPI_F32>(x + k0, d, m0, a_rows, w + n0 * d + k0, nullptr, d, b_rows, (int)Ks,
+                       part + (int64_t)s * T * E, E, n0, b_rows, lds);
+}
+
+// One wave per token: bounds, candidates, exact logits of the candidates in
+// the defined order, selection and gates.
+constexpr int RF_WAVES = 4;
+__global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
+    int64_t T, int64_t d, int64_t E, int64_t k, int S, const bf16_t *__restrict__ x,
+    const bf16_t *__restrict__ wt, const float *__restrict__ wnorm, const float *__restrict__ bias,
+    const float *__restrict__ part, int32_t *__restrict__ ids, float *__restrict__ gates) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * RF_WAVES + wave;
+    if (t >= T) return;  // wave-uniform; the kernel has no workgroup barrier
+
+    const int64_t dc = d / 16, ppc = dc / 8;
+    const int64_t cbs = dc * 2 + 16;
+    const int64_t per_wave = stag_pitch(d) + E * 8;
+    char *xs = smem + wave * per_wave;                          // staged x_t
+    int32_t *cand = reinterpret_cast<int32_t *>(xs + stag_pitch(d));  // [E]
+    float *exact = reinterpret_cast<float *>(cand + E);                // [E]
+
+    // stage x_t (coalesced) and ||x_t||
+    float ss = 0.0f;
+    for (int64_t p = lane; p < d / 8; p += 64) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t *>(x + t * d)[p];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float f = bf16x8_elem(v, q);
+            ss = __builtin_fmaf(f, f, ss);
+        }
+        *reinterpret_cast<u32x4_t *>(xs + (p / ppc) * cbs + (p % ppc) * 16) = v;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float xn = sqrtf(ss) * (1.0f + 0x1p-10f);
+    // any-order float32 sums of d exact products err by <= d*u*sum|p|; two
+    // such sums (approximate and defined order) and the split-K partials,
+    // with a margin of 2.5x over u = 2^-24
+    const float gam = 2.5f * (float)d * 0x1p-23f;
+
+    // bounds of this lane's experts e = lane + 64*r2
+    constexpr int RMAX = 16;  // E <= 1024
+    float lo[RMAX], hi[RMAX];
+#pragma unroll
+    for (int r2 = 0; r2 < RMAX; ++r2) {
+        lo[r2] = -__builtin_inff();
+        hi[r2] = -__builtin_inff();
+        const int64_t e = r2 * 64 + lane;
+        if (e < E) {
+            float la = 0.0f;
+            for (int s = 0; s < S; ++s) la += part[((int64_t)s * T + t) * E + e];
+            if (bias) la += bias[e];
+            const float eps = gam * xn * wnorm[e] + 0x1p-20f * fabsf(la) + 1e-30f;
+            lo[r2] = la - eps;
+            hi[r2] = la + eps;
+        }
+    }
+    // Lk = k-th largest lower bound (k rounds of a wave max)
+    uint32_t taken = 0;
+    float Lk = -__builtin_inff();
+    for (int64_t j = 0; j < k; ++j) {
+        float bv = -__builtin_inff();
+        int bs = -1;
+#pragma unroll
+        for (int r2 = 0; r2 < RMAX; ++r2)
+            if (!(taken & (1u << r2)) && r2 * 64 + lane < E && (bs < 0 || lo[r2] > bv)) {
+                bv = lo[r2];
+                bs = r2 * 64 + lane;
+            }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const float ov = __shfl_xor(bv, m, 64);
+            const int os = __shfl_xor(bs, m, 64);
+            if (os >= 0 && (bs < 0 || ov > bv || (ov == bv && os < bs))) {
+                bv = ov;
+                bs = os;
+            }
+        }
+        if (bs >= 0 && (bs & 63) == lane) taken |= 1u << (bs >> 6);
+        Lk = bv;
+    }
+    // candidates: upper bound >= Lk, compacted in ascending expert order
+    int ns = 0;
+#pragma unroll
+    for (int r2 = 0; r2 < RMAX; ++r2) {
+        const bool keep = r2 * 64 + lane < E && hi[r2] >= Lk;
+        const uint64_t bal = __ballot(keep);
+        const int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (keep) cand[ns + before] = r2 * 64 + lane;
+        ns += __popcll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // exact logits of the candidates, four at a time: lane = (u, chunk c)
+    const int c = lane & 15;
+    const int u = lane >> 4;
+    const char *xc = xs + c * cbs;
+    for (int b = 0; b < ns; b += 4) {
+        const int ci = b + u;
+        const int e = cand[ci < ns ? ci : b];
+        const u32x4_t *wp = reinterpret_cast<const u32x4_t *>(wt + (int64_t)e * d) + c;
+        float acc = 0.0f;
+        u32x4_t wa[4], wb[4];
+        auto load = [&](u32x4_t (&r)[4], int64_t i0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = (i0 + q < ppc) ? wp[(i0 + q) * 16] : u32x4_t{0u, 0u, 0u, 0u};
+        };
+        auto compute = [&](const u32x4_t (&r)[4], int64_t i0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (i0 + q >= ppc) break;
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xc + (i0 + q) * 16);
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    acc = __builtin_fmaf(bf16x8_elem(xv, h), bf16x8_elem(r[q], h), acc);
+            }
+        };
+        load(wa, 0);
+        for (int64_t i0 = 0; i0 < ppc; i0 += 8) {
+            if (i0 + 4 < ppc) load(wb, i0 + 4);
+            compute(wa, i0);
+            if (i0 + 8 < ppc) load(wa, i0 + 8);
+            if (i0 + 4 < ppc) compute(wb, i0 + 4);
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) acc = acc + __shfl_xor(acc, m, 64);
+        if (c == 0 && ci < ns) {
+            float l = acc;
+            if (bias) l = l + bias[e];
+            exact[ci] = l;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_topk_gates(exact, cand, ns, k, lane, ids + t * k, gates + t * k);
+}
+
 template <int TPT, int EPT>
-hipError_t launch_route_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
+hipError_t launch_exact_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
                           int32_t *ids, float *gates, float *logits, hipStream_t s) {
     const size_t lds = (size_t)RT_TOK * D.E * sizeof(float);
     const unsigned grid = (unsigned)((D.T + RT_TOK - 1) / RT_TOK);
-    if (grid == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)route_kernel<TPT, EPT>,
+    hipError_t e = hipFuncSetAttribute((const void *)route_exact_kernel<TPT, EPT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_kernel<TPT, EPT>), dim3(grid), dim3(RT_THREADS), lds, s, D.T, D.d,
-                       D.E, D.k, x, w, bias, ids, gates, logits);
+    hipLaunchKernelGGL((route_exact_kernel<TPT, EPT>), dim3(grid), dim3(RT_THREADS), lds, s, D.T,
+                       D.d, D.E, D.k, x, w, bias, ids, gates, logits);
     return hipGetLastError();
 }
 
+template <int EP>
+hipError_t launch_small_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
+                          int32_t *ids, float *gates, hipStream_t s) {
+    const size_t lds = (size_t)(D.E * stag_pitch(D.d) + RT_TOK * D.E * sizeof(float));
+    const unsigned grid = (unsigned)((D.T + RT_TOK - 1) / RT_TOK);
+    hipError_t e = hipFuncSetAttribute((const void *)route_small_kernel<EP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_small_kernel<EP>), dim3(grid), dim3(RT_THREADS), lds, s, D.T, D.d,
+                       D.E, D.k, x, w, bias, ids, gates);
+    return hipGetLastError();
+}
+
+constexpr size_t SMALL_LDS_MAX = 150 * 1024;
+
 }  // namespace
 
+int route_splits(const Dims &D) {
+    const int64_t tiles = ((D.T + BM - 1) / BM) * ((D.E + BN_TILE - 1) / BN_TILE);
+    int S = 1;
+    while (S < 8 && tiles * S < 256 && D.d / (2 * S) >= 128 && (D.d / (2 * S)) % BK == 0) S *= 2;
+    return S;
+}
+
+bool route_uses_fast_path(const Dims &D) {
+    return D.E > 16 && (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8) <= 150 * 1024;
+}
+
+size_t route_workspace_bytes(const Dims &D) {
+    if (!route_uses_fast_path(D)) return 0;
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    return al((size_t)route_splits(D) * D.T * D.E * 4) + al((size_t)D.E * D.d * 2) +
+           al((size_t)D.E * 4);
+}
+
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
-                        int32_t *ids, float *gates, float *logits, hipStream_t s) {
-    // E <= 8: one token per thread slot, all experts in one pass.
-    // E <= 16: same with 16 experts per thread.
-    // Otherwise: 4 tokens x 8 experts per thread, 32 experts per pass.
-    if (D.E <= 8) return launch_route_t<1, 8>(D, x, w_router, bias, ids, gates, logits, s);
-    if (D.E <= 16) return launch_route_t<1, 16>(D, x, w_router, bias, ids, gates, logits, s);
-    return launch_route_t<4, 8>(D, x, w_router, bias, ids, gates, logits, s);
+                        int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
+                        hipStream_t s) {
+    if (D.T == 0) return hipSuccess;
+    if (logits || (route_uses_fast_path(D) && (!ws || ws_bytes < route_workspace_bytes(D)))) {
+        // every logit in the defined order
+        if (D.E <= 8) return launch_exact_t<1, 8>(D, x, w_router, bias, ids, gates, logits, s);
+        if (D.E <= 16) return launch_exact_t<1, 16>(D, x, w_router, bias, ids, gates, logits, s);
+        return launch_exact_t<4, 8>(D, x, w_router, bias, ids, gates, logits, s);
+    }
+    if (!route_uses_fast_path(D)) {
+        const size_t lds = (size_t)(D.E * stag_pitch(D.d) + RT_TOK * D.E * sizeof(float));
+        if (lds > SMALL_LDS_MAX) {
+            if (D.E <= 8) return launch_exact_t<1, 8>(D, x, w_router, bias, ids, gates, nullptr, s);
+            return launch_exact_t<1, 16>(D, x, w_router, bias, ids, gates, nullptr, s);
+        }
+        if (D.E <= 8) return launch_small_t<8>(D, x, w_router, bias, ids, gates, s);
+        return launch_small_t<16>(D, x, w_router, bias, ids, gates, s);
+    }
+    // fast path
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const int S = route_splits(D);
+    float *part = reinterpret_cast<float *>(ws);
+    bf16_t *wt = reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(ws) +
+                                            al((size_t)S * D.T * D.E * 4));
+    float *wnorm = reinterpret_cast<float *>(reinterpret_cast<char *>(wt) + al((size_t)D.E * D.d * 2));
+    hipLaunchKernelGGL(route_wprep_kernel, dim3((unsigned)D.E), dim3(256), 0, s, D.d, w_router, wt,
+                       wnorm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void *)route_gemm_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((D.T + BM - 1) / BM) * ((D.E + BN_TILE - 1) / BN_TILE) * S;
+    hipLaunchKernelGGL(route_gemm_kernel, dim3((unsigned)tiles), dim3(GEMM_THREADS), GEMM_LDS_BYTES,
+                       s, D.T, D.d, D.E, S, x, w_router, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8);
+    e = hipFuncSetAttribute((const void *)route_refine_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_refine_kernel, dim3((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES)),
+                       dim3(64 * RF_WAVES), lds, s, D.T, D.d, D.E, D.k, S, x, wt, wnorm, bias, part,
+                       ids, gates);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -41,14 +41,23 @@ def host_f32(t) -> np.ndarray:
 
 
 def rel_err(out: np.ndarray, ref: np.ndarray) -> float:
-    """max_i |o_i - r_i| / max(|r_i|, rms(r))  (relative error with an rms floor)."""
+    """Max relative error of a layer output, token by token:
+    max over (t, i) of |o[t,i] - r[t,i]| / max(|r[t,i]|, rms(r[t,:])).
+    A token whose reference row is exactly zero (no local expert) must come out
+    exactly zero: any nonzero value there counts as an infinite error."""
     out = np.asarray(out, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if ref.size == 0:
         return 0.0
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    floor = np.maximum(np.abs(ref), rms if rms > 0 else 1.0)
-    return float(np.max(np.abs(out - ref) / floor))
+    out2 = out.reshape(-1, ref.shape[-1])
+    ref2 = ref.reshape(-1, ref.shape[-1])
+    rms = np.sqrt(np.mean(ref2 * ref2, axis=1, keepdims=True))
+    floor = np.maximum(np.abs(ref2), rms)
+    num = np.abs(out2 - ref2)
+    zero = floor == 0
+    if np.any(num[zero] > 0):
+        return float("inf")
+    return float(np.max(np.where(zero, 0.0, num / np.where(zero, 1.0, floor))))
 
 
 def upload(cfg: W.MoEConfig, arrs) -> dict:

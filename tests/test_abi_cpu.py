@@ -47,6 +47,9 @@ def test_workspace_sizes_scale_with_problem():
     D = dims(T=4096, d=4096, f=14336)
     assert big >= 4096 * 2 * (4096 + 14336 + 4096) * 2
     assert M.moe_permute_workspace_bytes(dims()) > 0
+    # the router needs a workspace only on its fast path (more than 16 experts)
+    assert M.moe_route_workspace_bytes(dims()) == 0
+    assert M.moe_route_workspace_bytes(dims(T=8192, d=7168, f=2048, E=256, k=8)) > 8192 * 256 * 4
     assert M.moe_expert_ffn_workspace_bytes(dims()) > 256 * 2 * 1024 * 2
     # invalid dims size to 0
     assert M.moe_layer_workspace_bytes(dims(k=9)) == 0
@@ -61,7 +64,7 @@ def test_workspace_sizes_scale_with_problem():
 def test_bad_dims_rejected_by_every_entry_point(bad, status):
     lib = M.load()
     D = dims(**bad)
-    assert lib.moe_route(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, None, None) == status
+    assert lib.moe_route(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == status
     assert lib.moe_permute(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, 1 << 40,
                            None) == status
     assert lib.moe_expert_ffn(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, 1 << 40,
@@ -74,10 +77,13 @@ def test_bad_dims_rejected_by_every_entry_point(bad, status):
 def test_null_and_misaligned_pointers_rejected():
     lib = M.load()
     D = dims()
-    assert lib.moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, None) == INVALID
-    assert lib.moe_route(C.byref(D), None, FAKE, None, FAKE, FAKE, None, None) == INVALID
+    assert lib.moe_route(None, FAKE, FAKE, None, FAKE, FAKE, None, None, 0, None) == INVALID
+    assert lib.moe_route(C.byref(D), None, FAKE, None, FAKE, FAKE, None, None, 0, None) == INVALID
     assert lib.moe_route(C.byref(D), C.c_void_p(0x10002), FAKE, None, FAKE, FAKE, None,
-                         None) == INVALID
+                         None, 0, None) == INVALID
+    # a workspace that is not 256-byte aligned
+    assert lib.moe_route(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, None, C.c_void_p(0x100010),
+                         1 << 20, None) == WORKSPACE
     assert lib.moe_combine(C.byref(D), FAKE, FAKE, FAKE, FAKE, 7, None) == INVALID
     assert lib.moe_layer(C.byref(D), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, None, None,
                          FAKE_WS, 1 << 40, None) == INVALID
@@ -102,7 +108,7 @@ def test_workspace_checks():
 def test_empty_batch_is_a_no_op():
     lib = M.load()
     D = dims(T=0)
-    assert lib.moe_route(C.byref(D), None, None, None, None, None, None, None) == OK
+    assert lib.moe_route(C.byref(D), None, None, None, None, None, None, None, 0, None) == OK
     assert lib.moe_combine(C.byref(D), None, None, None, None, 0, None) == OK
     assert lib.moe_layer(C.byref(D), None, None, None, None, None, None, None, 0, None, None, None,
                          0, None) == OK

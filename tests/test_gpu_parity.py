@@ -37,6 +37,10 @@ SMALL = {
     "single_expert": W.CONFIGS["tiny"].scaled(T=77, d=256, f=128, E=1, k=1, seed=8),
     "one_token": W.CONFIGS["tiny"].scaled(T=1, d=256, f=128, E=8, k=2, seed=9),
     "multi_tile_rows": W.CONFIGS["tiny"].scaled(T=1000, d=256, f=256, E=4, k=2, seed=10),
+    "e32k4": W.CONFIGS["tiny"].scaled(T=300, d=512, f=128, E=32, k=4, seed=13),
+    "e1024k64": W.CONFIGS["tiny"].scaled(T=40, d=256, f=128, E=1024, k=64, seed=14),
+    "e256k8_local": W.CONFIGS["tiny"].scaled(T=700, d=1024, f=128, E=256, k=8, e_lo=32,
+                                             e_hi=64, out_fp32=True, seed=15),
 }
 
 
@@ -56,6 +60,13 @@ def _check_route(cfg, t, arrs):
     assert np.array_equal(logits.cpu().numpy().view(np.uint32), r_l.view(np.uint32)), "logits"
     assert np.array_equal(ids.cpu().numpy(), r_ids), "topk ids"
     assert np.abs(gates.cpu().numpy() - r_g).max() <= TOL_GATE, "gates"
+    # without the logits output the router takes its fast path (LDS-staged for
+    # E <= 16, MFMA bounds + exact candidates above); same ids and gate bits
+    say(f"moe_route fast path {cfg.name}")
+    f_ids, f_gates, _ = M.moe_route(D, t["x"], t["w_router"], t["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(f_ids, ids), "fast-path ids"
+    assert torch.equal(f_gates.view(torch.int32), gates.view(torch.int32)), "fast-path gates"
     return ids, gates, r_ids, r_g
 
 
@@ -230,7 +241,7 @@ def test_full_size_workload(name):
     must = local_tok[:3].tolist() + local_tok[-3:].tolist()
     if cfg.E_loc < cfg.E:
         must += np.nonzero(~(ri >= 0).any(1))[0][:2].tolist()
-    toks = sample_tokens(cfg.T, 16, seed=2, must=must)
+    toks = sample_tokens(cfg.T, 48, seed=2, must=must)
     _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
     del t, xp, y, staged
     torch.cuda.empty_cache()
@@ -262,3 +273,26 @@ def test_fused_visibility_poisoned_workspace_alternating_inputs(name, hot):
         torch.cuda.synchronize()
         assert not torch.isnan(out.float()).any()
         assert torch.equal(out.view(torch.int16), staged.view(torch.int16)), "fused != staged"
+
+
+@pytest.mark.parametrize("pattern", ["duplicated_rows", "all_equal", "scaled_copies"])
+def test_router_fast_path_on_constructed_ties(pattern):
+    # Router weights built so that logits tie exactly (duplicated expert rows),
+    # all tie (identical rows: every expert is a candidate), or sit at the
+    # tolerance edge (rows that are exact power-of-two multiples of others):
+    # the fast path must still return the exact-order selection and gates.
+    cfg = W.CONFIGS["tiny"].scaled(name=f"ties_{pattern}", T=257, d=512, f=128, E=96, k=6,
+                                   seed=16)
+    arrs = W.generate(cfg)
+    wr = W.bf16_bits_to_f32(arrs["w_router"]).reshape(cfg.E, cfg.d)
+    if pattern == "duplicated_rows":
+        wr[1::2] = wr[0::2]
+    elif pattern == "all_equal":
+        wr[:] = wr[0]
+    else:
+        wr[48:] = wr[:48] * 2.0
+    arrs["w_router"] = W.f32_to_bf16_bits(wr.astype(np.float32))
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    if pattern == "all_equal":
+        assert np.array_equal(r_ids[0], np.arange(cfg.k))
