@@ -197,10 +197,21 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
 
     // stage W_r: 16-byte piece p of row e (elements 8p..8p+7) -> chunk p / (dc/8)
     const int64_t ppr = d / 8, ppc = dc / 8;
-    for (int64_t p = threadIdx.x; p < E * ppr; p += RT_THREADS) {
-        const int64_t e = p / ppr, q = p % ppr;
-        const u32x4_t v = reinterpret_cast<const u32x4_t *>(w + e * d)[q];
-        *reinterpret_cast<u32x4_t *>(smem + e * wp + (q / ppc) * cbs + (q % ppc) * 16) = v;
+    // eight independent loads in flight per thread before their stores
+    for (int64_t p0 = threadIdx.x; p0 < E * ppr; p0 += 8 * RT_THREADS) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t p = p0 + u * RT_THREADS;
+            if (p < E * ppr) v[u] = reinterpret_cast<const u32x4_t *>(w)[p];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t p = p0 + u * RT_THREADS;
+            if (p >= E * ppr) break;
+            const int64_t e = p / ppr, q = p % ppr;
+            *reinterpret_cast<u32x4_t *>(smem + e * wp + (q / ppc) * cbs + (q % ppc) * 16) = v[u];
+        }
     }
     __syncthreads();
 
@@ -216,13 +227,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
     float acc[EP];
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = 0.0f;
-    auto load = [&](u32x4_t (&r)[4], int b) {
+    constexpr int PG = 16;  // vectors per prefetch group
+    auto load = [&](u32x4_t (&r)[PG], int b) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = (b + u < nvec) ? xp[b + u] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int u = 0; u < PG; ++u) r[u] = (b + u < nvec) ? xp[b + u] : u32x4_t{0u, 0u, 0u, 0u};
     };
-    auto compute = [&](const u32x4_t (&r)[4], int b) {
+    auto compute = [&](const u32x4_t (&r)[PG], int b) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < PG; ++u) {
             if (b + u >= nvec) break;
             u32x4_t wv[EP];
 #pragma unroll
@@ -237,14 +249,14 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
             }
         }
     };
-    // activations prefetched one block of 4 vectors ahead
-    u32x4_t xa[4], xb[4];
+    // activations prefetched one group of PG vectors ahead
+    u32x4_t xa[PG], xb[PG];
     load(xa, 0);
-    for (int b = 0; b < nvec; b += 8) {
-        if (b + 4 < nvec) load(xb, b + 4);
+    for (int b = 0; b < nvec; b += 2 * PG) {
+        if (b + PG < nvec) load(xb, b + PG);
         compute(xa, b);
-        if (b + 8 < nvec) load(xa, b + 8);
-        if (b + 4 < nvec) compute(xb, b + 4);
+        if (b + 2 * PG < nvec) load(xa, b + 2 * PG);
+        if (b + PG < nvec) compute(xb, b + PG);
     }
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1)
@@ -272,6 +284,13 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
 }
 
 // ------------------------------------------------------------ fast path
+// Factor that rounds a float32 norm sqrt(sum of d squares) up past its exact
+// value: the sum errs by at most d*2^-24 relative, the sqrt halves that and
+// adds 2^-24.
+__device__ __forceinline__ float norm_inflation(int64_t d) {
+    return 1.0f + (float)d * 0x1p-24f + 0x1p-20f;
+}
+
 // W_r re-laid out so the 16 chunk pieces of one step are contiguous:
 // piece (e, step i, chunk c) at ((e * (dc/8) + i) * 16 + c) * 16 bytes; and
 // ||w_e|| (float32, rounded up by a relative 2^-10 to cover its own rounding).
@@ -298,7 +317,7 @@ __global__ __launch_bounds__(256) void route_wprep_kernel(int64_t d, const bf16_
         if ((int)threadIdx.x < m) s_red[threadIdx.x] += s_red[threadIdx.x + m];
         __syncthreads();
     }
-    if (threadIdx.x == 0) wnorm[e] = sqrtf(s_red[0]) * (1.0f + 0x1p-10f);
+    if (threadIdx.x == 0) wnorm[e] = sqrtf(s_red[0]) * norm_inflation(d);
 }
 
 // Approximate logits: float32 partial sums of x . w over K split S ways,
@@ -344,22 +363,35 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
 
     // stage x_t (coalesced) and ||x_t||
     float ss = 0.0f;
-    for (int64_t p = lane; p < d / 8; p += 64) {
-        const u32x4_t v = reinterpret_cast<const u32x4_t *>(x + t * d)[p];
+    for (int64_t p0 = lane; p0 < d / 8; p0 += 8 * 64) {
+        u32x4_t v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float f = bf16x8_elem(v, q);
-            ss = __builtin_fmaf(f, f, ss);
+        for (int u = 0; u < 8; ++u) {
+            const int64_t p = p0 + u * 64;
+            if (p < d / 8) v[u] = reinterpret_cast<const u32x4_t *>(x + t * d)[p];
         }
-        *reinterpret_cast<u32x4_t *>(xs + (p / ppc) * cbs + (p % ppc) * 16) = v;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t p = p0 + u * 64;
+            if (p >= d / 8) break;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float f = bf16x8_elem(v[u], q);
+                ss = __builtin_fmaf(f, f, ss);
+            }
+            *reinterpret_cast<u32x4_t *>(xs + (p / ppc) * cbs + (p % ppc) * 16) = v[u];
+        }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-    const float xn = sqrtf(ss) * (1.0f + 0x1p-10f);
-    // any-order float32 sums of d exact products err by <= d*u*sum|p|; two
-    // such sums (approximate and defined order) and the split-K partials,
-    // with a margin of 2.5x over u = 2^-24
-    const float gam = 2.5f * (float)d * 0x1p-23f;
+    const float xn = sqrtf(ss) * norm_inflation(d);
+    // |l~ - l| <= (d*2^-23 + (d/16 + 4)*2^-24) * sum|x_i w_i| + bias roundings:
+    // the MFMA split-K sum, whatever its internal order, passes each of the d
+    // exact products through at most d roundings of at most 2^-23 (round to
+    // nearest or toward zero); the defined-order sum through at most d/16 + 4
+    // of 2^-24; sum|x_i w_i| <= ||x|| ||w|| (Cauchy-Schwarz).  +8 and 2^-10
+    // cover the float32 evaluation of the bound itself.
+    const float gam = ((float)(2 * d + d / 16 + 8) * 0x1p-24f) * (1.0f + 0x1p-10f);
 
     // bounds of this lane's experts e = lane + 64*r2
     constexpr int RMAX = 16;  // E <= 1024
@@ -368,14 +400,31 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     for (int r2 = 0; r2 < RMAX; ++r2) {
         lo[r2] = -__builtin_inff();
         hi[r2] = -__builtin_inff();
-        const int64_t e = r2 * 64 + lane;
-        if (e < E) {
+    }
+    // 4 expert slots x up to 8 partials loaded before any is summed
+#pragma unroll
+    for (int r0 = 0; r0 < RMAX; r0 += 4) {
+        if (r0 * 64 >= E) break;  // wave-uniform
+        float pv[4][8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = (r0 + q) * 64 + lane;
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2)
+                pv[q][s2] = (s2 < S && e < E) ? part[((int64_t)s2 * T + t) * E + e] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t e = (r0 + q) * 64 + lane;
+            if (e >= E) continue;
             float la = 0.0f;
-            for (int s = 0; s < S; ++s) la += part[((int64_t)s * T + t) * E + e];
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) la += pv[q][s2];
             if (bias) la += bias[e];
-            const float eps = gam * xn * wnorm[e] + 0x1p-20f * fabsf(la) + 1e-30f;
-            lo[r2] = la - eps;
-            hi[r2] = la + eps;
+            const float g = gam * xn * wnorm[e];
+            const float eps = g + 0x1p-21f * (fabsf(la) + g) + 1e-30f;
+            lo[r0 + q] = la - eps;
+            hi[r0 + q] = la + eps;
         }
     }
     // Lk = k-th largest lower bound (k rounds of a wave max)
@@ -425,15 +474,16 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
         const int e = cand[ci < ns ? ci : b];
         const u32x4_t *wp = reinterpret_cast<const u32x4_t *>(wt + (int64_t)e * d) + c;
         float acc = 0.0f;
-        u32x4_t wa[4], wb[4];
-        auto load = [&](u32x4_t (&r)[4], int64_t i0) {
+        constexpr int PG = 8;   // vectors per prefetch group
+        u32x4_t wa[PG], wb[PG];
+        auto load = [&](u32x4_t (&r)[PG], int64_t i0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < PG; ++q)
                 r[q] = (i0 + q < ppc) ? wp[(i0 + q) * 16] : u32x4_t{0u, 0u, 0u, 0u};
         };
-        auto compute = [&](const u32x4_t (&r)[4], int64_t i0) {
+        auto compute = [&](const u32x4_t (&r)[PG], int64_t i0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < PG; ++q) {
                 if (i0 + q >= ppc) break;
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xc + (i0 + q) * 16);
 #pragma unroll
@@ -442,11 +492,11 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
             }
         };
         load(wa, 0);
-        for (int64_t i0 = 0; i0 < ppc; i0 += 8) {
-            if (i0 + 4 < ppc) load(wb, i0 + 4);
+        for (int64_t i0 = 0; i0 < ppc; i0 += 2 * PG) {
+            if (i0 + PG < ppc) load(wb, i0 + PG);
             compute(wa, i0);
-            if (i0 + 8 < ppc) load(wa, i0 + 8);
-            if (i0 + 4 < ppc) compute(wb, i0 + 4);
+            if (i0 + 2 * PG < ppc) load(wa, i0 + 2 * PG);
+            if (i0 + PG < ppc) compute(wb, i0 + PG);
         }
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1) acc = acc + __shfl_xor(acc, m, 64);
