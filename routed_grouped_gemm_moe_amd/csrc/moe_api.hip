@@ -29,8 +29,12 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
+    L.dn_part = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
+    L.dn_acc = take(layer && D.dn_splits() > 1
+                        ? MT * (size_t)D.nt_dn() * (size_t)(4 * 4 * 16 * GEMM_THREADS) * sizeof(float)
+                        : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
     L.blk_counts = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
@@ -291,6 +295,8 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.queues = at<int32_t>(ws, L.queues);
         a.gu_done = at<int32_t>(ws, L.gu_done);
         a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
+        a.dn_part = at<int32_t>(ws, L.dn_part);
+        a.dn_acc = at<float>(ws, L.dn_acc);
         a.dn_flag = at<int32_t>(ws, L.dn_flag);
         a.status = at<int32_t>(ws, L.status);
         a.out = out;

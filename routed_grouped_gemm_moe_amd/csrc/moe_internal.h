@@ -70,6 +70,13 @@ struct Dims {
     __host__ __device__ int64_t nt_dn() const { return d / BN_DN; }
     __host__ __device__ int64_t perm_blocks() const { return (T + PERM_TB - 1) / PERM_TB; }
     __host__ __device__ int64_t comb_blocks() const { return (T + COMB_TOK - 1) / COMB_TOK; }
+    // K parts of a down tile in the persistent kernel: the largest power of two
+    // (<= 8) that keeps each part at least 3072 deep and a multiple of 32.
+    __host__ __device__ int64_t dn_splits() const {
+        int64_t S = 1;
+        while (S < 8 && f / (2 * S) >= 3072 && (f / (2 * S)) % 32 == 0) S *= 2;
+        return S;
+    }
 };
 
 // An m-tile of the grouped GEMM: rows [row0, row0 + rows) of expert e.
@@ -79,7 +86,7 @@ struct MTile {
 
 // Byte offsets of every region in a workspace (each 256-byte aligned).
 struct Layout {
-    size_t status, queues, gu_done, gu_xcd, dn_flag, route, ids, gates, blk_counts, blk_base, counts, offsets,
+    size_t status, queues, gu_done, gu_xcd, dn_part, dn_flag, route, dn_acc, ids, gates, blk_counts, blk_base, counts, offsets,
         perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm, h, y, total;
 };
 
@@ -132,7 +139,8 @@ struct LayerArgs {
     const int32_t *ids, *inv_perm, *offsets, *mtile_base, *n_mtiles;
     const float *gates;
     const MTile *mtiles;
-    int32_t *queues, *gu_done, *gu_xcd, *dn_flag, *status;
+    int32_t *queues, *gu_done, *gu_xcd, *dn_part, *dn_flag, *status;
+    float *dn_acc;  // float32 partials of split down tiles (dn_splits() > 1)
     void *out;
     int out_f32;
     int64_t wait_ticks;  // flag-wait timeout in wall_clock64 ticks
