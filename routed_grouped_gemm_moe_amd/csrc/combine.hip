@@ -1,5 +1,5 @@
 // Combine: the gate-weighted sum of each token's expert outputs, back in
-// token order (Weave, §2.1 stage 5: "weighted summation").  A gather in slot
+// token order (Weave, §2.1 stage 5: the gate-weighted sum).  A gather in slot
 // order rather than a scatter, so every output element is written once and the
 // result is deterministic: out[t] = sum_j gate[t,j] * y[inv_perm[t,j]] in
 // float32, j ascending, slots with inv_perm < 0 skipped.

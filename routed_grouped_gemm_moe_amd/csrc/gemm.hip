@@ -1,6 +1,7 @@
-// Standalone grouped expert GEMMs (the moe_expert_ffn path) and the m-tile
-// table builder.  The tile table is built on the device from the segment
-// offsets that the permute produced, so no count ever returns to the host
+// Standalone grouped expert GEMMs (the moe_expert_ffn path) over the packed
+// activation layout of gemm_pa.h, and the m-tile table builder.  The tile table is built on the device from
+// the segment offsets that the permute produced, so no count ever returns to
+// the host
 // (Weave §3: the workload is fixed once routing completes; §4: the routing
 // result reaches the kernel as a parameter).
 //
@@ -10,7 +11,7 @@
 // flight share weight and activation tiles) and each of the 8 XCDs takes one
 // contiguous eighth of that order: workgroup b runs on XCD b % 8 (round-robin
 // dispatch), so the workgroups sharing a tile meet in one XCD's L2.
-#include "gemm_tile.h"
+#include "gemm_pa.h"
 
 namespace moe {
 namespace {
@@ -19,22 +20,31 @@ __global__ __launch_bounds__(1024) void build_mtiles_kernel(int64_t EL,
                                                             const int32_t *__restrict__ offsets,
                                                             MTile *__restrict__ mtiles,
                                                             int32_t *__restrict__ n_mtiles,
-                                                            int32_t *__restrict__ mtile_base) {
-    extern __shared__ int32_t s_mt[];  // [EL + 1]
-    for (int64_t e = threadIdx.x; e < EL; e += 1024)
-        s_mt[e] = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+                                                            int32_t *__restrict__ mtile_base,
+                                                            int32_t *__restrict__ pstart) {
+    extern __shared__ int32_t s_mt[];  // [2 * (EL + 1)]: m-tile starts, packed segment starts
+    int32_t *s_ps = s_mt + EL + 1;
+    for (int64_t e = threadIdx.x; e < EL; e += 1024) {
+        const int32_t c = offsets[e + 1] - offsets[e];
+        s_mt[e] = (c + BM - 1) / BM;
+        s_ps[e] = (c + 31) & ~31;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int32_t run = 0;
+        int32_t run = 0, ps = 0;
         for (int64_t e = 0; e < EL; ++e) {
-            int32_t m = s_mt[e];
+            const int32_t m = s_mt[e], p = s_ps[e];
             s_mt[e] = run;
+            s_ps[e] = ps;
             run += m;
+            ps += p;
         }
         s_mt[EL] = run;
+        s_ps[EL] = ps;
         *n_mtiles = run;
     }
     __syncthreads();
+    for (int64_t e = threadIdx.x; e <= EL; e += 1024) pstart[e] = s_ps[e];
     for (int64_t e = threadIdx.x; e < EL; e += 1024) {
         const int32_t base = s_mt[e], n = s_mt[e + 1] - base;
         const int32_t row0 = offsets[e], cnt = offsets[e + 1] - row0;
@@ -44,7 +54,7 @@ __global__ __launch_bounds__(1024) void build_mtiles_kernel(int64_t EL,
             t.e = (int32_t)e;
             t.row0 = row0 + m * BM;
             t.rows = min(BM, cnt - m * BM);
-            t.pad = 0;
+            t.prow0 = s_ps[e] + m * BM;
             mtiles[base + m] = t;
         }
     }
@@ -73,15 +83,16 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     int mt, nt;
     blocked_tile(L, MT, NT, &mt, &nt);
     const MTile t = mtiles[mt];
+    const int64_t prb = t.prow0 / 32;  // first packed row block
     if (GATE_UP) {
         const bf16_t *wg = W0 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
         const bf16_t *wu = W1 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
-        gemm_tile<EPI_SILU_BF16>(A, d, t.row0, t.rows, wg, wu, d, BN_GU, (int)d, out, f,
-                                 (int64_t)nt * BN_GU, BN_GU, lds);
+        gemm_tile_pa<PA_SILU_PACKED>(A + prb * (d / 16) * 512, d / 16, t.rows, (int)d, wg, wu, d,
+                                     out + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16, lds);
     } else {
         const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
-        gemm_tile<EPI_BF16>(A, f, t.row0, t.rows, wd, nullptr, f, BN_DN, (int)f, out, d,
-                            (int64_t)nt * BN_DN, BN_DN, lds);
+        gemm_tile_pa<PA_BF16>(A + prb * (f / 16) * 512, f / 16, t.rows, (int)f, wd, nullptr, f,
+                              out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
     }
 }
 
@@ -103,16 +114,18 @@ hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, cons
 }  // namespace
 
 hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
-                               int32_t *n_mtiles, int32_t *mtile_base, hipStream_t s) {
-    hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024), (D.EL() + 1) * sizeof(int32_t), s,
-                       D.EL(), offsets, mtiles, n_mtiles, mtile_base);
+                               int32_t *n_mtiles, int32_t *mtile_base, int32_t *pstart,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024),
+                       2 * (D.EL() + 1) * sizeof(int32_t), s, D.EL(), offsets, mtiles, n_mtiles,
+                       mtile_base, pstart);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *x_perm, const MTile *mtiles,
+hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
                                const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
                                bf16_t *h, hipStream_t s) {
-    return launch_gemm<true>(D, x_perm, mtiles, n_mtiles, w_gate, w_up, h, s);
+    return launch_gemm<true>(D, xp, mtiles, n_mtiles, w_gate, w_up, h, s);
 }
 
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,

@@ -1,6 +1,8 @@
-// One output tile of the grouped expert GEMM on gfx950 bf16 MFMA with float32
-// accumulation (Weave, §2.1: GEMM0 = up and gate projections, then "SiLU
-// followed by element-wise multiplication", GEMM1 = down projection).
+// A GEMM tile with both operands staged through LDS, on gfx950 bf16 MFMA with
+// float32 accumulation.  The router's logit GEMM uses it (EPI_F32); the expert
+// FFN uses the packed-operand tile of gemm_pa.h, which keeps this tile's
+// k-order.  Its epilogues also cover the expert GEMMs of Weave, §2.1 (GEMM0 =
+// gate and up projections with the SiLU-gated product, GEMM1 = down).
 //
 // Tile: BM = 256 rows (one expert's rows, clamped at the segment end) by
 // BN_TILE = 256 B rows.  256 threads = 4 waves in a 2x2 grid; each wave owns a
@@ -99,23 +101,12 @@ enum { EPI_SILU_BF16 = 0, EPI_BF16 = 1, EPI_F32 = 2 };
 // A: a_rows rows from a_row0, stride lda; B0 (and B1 for the dual-B tile):
 // b_rows valid rows each, stride ldb; K columns of both are used.  The buffer
 // descriptors cover exactly the bytes those rows and columns span.
-// Split K (down tiles of the persistent kernel): with acc_in the accumulators
-// start from a previous part's float32 partial instead of zero (read with
-// device-coherent loads: it may come from another XCD); with acc_out the
-// accumulators are stored there instead of the epilogue.  A tile computed as
-// parts over consecutive K ranges therefore runs exactly the MFMA sequence of
-// the whole tile.  Partial layout: float index
-// (((i*4 + j)*4 + v/4) * 256 + thread) * 4 + v%4, 256 KiB per tile.
-constexpr int64_t ACC_TILE_FLOATS = 4 * 4 * 16 * GEMM_THREADS;
-
 template <int EPI>
 __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t lda, int64_t a_row0,
                                           int a_rows, const bf16_t *__restrict__ B0,
                                           const bf16_t *__restrict__ B1, int64_t ldb, int b_rows,
                                           int K, void *__restrict__ out, int64_t ldo,
-                                          int64_t out_col0, int out_cols, char *lds,
-                                          const float *acc_in = nullptr,
-                                          float *acc_out = nullptr) {
+                                          int64_t out_col0, int out_cols, char *lds) {
     constexpr bool GATE_UP = EPI == EPI_SILU_BF16;
     // An opaque copy of the thread index: inside a persistent tile loop this
     // keeps the compiler from hoisting every lane-dependent address out of the
@@ -194,25 +185,6 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    if (acc_in) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const uint64_t *q = reinterpret_cast<const uint64_t *>(
-                        acc_in + ((((i * 4 + j) * 4 + v4) * GEMM_THREADS + tid) * 4));
-                    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                    acc[i][j][4 * v4 + 0] = __uint_as_float((uint32_t)lo);
-                    acc[i][j][4 * v4 + 1] = __uint_as_float((uint32_t)(lo >> 32));
-                    acc[i][j][4 * v4 + 2] = __uint_as_float((uint32_t)hi);
-                    acc[i][j][4 * v4 + 3] = __uint_as_float((uint32_t)(hi >> 32));
-                }
-    }
 
     // valid 32-row blocks of this wave (wave-uniform)
     const int nblk = __builtin_amdgcn_readfirstlane(max(0, min(4, (a_rows - wm * 128 + 31) >> 5)));
@@ -257,20 +229,6 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
     step(KT - 3, no{}, no{}, yes{});
     step(KT - 2, yes{}, no{}, yes{});
     step(KT - 1, yes{}, no{}, no{});
-
-    if (acc_out) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    *reinterpret_cast<f32x4_t *>(
-                        acc_out + ((((i * 4 + j) * 4 + v4) * GEMM_THREADS + tid) * 4)) =
-                        f32x4_t{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
-                                acc[i][j][4 * v4 + 3]};
-        return;
-    }
 
     // Epilogue.  Accumulator v of lane l in a 32x32 tile sits at
     // row 8*(v/4) + 4*(l/32) + v%4, column l%32.

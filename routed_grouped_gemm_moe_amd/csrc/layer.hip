@@ -15,6 +15,9 @@
 // side flag as soon as it is written (the producer-consumer tile signaling of
 // Cui et al., abstract), not at a kernel boundary.
 //
+// GEMM tiles are those of gemm_pa.h: x_perm and h are in its packed layout
+// (h written by the gate/up epilogue, read as the down tiles' A operand).
+//
 // Queues: gate/up and down tiles follow the blocked order of gemm_tile.h and
 // each kind is split into 8 contiguous ranges, one per XCD.  A workgroup reads
 // the XCD it runs on from the hardware (XCC_ID), drains that XCD's range
@@ -39,7 +42,7 @@
 // MOE_ERR_DEVICE_TIMEOUT in the status word and carries on (the result is
 // then invalid, but the kernel drains).
 #include "combine_tile.h"
-#include "gemm_tile.h"
+#include "gemm_pa.h"
 
 namespace moe {
 namespace {
@@ -83,32 +86,8 @@ __device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd) {
     return -1;
 }
 
-// Claim with `parts` passes over each queue's range: queue y hands out
-// part p of every tile in its range before part p+1 of any, so a part's
-// predecessor (same tile, previous part, same queue) was always claimed
-// earlier.  Returns p * n + tile, or -1.
-__device__ __forceinline__ int claim_tile_parts(int32_t *q, int n, int parts, int xcd) {
-    const int per = (n + NUM_XCD - 1) / NUM_XCD;
-    for (int r = 0; r < NUM_XCD; ++r) {
-        const int y = (xcd + r) & (NUM_XCD - 1);
-        const int lo = y * per;
-        const int len = min(n, lo + per) - lo;
-        if (len <= 0) continue;
-        int32_t *c = q + y * QSTRIDE;
-        if (uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >=
-            len * parts)
-            continue;
-        const int old = uniform(__hip_atomic_fetch_add(c, lane_id() == 0 ? 1 : 0,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (old < len * parts) return (old / len) * n + lo + old % len;
-    }
-    return -1;
-}
-
-__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim,
-                                         int parts = 1) {
-    if (wave_id() == 0)  // all lanes store the same value
-        *s_claim = parts == 1 ? claim_tile(q, n, xcd) : claim_tile_parts(q, n, parts, xcd);
+__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim) {
+    if (wave_id() == 0) *s_claim = claim_tile(q, n, xcd);  // all lanes store the same value
     __syncthreads();
     const int L = uniform(*s_claim);
     __syncthreads();
@@ -202,34 +181,26 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             blocked_tile(L, MT, NT1, &mt, &nt);
             const MTile t = a.mtiles[mt];
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
-            gemm_tile<EPI_SILU_BF16>(a.x_perm, d, t.row0, t.rows, a.w_gate + wo, a.w_up + wo, d,
-                                     BN_GU, (int)d, a.h, f, (int64_t)nt * BN_GU, BN_GU, lds);
+            const int64_t prb = t.prow0 / 32;  // first packed row block
+            gemm_tile_pa<PA_SILU_PACKED>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows, (int)d,
+                                         a.w_gate + wo, a.w_up + wo, d,
+                                         a.h + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16,
+                                         lds);
             publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
             trace_tile(a, 1, L, xcd, t0);
         }
 
-    // 2. down tiles, each as S parts over consecutive K ranges (S = 1 unless
-    // f is deep): part p > 0 starts from part p-1's float32 partial, so the
-    // MFMA sequence is that of the whole tile, and the last part writes y.
+    // 2. down tiles
     const int n2 = MT * NT2;
-    const int S2 = (int)D.dn_splits();
-    const int64_t Ks = f / S2;
     if (n2 > 0)
         for (;;) {
-            const int Lp = next_tile(a.queues + NUM_XCD * QSTRIDE, n2, xcd, &s_claim, S2);
-            if (Lp < 0) break;
+            const int L = next_tile(a.queues + NUM_XCD * QSTRIDE, n2, xcd, &s_claim);
+            if (L < 0) break;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
-            const int part = Lp / n2, L = Lp % n2;
             int mt, nt;
             blocked_tile(L, MT, NT2, &mt, &nt);
             const MTile t = a.mtiles[mt];
-            const int64_t tile = (int64_t)mt * NT2 + nt;
-            if (wave_id() == 0) {
-                if (part == 0)
-                    wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
-                else
-                    wave_wait_geq(a.dn_part + tile, part, true, a.wait_ticks, a.status);
-            }
+            if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
             __syncthreads();
             const int producers =
                 uniform(__hip_atomic_load(a.gu_xcd + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -237,18 +208,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             else
                 invalidate_l1();
-            const int64_t k0 = (int64_t)part * Ks;
-            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
-            float *acc = a.dn_acc + tile * ACC_TILE_FLOATS;
-            const bool last = part == S2 - 1;
-            gemm_tile<EPI_BF16>(a.h + k0, f, t.row0, t.rows, a.w_down + wo, nullptr, f, BN_DN,
-                                (int)Ks, a.y, d, (int64_t)nt * BN_DN, BN_DN, lds,
-                                part > 0 ? acc : nullptr, last ? nullptr : acc);
-            if (last)
-                publish(a.dn_flag + tile, false, nullptr, xcd);
-            else
-                publish(a.dn_part + tile, true, nullptr, xcd);
-            trace_tile(a, 2, Lp, xcd, t0);
+            const int64_t prb = t.prow0 / 32;
+            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
+            gemm_tile_pa<PA_BF16>(a.h + prb * (f / 16) * 512, f / 16, t.rows, (int)f, a.w_down + wo,
+                                  nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d,
+                                  lds);
+            publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
+            trace_tile(a, 2, L, xcd, t0);
         }
 
     // 3. combine tiles

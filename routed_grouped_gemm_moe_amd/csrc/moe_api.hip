@@ -29,25 +29,25 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
-    L.dn_part = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
-    L.dn_acc = take(layer && D.dn_splits() > 1
-                        ? MT * (size_t)D.nt_dn() * (size_t)(4 * 4 * 16 * GEMM_THREADS) * sizeof(float)
-                        : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
     L.blk_counts = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
     L.blk_base = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
     L.counts = take(layer ? EL * sizeof(int32_t) : 0);
     L.offsets = take(layer ? (EL + 1) * sizeof(int32_t) : 0);
+    L.pstart = take(ffn ? (EL + 1) * sizeof(int32_t) : 0);
     L.perm_src = take(layer ? cap * sizeof(int32_t) : 0);
     L.inv_perm = take(layer ? Tk * sizeof(int32_t) : 0);
     L.mtiles = take(ffn ? MT * sizeof(MTile) : 0);
     L.n_mtiles = take(ffn ? sizeof(int32_t) : 0);
     L.mtile_base = take(ffn ? EL * sizeof(int32_t) : 0);
-    L.x_perm = take(layer ? cap * (size_t)D.d * 2 : 0);
-    L.h = take(ffn ? cap * (size_t)D.f * 2 : 0);
+    // packed activations (gemm_pa.h): x_perm gathered (layer) or repacked
+    // from the caller's rows (staged FFN), and h
+    const size_t pcap = (size_t)D.pcap();
+    L.x_perm = take(ffn ? pcap * (size_t)D.d * 2 : 0);
+    L.h = take(ffn ? pcap * (size_t)D.f * 2 : 0);
     L.y = take(layer ? cap * (size_t)D.d * 2 : 0);
     L.total = off;
     return L;
@@ -164,7 +164,7 @@ moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_
     return hip_status(launch_permute(D, (const bf16_t *)x, topk_ids, counts, offsets, perm_src,
                                      inv_perm, (bf16_t *)x_perm, at<int32_t>(ws, L.blk_counts),
                                      at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr,
-                                     nullptr, 0, (hipStream_t)stream));
+                                     nullptr, nullptr, 0, (hipStream_t)stream));
 }
 
 size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims) {
@@ -190,10 +190,13 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
     MTile *mt = at<MTile>(ws, L.mtiles);
     int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
     bf16_t *h = at<bf16_t>(ws, L.h);
-    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), s);
+    int32_t *pstart = at<int32_t>(ws, L.pstart);
+    bf16_t *xp = at<bf16_t>(ws, L.x_perm);
+    hipError_t e =
+        launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart, s);
+    if (e == hipSuccess) e = launch_pack_rows(D, (const bf16_t *)x_perm, offsets, pstart, xp, s);
     if (e == hipSuccess)
-        e = launch_gemm_gate_up(D, (const bf16_t *)x_perm, mt, nmt, (const bf16_t *)w_gate,
-                                (const bf16_t *)w_up, h, s);
+        e = launch_gemm_gate_up(D, xp, mt, nmt, (const bf16_t *)w_gate, (const bf16_t *)w_up, h, s);
     if (e == hipSuccess)
         e = launch_gemm_down(D, h, mt, nmt, (const bf16_t *)w_down, (bf16_t *)y_perm, s);
     return hip_status(e);
@@ -273,8 +276,9 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
                            at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
-                           at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), mt, nmt,
-                           mtile_base, at<int32_t>(ws, L.status), sched_ints, s);
+                           at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
+                           at<int32_t>(ws, L.pstart), mt, nmt, mtile_base,
+                           at<int32_t>(ws, L.status), sched_ints, s);
     mark(2);
     if (e == hipSuccess) {
         LayerArgs a;
@@ -295,8 +299,6 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.queues = at<int32_t>(ws, L.queues);
         a.gu_done = at<int32_t>(ws, L.gu_done);
         a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
-        a.dn_part = at<int32_t>(ws, L.dn_part);
-        a.dn_acc = at<float>(ws, L.dn_acc);
         a.dn_flag = at<int32_t>(ws, L.dn_flag);
         a.status = at<int32_t>(ws, L.status);
         a.out = out;

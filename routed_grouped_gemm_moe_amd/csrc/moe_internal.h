@@ -66,28 +66,26 @@ struct Dims {
     __host__ __device__ int64_t EL() const { return e_hi - e_lo; }
     __host__ __device__ int64_t cap() const { return T * k; }                       // worst-case local rows
     __host__ __device__ int64_t max_mtiles() const { return (cap() + EL() * (BM - 1)) / BM; }
+    // rows of the packed activation buffers: every expert segment starts on a
+    // 32-row boundary
+    __host__ __device__ int64_t pcap() const { return (cap() + EL() * 31 + 31) / 32 * 32; }
     __host__ __device__ int64_t nt_gu() const { return f / BN_GU; }
     __host__ __device__ int64_t nt_dn() const { return d / BN_DN; }
     __host__ __device__ int64_t perm_blocks() const { return (T + PERM_TB - 1) / PERM_TB; }
     __host__ __device__ int64_t comb_blocks() const { return (T + COMB_TOK - 1) / COMB_TOK; }
-    // K parts of a down tile in the persistent kernel: the largest power of two
-    // (<= 8) that keeps each part at least 3072 deep and a multiple of 32.
-    __host__ __device__ int64_t dn_splits() const {
-        int64_t S = 1;
-        while (S < 8 && f / (2 * S) >= 3072 && (f / (2 * S)) % 32 == 0) S *= 2;
-        return S;
-    }
 };
 
 // An m-tile of the grouped GEMM: rows [row0, row0 + rows) of expert e.
 struct MTile {
-    int32_t e, row0, rows, pad;
+    int32_t e, row0, rows;
+    int32_t prow0;  // first row in the packed buffers (x_perm, h): multiple of 32
 };
 
 // Byte offsets of every region in a workspace (each 256-byte aligned).
 struct Layout {
-    size_t status, queues, gu_done, gu_xcd, dn_part, dn_flag, route, dn_acc, ids, gates, blk_counts, blk_base, counts, offsets,
-        perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm, h, y, total;
+    size_t status, queues, gu_done, gu_xcd, dn_flag, route, ids, gates, blk_counts,
+        blk_base, counts, offsets, pstart, perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm,
+        h, y, total;
 };
 
 enum LayoutKind { LAYOUT_PERMUTE = 0, LAYOUT_FFN = 1, LAYOUT_LAYER = 2 };
@@ -111,18 +109,27 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
                         hipStream_t s);
 
+// Permute.  With pstart != NULL (the fused layer) x_perm is written in the
+// packed fragment layout of gemm_pa.h at the 32-aligned segment starts
+// pstart[], and the GEMM m-tile table is built and the scheduler state of the
+// persistent kernel cleared; otherwise x_perm is row-major at offsets[].
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
-                          int32_t *blk_counts, int32_t *blk_base,
-                          // optional: also build the GEMM m-tile table and clear the
-                          // scheduler state of the persistent kernel (NULL to skip)
+                          int32_t *blk_counts, int32_t *blk_base, int32_t *pstart,
                           MTile *mtiles, int32_t *n_mtiles, int32_t *mtile_base,
                           int32_t *sched_state, int64_t sched_state_ints, hipStream_t s);
 
+// Staged FFN: m-tile table and pstart[] from offsets[], then the row-major
+// x_perm repacked into xp (packed, pcap rows).
 hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
-                               int32_t *n_mtiles, int32_t *mtile_base, hipStream_t s);
+                               int32_t *n_mtiles, int32_t *mtile_base, int32_t *pstart,
+                               hipStream_t s);
+hipError_t launch_pack_rows(const Dims &D, const bf16_t *x_perm, const int32_t *offsets,
+                            const int32_t *pstart, bf16_t *xp, hipStream_t s);
 
-hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *x_perm, const MTile *mtiles,
+// Grouped GEMMs over packed activations: h (packed) from xp; y (row-major at
+// the m-tiles' row0) from h.
+hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
                                const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
                                bf16_t *h, hipStream_t s);
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
@@ -139,8 +146,7 @@ struct LayerArgs {
     const int32_t *ids, *inv_perm, *offsets, *mtile_base, *n_mtiles;
     const float *gates;
     const MTile *mtiles;
-    int32_t *queues, *gu_done, *gu_xcd, *dn_part, *dn_flag, *status;
-    float *dn_acc;  // float32 partials of split down tiles (dn_splits() > 1)
+    int32_t *queues, *gu_done, *gu_xcd, *dn_flag, *status;
     void *out;
     int out_f32;
     int64_t wait_ticks;  // flag-wait timeout in wall_clock64 ticks

@@ -8,7 +8,13 @@
 // per-expert token bitmaps, so a row's position is fixed by its token index:
 // offsets[e] + (rows of e in earlier token blocks) + (tokens before it in its
 // block that chose e).
-#include "moe_internal.h"
+//
+// For the fused layer the gathered rows go to the packed fragment layout of
+// the expert GEMM (gemm_pa.h), each expert segment starting at the 32-aligned
+// row pstart[e] (exclusive scan of the counts rounded up to 32); the row index
+// inside the segment is the same as in the row-major x_perm.  The same packed
+// gather repacks a caller's row-major x_perm for the staged FFN.
+#include "gemm_pa.h"
 
 namespace moe {
 namespace {
@@ -35,12 +41,13 @@ __global__ __launch_bounds__(PERM_TB) void hist_kernel(int64_t T, int64_t k, int
 constexpr int SCAN_THREADS = 1024;
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     int64_t EL, int64_t nblk, const int32_t *__restrict__ blk_counts, int32_t *__restrict__ blk_base,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, MTile *__restrict__ mtiles,
-    int32_t *__restrict__ n_mtiles, int32_t *__restrict__ mtile_base, int32_t *__restrict__ sched,
-    int64_t sched_ints) {
-    extern __shared__ int32_t s_tmp[];  // [2*EL + 2]
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ pstart,
+    MTile *__restrict__ mtiles, int32_t *__restrict__ n_mtiles, int32_t *__restrict__ mtile_base,
+    int32_t *__restrict__ sched, int64_t sched_ints) {
+    extern __shared__ int32_t s_tmp[];  // [3*EL + 3]
     int32_t *s_cnt = s_tmp;
     int32_t *s_mt = s_tmp + EL + 1;
+    int32_t *s_ps = s_tmp + 2 * EL + 2;
     for (int64_t e = threadIdx.x; e < EL; e += SCAN_THREADS) {
         int32_t run = 0;
         for (int64_t b = 0; b < nblk; ++b) {
@@ -51,25 +58,30 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         s_cnt[e] = run;
         counts[e] = run;
         s_mt[e] = (run + BM - 1) / BM;
+        s_ps[e] = (run + 31) & ~31;
     }
     for (int64_t i = threadIdx.x; i < sched_ints; i += SCAN_THREADS) sched[i] = 0;
     __syncthreads();
     if (threadIdx.x == 0) {
         // exclusive scans over at most 1024 experts
-        int32_t off = 0, mt = 0;
+        int32_t off = 0, mt = 0, ps = 0;
         for (int64_t e = 0; e < EL; ++e) {
-            int32_t c = s_cnt[e], m = s_mt[e];
+            int32_t c = s_cnt[e], m = s_mt[e], p = s_ps[e];
             s_cnt[e] = off;
             s_mt[e] = mt;
+            s_ps[e] = ps;
             off += c;
             mt += m;
+            ps += p;
         }
         s_cnt[EL] = off;
         s_mt[EL] = mt;
+        s_ps[EL] = ps;
     }
     __syncthreads();
     for (int64_t e = threadIdx.x; e <= EL; e += SCAN_THREADS) offsets[e] = s_cnt[e];
-    if (mtiles) {
+    if (pstart) {
+        for (int64_t e = threadIdx.x; e <= EL; e += SCAN_THREADS) pstart[e] = s_ps[e];
         if (threadIdx.x == 0) *n_mtiles = s_mt[EL];
         for (int64_t e = threadIdx.x; e < EL; e += SCAN_THREADS) {
             int32_t base = s_mt[e], n = s_mt[e + 1] - base;
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 t.e = (int32_t)e;
                 t.row0 = row0 + m * BM;
                 t.rows = min(BM, cnt - m * BM);
-                t.pad = 0;
+                t.prow0 = s_ps[e] + m * BM;
                 mtiles[base + m] = t;
             }
         }
@@ -123,8 +135,9 @@ __global__ __launch_bounds__(PERM_TB) void rank_kernel(int64_t T, int64_t k, int
         }
 }
 
-// Row gather: each workgroup copies GATHER_TOK token rows, each read once and
-// written to every local slot of that token.  16-byte vectors.
+// Row gather into row-major x_perm (moe_permute): each workgroup copies
+// GATHER_TOK token rows, each read once and written to every local slot of
+// that token.  16-byte vectors.
 constexpr int GATHER_TOK = 4;
 constexpr int GATHER_THREADS = 256;
 __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(int64_t T, int64_t d, int64_t k,
@@ -146,11 +159,80 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(int64_t T, int64
     }
 }
 
+// Packed gather: one workgroup per (packed 32-row block, 256 columns).  The
+// 32 source rows (x[perm_src[...]] for the fused layer, the caller's
+// row-major x_perm for the staged FFN; zeros for the padding rows of a
+// segment) are read as 512-byte row pieces, transposed through LDS and
+// written as 16 contiguous 1 KiB fragments.  LDS slot of fragment kk, lane
+// position p: kk*64 + (p ^ (kk & 15)), which spreads both the row-order
+// writes and the fragment-order reads over the banks.
+constexpr int PACK_THREADS = 256;
+constexpr int PACK_COLS = 256;
+__global__ __launch_bounds__(PACK_THREADS) void pack_kernel(int64_t d, int64_t EL,
+                                                            const bf16_t *__restrict__ src,
+                                                            const int32_t *__restrict__ perm_src,
+                                                            const int32_t *__restrict__ offsets,
+                                                            const int32_t *__restrict__ pstart,
+                                                            bf16_t *__restrict__ dst) {
+    __shared__ u32x4_t s_frag[32 * (PACK_COLS / 8)];  // 16 KiB
+    __shared__ int32_t s_row[32];
+    const int64_t rb = blockIdx.x;
+    const int64_t prow0 = rb * 32;
+    if (prow0 >= pstart[EL]) return;  // past the last segment (uniform)
+    if (threadIdx.x < 32) {
+        int64_t lo = 0, hi = EL - 1;  // segment holding prow0: last e with pstart[e] <= prow0
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (pstart[mid] <= prow0) lo = mid;
+            else hi = mid - 1;
+        }
+        const int64_t local = prow0 + threadIdx.x - pstart[lo];
+        const int64_t cnt = offsets[lo + 1] - offsets[lo];
+        int32_t r = -1;
+        if (local < cnt) r = perm_src ? perm_src[offsets[lo] + local] : (int32_t)(offsets[lo] + local);
+        s_row[threadIdx.x] = r;
+    }
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.y * PACK_COLS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = threadIdx.x + PACK_THREADS * i;
+        const int r = q >> 5, c = q & 31;
+        const int32_t srow = s_row[r];
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (srow >= 0) v = *reinterpret_cast<const u32x4_t *>(src + (int64_t)srow * d + c0 + c * 8);
+        const int kk = c >> 1, pos = r + 32 * (c & 1);
+        s_frag[kk * 64 + (pos ^ (kk & 15))] = v;
+    }
+    __syncthreads();
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(dst) + (rb * (d / 16) + blockIdx.y * (PACK_COLS / 16)) * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = threadIdx.x + PACK_THREADS * i;
+        const int kk = g >> 6, pos = g & 63;
+        o[g] = s_frag[kk * 64 + (pos ^ (kk & 15))];
+    }
+}
+
+hipError_t launch_pack(const Dims &D, const bf16_t *src, const int32_t *perm_src,
+                       const int32_t *offsets, const int32_t *pstart, bf16_t *dst, hipStream_t s) {
+    const int64_t nrb = D.pcap() / 32;
+    if (nrb == 0 || D.EL() == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nrb, (unsigned)(D.d / PACK_COLS)),
+                       dim3(PACK_THREADS), 0, s, D.d, D.EL(), src, perm_src, offsets, pstart, dst);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_pack_rows(const Dims &D, const bf16_t *x_perm, const int32_t *offsets,
+                            const int32_t *pstart, bf16_t *xp, hipStream_t s) {
+    return launch_pack(D, x_perm, nullptr, offsets, pstart, xp, s);
+}
 
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
-                          int32_t *blk_counts, int32_t *blk_base, MTile *mtiles,
+                          int32_t *blk_counts, int32_t *blk_base, int32_t *pstart, MTile *mtiles,
                           int32_t *n_mtiles, int32_t *mtile_base, int32_t *sched_state,
                           int64_t sched_state_ints, hipStream_t s) {
     const int64_t EL = D.EL(), nblk = D.perm_blocks();
@@ -160,8 +242,8 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
                            s, D.T, D.k, D.e_lo, EL, ids, blk_counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), (2 * EL + 2) * sizeof(int32_t), s,
-                       EL, nblk, blk_counts, blk_base, counts, offsets, mtiles, n_mtiles,
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), (3 * EL + 3) * sizeof(int32_t), s,
+                       EL, nblk, blk_counts, blk_base, counts, offsets, pstart, mtiles, n_mtiles,
                        mtile_base, sched_state, sched_state ? sched_state_ints : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nblk > 0) {
@@ -169,15 +251,17 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
                            EL * (PERM_TB / 32) * sizeof(uint32_t), s, D.T, D.k, D.e_lo, EL, ids,
                            offsets, blk_base, perm_src, inv_perm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const unsigned g = (unsigned)((D.T + GATHER_TOK - 1) / GATHER_TOK);
-        hipLaunchKernelGGL(gather_kernel, dim3(g), dim3(GATHER_THREADS), 0, s, D.T, D.d, D.k, x,
-                           inv_perm, x_perm);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (pstart) {
+            e = launch_pack(D, x, perm_src, offsets, pstart, x_perm, s);
+        } else {
+            const unsigned g = (unsigned)((D.T + GATHER_TOK - 1) / GATHER_TOK);
+            hipLaunchKernelGGL(gather_kernel, dim3(g), dim3(GATHER_THREADS), 0, s, D.T, D.d, D.k, x,
+                               inv_perm, x_perm);
+            e = hipGetLastError();
+        }
+        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
-
-hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
-                               int32_t *n_mtiles, int32_t *mtile_base, hipStream_t s);
 
 }  // namespace moe
