@@ -88,12 +88,15 @@ int moe_version(void);
  *   logits   f32  [T, E]  out, optional (NULL to skip)
  *   ws, ws_bytes               workspace of moe_route_workspace_bytes(dims)
  *                              bytes (256-byte aligned), or NULL
- * For E > 16 a workspace enables the fast path: MFMA logits with a rigorous
- * rounding-error bound pick the candidate experts, whose logits are then
- * evaluated in the defined order; ids and gates are the same as when every
- * logit is evaluated in that order, which is what happens with logits != NULL
- * or without a workspace (slower).  moe_route_workspace_bytes returns 0 when
- * no workspace is used.
+ * A workspace enables the fast paths.  E <= 16: one lane per token and one
+ * wave per chunk of the hidden dimension, with the router weights (widened to
+ * float32 in the workspace) as wave-uniform scalar operands, chunk sums kept
+ * in the workspace and folded by a second kernel.  E > 16: MFMA logits with a
+ * rigorous rounding-error bound pick the candidate experts, whose logits are
+ * then evaluated in the defined order.  Either way ids and gates are the same
+ * as when every logit is evaluated in that order, which is what happens with
+ * logits != NULL or without a workspace (slower).  moe_route_workspace_bytes
+ * returns 0 when no workspace is used.
  */
 size_t moe_route_workspace_bytes(const moe_dims *dims);
 moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,

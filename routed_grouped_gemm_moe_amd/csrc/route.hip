@@ -14,8 +14,12 @@
 // Three implementations of that one definition:
 //  - route_exact_kernel: every logit in the defined order (also the optional
 //    logits output).  Used for the logits output and when no workspace is given.
-//  - route_small_kernel (E <= 16): the same, with W_r staged in LDS and the
-//    activations prefetched, so it runs at memory speed.
+//  - route_tok_* (E <= 16, with a workspace): lane = token, wave = chunk, the
+//    router weights (widened to float32 once) wave-uniform: scalar loads and
+//    operands; chunk sums go through the workspace to a kernel that folds
+//    and selects.
+//  - route_small_kernel (E <= 16, no workspace): the same order with W_r
+//    staged in LDS and the activations prefetched.
 //  - fast path (E > 16, with a workspace): bf16 MFMA logits (split-K float32
 //    partials) are an approximation l~ with |l~ - l| <= eps, eps bounded from
 //    ||x_t||, ||w_e|| and the float32 unit roundoff (any summation order of d
@@ -281,6 +285,180 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
         if (tt >= T) break;
         wave_topk_gates(s_logit + tl * E, nullptr, (int)E, k, lane, ids + tt * k, gates + tt * k);
     }
+}
+
+// ------------------------------------------------------------ E <= 16, token lanes
+// Same defined order, laid out so that the router weights are wave-uniform:
+// lane = token (64 per wave), wave = one chunk c, so each step's weights of
+// every expert come from scalar loads and enter the FMAs as scalar operands;
+// each lane keeps EP accumulators.  Only the activations use the vector
+// memory path (each token row read once).
+//  route_tok_wprep_kernel: W_r widened to float32 (exact), wf[e][i];
+//  route_tok_chunks_kernel: workgroup = 64 tokens x 4 chunks x 4 experts;
+//    writes the chunk sums part[blk][c][e][lane];
+//  route_tok_finish_kernel: workgroup = 64 tokens; folds the 16 chunk sums by
+//    the balanced tree, adds the bias, then one lane per token selects (logit
+//    desc, id asc) and forms the gates with the same float32 operations, in
+//    the same order, as wave_topk_gates.
+constexpr int RTOK = 64;  // tokens per block (one per lane)
+
+// Rows E..EP-1 of wf are zero, so the chunk kernel runs all EP experts
+// without branches (their sums are never stored).
+__global__ __launch_bounds__(256) void route_tok_wprep_kernel(int64_t n, int64_t n_pad,
+                                                              const bf16_t *__restrict__ w,
+                                                              float *__restrict__ wf) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8 elements each
+    if (p * 8 >= n_pad) return;
+    const u32x4_t v = p * 8 < n ? reinterpret_cast<const u32x4_t *>(w)[p] : u32x4_t{0u, 0u, 0u, 0u};
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    f32x4v *o = reinterpret_cast<f32x4v *>(wf) + 2 * p;
+    o[0] = f32x4v{bf16x8_elem(v, 0), bf16x8_elem(v, 1), bf16x8_elem(v, 2), bf16x8_elem(v, 3)};
+    o[1] = f32x4v{bf16x8_elem(v, 4), bf16x8_elem(v, 5), bf16x8_elem(v, 6), bf16x8_elem(v, 7)};
+}
+
+// Each wave takes EG of the EP experts (two or more waves per SIMD, so one
+// wave's scalar-load waits overlap another's FMAs); grid = token blocks x 4
+// chunk quads x EP/EG expert groups.
+constexpr int RT_EG = 4;
+
+template <int EP>
+__global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_t d, int64_t E,
+                                                               const bf16_t *__restrict__ x,
+                                                               const float *__restrict__ wf,
+                                                               float *__restrict__ part) {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    constexpr int NG = EP / RT_EG;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t blk = blockIdx.x / (4 * NG);
+    const int rem = (int)(blockIdx.x % (4 * NG));
+    const int e0 = (rem / 4) * RT_EG;           // first expert of this wave
+    const int c = (rem % 4) * 4 + wave;         // chunk, wave-uniform
+    const int64_t t = blk * RTOK + lane;
+    const int64_t dc = d / 16;
+    const int nvec = (int)(dc / 8);  // 16-byte activation vectors per chunk
+    const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (t < T ? t : T - 1) * d + c * dc);
+    const int64_t wstride = d / 4;  // float4s between experts
+    const f32x4v *wp = reinterpret_cast<const f32x4v *>(wf + c * dc) + e0 * wstride;
+
+    float acc[RT_EG];
+#pragma unroll
+    for (int e = 0; e < RT_EG; ++e) acc[e] = 0.0f;
+    constexpr int PG = 16;  // activation vectors per prefetch group
+    u32x4_t xa[PG], xb[PG];
+    auto load = [&](u32x4_t (&r)[PG], int b) {
+#pragma unroll
+        for (int u = 0; u < PG; ++u) r[u] = (b + u < nvec) ? xp[b + u] : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    // the weights of vector v + 1 are loaded (scalar) while vector v computes
+    f32x4v wc0[RT_EG], wc1[RT_EG], wn0[RT_EG], wn1[RT_EG];
+    auto loadw = [&](f32x4v (&w0)[RT_EG], f32x4v (&w1)[RT_EG], int v) {
+        const int vv = v < nvec ? v : nvec - 1;
+#pragma unroll
+        for (int e = 0; e < RT_EG; ++e) {
+            w0[e] = wp[e * wstride + 2 * vv];
+            w1[e] = wp[e * wstride + 2 * vv + 1];
+        }
+    };
+    auto compute = [&](const u32x4_t (&r)[PG], int b) {
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+            if (b + u >= nvec) break;
+            loadw(wn0, wn1, b + u + 1);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float xf = bf16x8_elem(r[u], q);
+#pragma unroll
+                for (int e = 0; e < RT_EG; ++e)
+                    acc[e] = __builtin_fmaf(xf, q < 4 ? wc0[e][q] : wc1[e][q - 4], acc[e]);
+            }
+#pragma unroll
+            for (int e = 0; e < RT_EG; ++e) {
+                wc0[e] = wn0[e];
+                wc1[e] = wn1[e];
+            }
+        }
+    };
+    loadw(wc0, wc1, 0);
+    load(xa, 0);
+    for (int b = 0; b < nvec; b += 2 * PG) {
+        if (b + PG < nvec) load(xb, b + PG);
+        compute(xa, b);
+        if (b + 2 * PG < nvec) load(xa, b + 2 * PG);
+        if (b + PG < nvec) compute(xb, b + PG);
+    }
+    float *pp = part + ((blk * 16 + c) * EP + e0) * RTOK + lane;
+#pragma unroll
+    for (int e = 0; e < RT_EG; ++e)
+        if (e0 + e < E) pp[e * RTOK] = acc[e];
+}
+
+template <int EP>
+__global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_t E, int64_t k,
+                                                               const float *__restrict__ part,
+                                                               const float *__restrict__ bias,
+                                                               int32_t *__restrict__ ids,
+                                                               float *__restrict__ gates) {
+    __shared__ float s_l[EP][RTOK];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t blk = blockIdx.x;
+    const float *pb = part + blk * 16 * EP * RTOK + lane;
+    for (int e = wave; e < E; e += 4) {
+        float p[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) p[c] = pb[(c * EP + e) * RTOK];
+        // ((s0+s1)+(s2+s3))+((s4+s5)+(s6+s7)), ... : the chunk-lane butterfly
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+            for (int c = 0; c < 16; c += 2 * m) p[c] = p[c] + p[c + m];
+        float l = p[0];
+        if (bias) l = l + bias[e];
+        s_l[e][lane] = l;
+    }
+    __syncthreads();
+    const int64_t t = blk * RTOK + lane;
+    if (wave != 0 || t >= T) return;
+    float l[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) l[e] = e < E ? s_l[e][lane] : -__builtin_inff();
+    uint32_t taken = 0;
+    float sel[EP];
+    int32_t sid[EP];
+    float first = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+        sel[j] = 0.0f;
+        sid[j] = 0;
+        if (j >= k) continue;
+        // ascending scan with a strict '>' keeps the lowest id among ties
+        float bv = -__builtin_inff();
+        int32_t be = -1;
+#pragma unroll
+        for (int e = 0; e < EP; ++e)
+            if (e < E && !(taken & (1u << e)) && (be < 0 || l[e] > bv)) {
+                bv = l[e];
+                be = e;
+            }
+        taken |= 1u << be;
+        sel[j] = bv;
+        sid[j] = be;
+        if (j == 0) first = bv;
+    }
+    float ej[EP];
+    float denom = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+        ej[j] = j < k ? expf(sel[j] - first) : 0.0f;
+        if (j < k) denom += ej[j];
+    }
+#pragma unroll
+    for (int j = 0; j < EP; ++j)
+        if (j < k) {
+            ids[t * k + j] = sid[j];
+            gates[t * k + j] = ej[j] / denom;
+        }
 }
 
 // ------------------------------------------------------------ fast path
@@ -553,11 +731,38 @@ bool route_uses_fast_path(const Dims &D) {
     return D.E > 16 && (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8) <= 150 * 1024;
 }
 
+static int tok_ep(const Dims &D) { return D.E <= 8 ? 8 : 16; }
+
 size_t route_workspace_bytes(const Dims &D) {
-    if (!route_uses_fast_path(D)) return 0;
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    if (D.E <= 16)  // token-lane chunk sums, then W_r in float32
+        return al((size_t)((D.T + RTOK - 1) / RTOK) * 16 * tok_ep(D) * RTOK * sizeof(float)) +
+               al((size_t)tok_ep(D) * D.d * sizeof(float));
+    if (!route_uses_fast_path(D)) return 0;
     return al((size_t)route_splits(D) * D.T * D.E * 4) + al((size_t)D.E * D.d * 2) +
            al((size_t)D.E * 4);
+}
+
+template <int EP>
+static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
+                               int32_t *ids, float *gates, void *ws, hipStream_t s) {
+    const unsigned nblk = (unsigned)((D.T + RTOK - 1) / RTOK);
+    float *part = reinterpret_cast<float *>(ws);
+    float *wf = reinterpret_cast<float *>(
+        reinterpret_cast<char *>(ws) +
+        (((size_t)nblk * 16 * EP * RTOK * sizeof(float) + 255) & ~(size_t)255));
+    const int64_t n = D.E * D.d, n_pad = EP * D.d;
+    hipLaunchKernelGGL(route_tok_wprep_kernel, dim3((unsigned)((n_pad / 8 + 255) / 256)), dim3(256),
+                       0, s, n, n_pad, w, wf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3(nblk * 4 * (EP / RT_EG)), dim3(256), 0,
+                       s, D.T, D.d, D.E, x, wf, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
+                       part, bias, ids, gates);
+    return hipGetLastError();
 }
 
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
@@ -569,6 +774,10 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
         if (D.E <= 8) return launch_exact_t<1, 8>(D, x, w_router, bias, ids, gates, logits, s);
         if (D.E <= 16) return launch_exact_t<1, 16>(D, x, w_router, bias, ids, gates, logits, s);
         return launch_exact_t<4, 8>(D, x, w_router, bias, ids, gates, logits, s);
+    }
+    if (D.E <= 16 && ws && ws_bytes >= route_workspace_bytes(D)) {
+        if (D.E <= 8) return launch_tok_t<8>(D, x, w_router, bias, ids, gates, ws, s);
+        return launch_tok_t<16>(D, x, w_router, bias, ids, gates, ws, s);
     }
     if (!route_uses_fast_path(D)) {
         const size_t lds = (size_t)(D.E * stag_pitch(D.d) + RT_TOK * D.E * sizeof(float));
