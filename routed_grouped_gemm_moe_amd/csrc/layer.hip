@@ -245,11 +245,20 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 wave_wait_geq(flag, 1, need, a.wait_ticks, a.status);
             }
             __syncthreads();
-            for (int i = threadIdx.x; i < COMB_TOK * (BN_DN / 8); i += GEMM_THREADS) {
-                const int64_t t = (int64_t)tb * COMB_TOK + i / (BN_DN / 8);
-                if (t >= D.T) continue;
+            {
+                // thread: one 8-column vector of CNV tokens, all rows in flight
+                constexpr int CNV = COMB_TOK * (BN_DN / 8) / GEMM_THREADS;
+                static_assert(CNV * GEMM_THREADS == COMB_TOK * (BN_DN / 8), "combine tile shape");
+                const int i = threadIdx.x;
+                int64_t tt[CNV];
+                bool ok[CNV];
+#pragma unroll
+                for (int n = 0; n < CNV; ++n) {
+                    tt[n] = (int64_t)tb * COMB_TOK + (i + n * GEMM_THREADS) / (BN_DN / 8);
+                    ok[n] = tt[n] < D.T;
+                }
                 const int64_t v = (int64_t)nt * (BN_DN / 8) + i % (BN_DN / 8);
-                combine_vec<OUT_F32, true>(t, v, d, k, a.y, a.inv_perm, a.gates, a.out);
+                combine_vecs<OUT_F32, true, CNV>(tt, ok, v, d, k, a.y, a.inv_perm, a.gates, a.out);
             }
             trace_tile(a, 3, L, xcd, t0);
         }
