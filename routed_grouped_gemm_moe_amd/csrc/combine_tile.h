@@ -94,8 +94,10 @@ __device__ __forceinline__ void combine_vecs(const int64_t (&tt)[NV], const bool
 #pragma unroll
             for (int u = 0; u < SB; ++u) {
                 const int64_t j = j0 + u;
-                p[n][u] = (ok[n] && j < k) ? inv_perm[tt[n] * k + j] : -1;
-                w[n][u] = p[n][u] >= 0 ? gates[tt[n] * k + j] : 0.0f;
+                // the gate is loaded alongside the index, not after it
+                const bool in = ok[n] && j < k;
+                p[n][u] = in ? inv_perm[tt[n] * k + j] : -1;
+                w[n][u] = in ? gates[tt[n] * k + j] : 0.0f;
             }
 #pragma unroll
         for (int n = 0; n < NV; ++n)

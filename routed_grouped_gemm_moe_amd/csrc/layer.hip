@@ -214,6 +214,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                                   nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d,
                                   lds);
             publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
+            // count published down tiles (after the release above, so a
+            // reader that sees the full count also sees every y row)
+            if (wave_id() == 0)
+                __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             trace_tile(a, 2, L, xcd, t0);
         }
 
@@ -226,8 +231,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             if (L < 0) break;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             const int nt = L / NTB, tb = L % NTB;
-            // every (token, slot) of the tile waits for the down tile holding its row
-            for (int base = 0; base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
+            // every (token, slot) of the tile waits for the down tile holding its
+            // row -- unless every down tile has already been published
+            const bool all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)) >= n2;
+            for (int base = 0; !all_done && base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
                 const int i = base + (int)threadIdx.x;
                 const int64_t t = (int64_t)tb * COMB_TOK + i / k;
                 const int64_t j = i % k;

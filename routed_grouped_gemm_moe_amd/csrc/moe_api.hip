@@ -301,6 +301,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
         a.dn_flag = at<int32_t>(ws, L.dn_flag);
         a.status = at<int32_t>(ws, L.status);
+        a.dn_done = at<int32_t>(ws, L.status) + 32;  // 128 bytes past the status word
         a.out = out;
         a.out_f32 = out_dtype == MOE_F32;
         a.wait_ticks = wait_us * (wall_clock_hz() / 1000000);

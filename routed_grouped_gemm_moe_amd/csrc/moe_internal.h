@@ -147,6 +147,7 @@ struct LayerArgs {
     const float *gates;
     const MTile *mtiles;
     int32_t *queues, *gu_done, *gu_xcd, *dn_flag, *status;
+    int32_t *dn_done;  // published down tiles (in the status block, cleared per call)
     void *out;
     int out_f32;
     int64_t wait_ticks;  // flag-wait timeout in wall_clock64 ticks
