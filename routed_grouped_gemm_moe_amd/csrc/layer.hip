@@ -9,8 +9,8 @@
 //   2. down tiles (m-tile, 256 y columns): wait until gu_done[m-tile] counts
 //      every gate/up tile of that row block, then GEMM1; a finished tile sets
 //      dn_flag[m-tile, column block].
-//   3. combine tiles (32 tokens, 256 columns): wait for the dn_flag of every
-//      (m-tile, column block) their rows live in, then the gated sum.
+//   3. combine tiles (32 tokens, up to 4 x 256 columns): wait for the dn_flag
+//      of every (m-tile, column block) their rows live in, then the gated sum.
 // A finished down tile thus hands its rows to the combine through a device-
 // side flag as soon as it is written (the producer-consumer tile signaling of
 // Cui et al., abstract), not at a kernel boundary.
@@ -223,51 +223,45 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
         }
 
     // 3. combine tiles
+    // tile = COMB_TOK tokens x up to COMB_CB column blocks of BN_DN
     const int NTB = (int)D.comb_blocks();
-    const int n3 = NTB * NT2;
+    const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
+    const int n3 = NTB * NCG;
+    bool all_done = false;
     if (n3 > 0)
         for (;;) {
             const int L = next_tile(a.queues + 2 * NUM_XCD * QSTRIDE, n3, xcd, &s_claim);
             if (L < 0) break;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
-            const int nt = L / NTB, tb = L % NTB;
+            const int cg = L / NTB, tb = L % NTB;
+            const int nt0 = cg * COMB_CB, ncb = min(COMB_CB, NT2 - nt0);
             // every (token, slot) of the tile waits for the down tile holding its
             // row -- unless every down tile has already been published
-            const bool all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)) >= n2;
+            if (!all_done)  // stays true once seen
+                all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)) >= n2;
             for (int base = 0; !all_done && base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
                 const int i = base + (int)threadIdx.x;
                 const int64_t t = (int64_t)tb * COMB_TOK + i / k;
                 const int64_t j = i % k;
                 bool need = false;
-                const int32_t *flag = a.dn_flag;
+                int32_t mt = 0;
                 if (i < COMB_TOK * k && t < D.T) {
                     const int32_t p = a.inv_perm[t * k + j];
                     if (p >= 0) {
                         const int32_t e = a.ids[t * k + j] - (int32_t)D.e_lo;
-                        const int32_t mt = a.mtile_base[e] + (p - a.offsets[e]) / BM;
-                        flag = a.dn_flag + (int64_t)mt * NT2 + nt;
+                        mt = a.mtile_base[e] + (p - a.offsets[e]) / BM;
                         need = true;
                     }
                 }
-                wave_wait_geq(flag, 1, need, a.wait_ticks, a.status);
+                for (int c = 0; c < ncb; ++c)
+                    wave_wait_geq(a.dn_flag + (int64_t)mt * NT2 + nt0 + c, 1, need, a.wait_ticks,
+                                  a.status);
             }
             __syncthreads();
-            {
-                // thread: one 8-column vector of CNV tokens, all rows in flight
-                constexpr int CNV = COMB_TOK * (BN_DN / 8) / GEMM_THREADS;
-                static_assert(CNV * GEMM_THREADS == COMB_TOK * (BN_DN / 8), "combine tile shape");
-                const int i = threadIdx.x;
-                int64_t tt[CNV];
-                bool ok[CNV];
-#pragma unroll
-                for (int n = 0; n < CNV; ++n) {
-                    tt[n] = (int64_t)tb * COMB_TOK + (i + n * GEMM_THREADS) / (BN_DN / 8);
-                    ok[n] = tt[n] < D.T;
-                }
-                const int64_t v = (int64_t)nt * (BN_DN / 8) + i % (BN_DN / 8);
-                combine_vecs<OUT_F32, true, CNV>(tt, ok, v, d, k, a.y, a.inv_perm, a.gates, a.out);
-            }
+            combine_tile_staged<OUT_F32, COMB_TOK, BN_DN / 8, GEMM_THREADS>(
+                (int64_t)tb * COMB_TOK, D.T, (int64_t)nt0 * (BN_DN / 8), ncb, d, k, a.y,
+                a.inv_perm, a.gates, a.out, lds);
             trace_tile(a, 3, L, xcd, t0);
         }
 }

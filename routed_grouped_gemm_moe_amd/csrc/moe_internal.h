@@ -29,8 +29,10 @@ constexpr int GEMM_LDS_BYTES = NSTAGE * STAGE_BYTES;    // 128 KiB
 
 // Permute: tokens per block of the histogram / rank kernels.
 constexpr int PERM_TB = 256;
-// Combine tile of the persistent kernel: tokens x BN_DN columns.
+// Combine tile of the persistent kernel: COMB_TOK tokens x up to COMB_CB
+// blocks of BN_DN columns.
 constexpr int COMB_TOK = 32;
+constexpr int COMB_CB = 4;
 
 constexpr int NUM_XCD = 8;            // MI355X: 8 accelerator complex dies
 constexpr int QSTRIDE = 32;           // ints between queue counters (128 B apart)
