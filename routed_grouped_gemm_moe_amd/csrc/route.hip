@@ -29,6 +29,8 @@
 //    remaining candidates (typically k plus a few) get their logits evaluated
 //    in the defined order, and the selection and gates are taken from those
 //    exact values.  Ids and gates are therefore identical to the exact path.
+#include <type_traits>
+
 #include "gemm_tile.h"
 
 namespace moe {
@@ -522,6 +524,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void route_gemm_kernel(
 // One wave per token: bounds, candidates, exact logits of the candidates in
 // the defined order, selection and gates.
 constexpr int RF_WAVES = 4;
+// RMAX = expert slots per lane (E <= 64 * RMAX), a template parameter so the
+// bound, selection and compaction loops run over only the slots E needs.
+template <int RMAX>
 __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     int64_t T, int64_t d, int64_t E, int64_t k, int S, const bf16_t *__restrict__ x,
     const bf16_t *__restrict__ wt, const float *__restrict__ wnorm, const float *__restrict__ bias,
@@ -572,27 +577,27 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     const float gam = ((float)(2 * d + d / 16 + 8) * 0x1p-24f) * (1.0f + 0x1p-10f);
 
     // bounds of this lane's experts e = lane + 64*r2
-    constexpr int RMAX = 16;  // E <= 1024
     float lo[RMAX], hi[RMAX];
 #pragma unroll
     for (int r2 = 0; r2 < RMAX; ++r2) {
         lo[r2] = -__builtin_inff();
         hi[r2] = -__builtin_inff();
     }
-    // 4 expert slots x up to 8 partials loaded before any is summed
+    // QN expert slots x up to 8 partials loaded before any is summed
+    constexpr int QN = RMAX < 4 ? RMAX : 4;
 #pragma unroll
-    for (int r0 = 0; r0 < RMAX; r0 += 4) {
+    for (int r0 = 0; r0 < RMAX; r0 += QN) {
         if (r0 * 64 >= E) break;  // wave-uniform
-        float pv[4][8];
+        float pv[QN][8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QN; ++q) {
             const int64_t e = (r0 + q) * 64 + lane;
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2)
                 pv[q][s2] = (s2 < S && e < E) ? part[((int64_t)s2 * T + t) * E + e] : 0.0f;
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QN; ++q) {
             const int64_t e = (r0 + q) * 64 + lane;
             if (e >= E) continue;
             float la = 0.0f;
@@ -807,12 +812,20 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
                        s, D.T, D.d, D.E, S, x, w_router, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds = (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8);
-    e = hipFuncSetAttribute((const void *)route_refine_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    auto refine = [&](auto rk) -> hipError_t {
+        constexpr int R = decltype(rk)::value;
+        hipError_t er = hipFuncSetAttribute((const void *)route_refine_kernel<R>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (er != hipSuccess) return er;
+        hipLaunchKernelGGL(route_refine_kernel<R>, dim3((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES)),
+                           dim3(64 * RF_WAVES), lds, s, D.T, D.d, D.E, D.k, S, x, wt, wnorm, bias,
+                           part, ids, gates);
+        return hipSuccess;
+    };
+    if (D.E <= 128) e = refine(std::integral_constant<int, 2>{});
+    else if (D.E <= 256) e = refine(std::integral_constant<int, 4>{});
+    else e = refine(std::integral_constant<int, 16>{});
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(route_refine_kernel, dim3((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES)),
-                       dim3(64 * RF_WAVES), lds, s, D.T, D.d, D.E, D.k, S, x, wt, wnorm, bias, part,
-                       ids, gates);
     return hipGetLastError();
 }
 
