@@ -11,6 +11,8 @@
 // flight share weight and activation tiles) and each of the 8 XCDs takes one
 // contiguous eighth of that order: workgroup b runs on XCD b % 8 (round-robin
 // dispatch), so the workgroups sharing a tile meet in one XCD's L2.
+#include <algorithm>
+
 #include "gemm_pa.h"
 
 namespace moe {
@@ -21,9 +23,12 @@ __global__ __launch_bounds__(1024) void build_mtiles_kernel(int64_t EL,
                                                             MTile *__restrict__ mtiles,
                                                             int32_t *__restrict__ n_mtiles,
                                                             int32_t *__restrict__ mtile_base,
-                                                            int32_t *__restrict__ pstart) {
+                                                            int32_t *__restrict__ pstart,
+                                                            int32_t *__restrict__ clear,
+                                                            int64_t clear_ints) {
     extern __shared__ int32_t s_mt[];  // [2 * (EL + 1)]: m-tile starts, packed segment starts
     int32_t *s_ps = s_mt + EL + 1;
+    for (int64_t i = threadIdx.x; i < clear_ints; i += 1024) clear[i] = 0;
     for (int64_t e = threadIdx.x; e < EL; e += 1024) {
         const int32_t c = offsets[e + 1] - offsets[e];
         s_mt[e] = (c + BM - 1) / BM;
@@ -70,16 +75,29 @@ __device__ __forceinline__ int xcd_tile(int n) {
     return L < n ? L : -1;
 }
 
+// State of the down tiles cut into K halves (unused by gate/up): the same
+// tiles as in the persistent kernel with `grid` workgroups are cut, so both
+// paths produce the same bits.
+struct DownSplit {
+    int32_t *cnt;
+    float *part;
+    int grid;
+};
+
 template <bool GATE_UP>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     int64_t d, int64_t f, const bf16_t *__restrict__ A, const MTile *__restrict__ mtiles,
     const int32_t *__restrict__ n_mtiles, const bf16_t *__restrict__ W0,
-    const bf16_t *__restrict__ W1, bf16_t *__restrict__ out) {
+    const bf16_t *__restrict__ W1, bf16_t *__restrict__ out, DownSplit ds) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int MT = *n_mtiles;
     const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
-    const int L = xcd_tile(MT * NT);
-    if (L < 0) return;
+    const int nsp =
+        GATE_UP ? 0 : dn_split_tiles(Dims{0, d, f, 0, 0, 0, 0}.dn_deep(), MT * NT, ds.grid);
+    const int LS = xcd_tile(MT * NT + nsp);
+    if (LS < 0) return;
+    int L, part, st;
+    dn_claim(LS, MT * NT, nsp, &L, &part, &st);
     int mt, nt;
     blocked_tile(L, MT, NT, &mt, &nt);
     const MTile t = mtiles[mt];
@@ -90,24 +108,30 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
         gemm_tile_pa<PA_SILU_PACKED>(A + prb * (d / 16) * 512, d / 16, t.rows, (int)d, wg, wu, d,
                                      out + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16, lds);
     } else {
-        const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
-        gemm_tile_pa<PA_BF16>(A + prb * (f / 16) * 512, f / 16, t.rows, (int)f, wd, nullptr, f,
-                              out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
+        // a cut tile computes K half `part`, starting at k = part * f / 2
+        const int64_t Kp = part < 0 ? f : f / 2, k0 = part < 0 ? 0 : part * Kp;
+        const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
+        const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (2 * BM * BN_DN), part};
+        gemm_tile_pa<PA_BF16>(A + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, wd,
+                              nullptr, f, out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
+                              part < 0 ? nullptr : &sc);
     }
 }
 
 template <bool GATE_UP>
 hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, const int32_t *n_mtiles,
-                       const bf16_t *W0, const bf16_t *W1, bf16_t *out, hipStream_t s) {
+                       const bf16_t *W0, const bf16_t *W1, bf16_t *out, const DownSplit &ds,
+                       hipStream_t s) {
     const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
     int64_t grid = D.max_mtiles() * NT;
+    if (!GATE_UP && D.dn_deep()) grid += std::min<int64_t>(grid, SPLIT_MAX);  // cut halves
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     if (grid == 0) return hipSuccess;
     hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_kernel<GATE_UP>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       GEMM_LDS_BYTES, s, D.d, D.f, A, mtiles, n_mtiles, W0, W1, out);
+                       GEMM_LDS_BYTES, s, D.d, D.f, A, mtiles, n_mtiles, W0, W1, out, ds);
     return hipGetLastError();
 }
 
@@ -115,23 +139,24 @@ hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, cons
 
 hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mtiles,
                                int32_t *n_mtiles, int32_t *mtile_base, int32_t *pstart,
-                               hipStream_t s) {
+                               int32_t *clear, int64_t clear_ints, hipStream_t s) {
     hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024),
                        2 * (D.EL() + 1) * sizeof(int32_t), s, D.EL(), offsets, mtiles, n_mtiles,
-                       mtile_base, pstart);
+                       mtile_base, pstart, clear, clear_ints);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
                                const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
                                bf16_t *h, hipStream_t s) {
-    return launch_gemm<true>(D, xp, mtiles, n_mtiles, w_gate, w_up, h, s);
+    return launch_gemm<true>(D, xp, mtiles, n_mtiles, w_gate, w_up, h, DownSplit{}, s);
 }
 
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
                             const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
-                            hipStream_t s) {
-    return launch_gemm<false>(D, h, mtiles, n_mtiles, w_down, nullptr, y, s);
+                            int32_t *dn_cnt, float *dn_part, int grid, hipStream_t s) {
+    return launch_gemm<false>(D, h, mtiles, n_mtiles, w_down, nullptr, y,
+                              DownSplit{dn_cnt, dn_part, grid}, s);
 }
 
 }  // namespace moe

@@ -53,6 +53,8 @@ __host__ __device__ __forceinline__ int64_t packed_chunk(int64_t row, int64_t c,
 
 __device__ i32x4_t raw_buffer_load_v4(i32x4_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+// Cache-policy operand of a buffer load: sc1 (bit 4).
+constexpr int PA_CPOL_SC1 = 16;
 
 // Memory instruction issued after MFMA k (0..15) of sub-step q (0..3):
 // kind 1: B-fragment LDS read idx (of sub-step q+1; of the next stage's
@@ -183,6 +185,97 @@ __device__ __forceinline__ void pa_kloop(f32x16_t (&acc)[4][4], const i32x4_t &r
 
 #pragma clang diagnostic pop
 
+// A down tile whose K depth is cut in two halves, computed by two workgroups
+// (possibly on different XCDs) in either order.  Each stores its float32
+// accumulators as partial `self` of the tile and arrives at *cnt; the later
+// one then forms y = bf16(P0 + P1) from the two partials, which does not
+// depend on the order of arrival.  *cnt starts at zero.
+struct SplitCtl {
+    int32_t *cnt;
+    float *part;  // 2 x (256 x 256) floats, each in accumulator-register order
+    int self;     // which half this call computes (0 or 1)
+};
+
+// Float offset of accumulator vector (wave, i, j, v/4 = g) of lane `lane`:
+// every 16-byte store or load of a wave covers 1 KiB contiguously.
+__device__ __forceinline__ int split_slot(int wave, int i, int j, int g, int lane) {
+    return ((((wave * 4 + i) * 4 + j) * 4 + g) * 64 + lane) * 4;
+}
+
+// y element (row r, column c) of a 256 x 256 bf16 tile staged in LDS: rows
+// of 256, 16-byte chunk index xor-ed with r & 7.
+__device__ __forceinline__ int y_stage_index(int r, int c) {
+    return r * 256 + (((c >> 3) ^ (r & 7)) << 3) + (c & 7);
+}
+
+// Returns false in the first-arriving workgroup.  In the second, the bf16
+// tile y = P0 + P1 is left in LDS (y_stage_index layout).  LDS must be free
+// (the K loop ends with a barrier); the caller copies the tile out.
+__device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitCtl &sp, int tid,
+                                             int wave, int lane, char *lds) {
+    float *mine = sp.part + sp.self * (BM * BN_DN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4_t *>(mine + split_slot(wave, i, j, g, lane)) =
+                    f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]};
+    // every wave's stores reached L2; one agent-scope release RMW writes this
+    // XCD's L2 back and counts the arrival
+    wait_vmcnt<0>();
+    __syncthreads();
+    int *s_x = reinterpret_cast<int *>(lds);
+    if (wave == 0) {
+        // lane 0 adds 1, the others 0: lane 0's pre-op value is the arrival
+        const int old = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
+            sp.cnt, lane == 0 ? 1 : 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
+        *s_x = old;  // every lane stores the same value
+    }
+    __syncthreads();
+    const bool last = __builtin_amdgcn_readfirstlane(*s_x) != 0;
+    __syncthreads();
+    if (!last) return false;
+    // Both partials, read with device-coherent loads: the other one may come
+    // from another XCD, and this XCD's L2 may hold stale lines of the buffer.
+    // Buffer loads with the sc1 cache-policy bit (agent-scope coherence in
+    // gfx950's memory model) miss in that L2.  16 loads per batch in flight.
+    i32x4_t r0 = make_rsrc(sp.part, BM * BN_DN * sizeof(float));
+    i32x4_t r1 = make_rsrc(sp.part + BM * BN_DN, BM * BN_DN * sizeof(float));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        r0[w] = __builtin_amdgcn_readfirstlane(r0[w]);
+        r1[w] = __builtin_amdgcn_readfirstlane(r1[w]);
+    }
+    bf16_t *st = reinterpret_cast<bf16_t *>(lds);
+    for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 8) {
+        i32x4_t p0[8], p1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = (it + u) * GEMM_THREADS + tid;  // float4 index
+            p0[u] = raw_buffer_load_v4(r0, idx * 16, 0, PA_CPOL_SC1);
+            p1[u] = raw_buffer_load_v4(r1, idx * 16, 0, PA_CPOL_SC1);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int idx = (it + u) * GEMM_THREADS + tid;
+            const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) & 3, i = (idx >> 10) & 3,
+                      w = idx >> 12;
+            const int r = (w >> 1) * 128 + i * 32 + 8 * g + 4 * (l >> 5);
+            const int c = (w & 1) * 128 + j * 32 + (l & 31);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st[y_stage_index(r + e, c)] =
+                    f2bf(__int_as_float(p0[u][e]) + __int_as_float(p1[u][e]));
+        }
+    }
+    (void)acc;
+    (void)wave;
+    return true;
+}
+
 // One tile.
 //   Ap     packed A at the tile's first row block and first k-step
 //   a_kb   fragments per packed row block (the full K of that matrix / 16)
@@ -191,12 +284,18 @@ __device__ __forceinline__ void pa_kloop(f32x16_t (&acc)[4][4], const i32x4_t &r
 //   out    PA_SILU_PACKED: packed h at (first row block, first of the 8
 //          k-steps this tile writes), o_kb fragments per h row block;
 //          PA_BF16: y at (row 0, column 0) of the tile, row stride o_ld
+//   sp     PA_BF16 only: this call computes one of two K halves of the tile
+//          (Ap and B0 point at its first k, K is the half's depth); the two
+//          halves meet through sp (see SplitCtl) and the later one writes y.
+// Returns whether this call wrote the tile's output (false only for the
+// earlier half of a split tile).
 // LDS: PA_LDS_BYTES at lds, free again when the call returns.
 template <int EPI>
-__device__ __forceinline__ void gemm_tile_pa(const bf16_t *__restrict__ Ap, int64_t a_kb,
+__device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int64_t a_kb,
                                              int a_rows, int K, const bf16_t *__restrict__ B0,
                                              const bf16_t *__restrict__ B1, int64_t ldb,
-                                             bf16_t *__restrict__ out, int64_t o_ld, char *lds) {
+                                             bf16_t *__restrict__ out, int64_t o_ld, char *lds,
+                                             const SplitCtl *sp = nullptr) {
     constexpr bool GATE_UP = EPI == PA_SILU_PACKED;
     // An opaque copy of the thread index keeps lane-dependent addresses from
     // being hoisted out of a persistent tile loop (and their registers live).
@@ -275,17 +374,19 @@ __device__ __forceinline__ void gemm_tile_pa(const bf16_t *__restrict__ Ap, int6
         // y tile: 256 rows x 256 columns, row-major in LDS with the 16-byte
         // chunk index of row r xor-ed with r & 7 (even spread of the row
         // writes of the two lane halves over the banks).
+        if (sp) {
+            if (!split_reduce(acc, *sp, tid, wave, lane, lds)) return false;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                for (int v = 0; v < 16; ++v) {
+                    const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = wn * 128 + j * 32 + l32;
-                    st[r * 256 + (((col >> 3) ^ (r & 7)) << 3) + (col & 7)] = f2bf(acc[i][j][v]);
+                    for (int j = 0; j < 4; ++j)
+                        st[y_stage_index(r, wn * 128 + j * 32 + l32)] = f2bf(acc[i][j][v]);
                 }
-            }
+        }
         __syncthreads();
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < a_rows * 32; g += GEMM_THREADS) {
@@ -293,6 +394,7 @@ __device__ __forceinline__ void gemm_tile_pa(const bf16_t *__restrict__ Ap, int6
             reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld)[c] = src[r * 32 + (c ^ (r & 7))];
         }
     }
+    return true;
 }
 
 }  // namespace moe

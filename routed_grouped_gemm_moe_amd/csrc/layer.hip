@@ -139,7 +139,8 @@ __device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, in
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // Optional per-tile trace (measurement aid): one 4 x int64 record per tile,
-// {kind << 32 | tile, workgroup << 8 | xcd, start, end}, times in
+// {kind << 32 | tile, workgroup << 8 | xcd, start, end} (kind 1 gate/up, 2
+// down, 4 half of a cut down tile, 3 combine), times in
 // wall_clock64 ticks.  Written by lane 0 of wave 0; slots come from an atomic
 // counter at trace[0]; records past the capacity are dropped.
 __device__ __forceinline__ void trace_tile(const LayerArgs &a, int kind, int L, int xcd,
@@ -190,13 +191,17 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             trace_tile(a, 1, L, xcd, t0);
         }
 
-    // 2. down tiles
+    // 2. down tiles; those of the last partial round (of gridDim.x
+    // workgroups) are cut into two K halves, claimed after the whole tiles
     const int n2 = MT * NT2;
+    const int nsp = dn_split_tiles(D.dn_deep(), n2, (int)gridDim.x);
     if (n2 > 0)
         for (;;) {
-            const int L = next_tile(a.queues + NUM_XCD * QSTRIDE, n2, xcd, &s_claim);
-            if (L < 0) break;
+            const int LS = next_tile(a.queues + NUM_XCD * QSTRIDE, n2 + nsp, xcd, &s_claim);
+            if (LS < 0) break;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+            int L, part, st;
+            dn_claim(LS, n2, nsp, &L, &part, &st);
             int mt, nt;
             blocked_tile(L, MT, NT2, &mt, &nt);
             const MTile t = a.mtiles[mt];
@@ -209,17 +214,25 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             else
                 invalidate_l1();
             const int64_t prb = t.prow0 / 32;
-            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f;
-            gemm_tile_pa<PA_BF16>(a.h + prb * (f / 16) * 512, f / 16, t.rows, (int)f, a.w_down + wo,
-                                  nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d,
-                                  lds);
+            // a cut tile computes K half `part`, starting at k = part * f / 2
+            const int64_t Kp = part < 0 ? f : f / 2, k0 = part < 0 ? 0 : part * Kp;
+            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
+            const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (2 * BM * BN_DN), part};
+            const bool wrote = gemm_tile_pa<PA_BF16>(
+                a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
+                nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
+                part < 0 ? nullptr : &sc);
+            if (!wrote) {  // the other half writes the tile
+                trace_tile(a, 4, LS, xcd, t0);
+                continue;
+            }
             publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
             // count published down tiles (after the release above, so a
             // reader that sees the full count also sees every y row)
             if (wave_id() == 0)
                 __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-            trace_tile(a, 2, L, xcd, t0);
+            trace_tile(a, part < 0 ? 2 : 4, LS, xcd, t0);
         }
 
     // 3. combine tiles

@@ -25,11 +25,15 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     const bool ffn = kind == LAYOUT_FFN || layer;
     const bool perm = kind == LAYOUT_PERMUTE || layer;
     // scheduler state first and contiguous (cleared by one kernel)
-    L.status = take(layer ? 256 : 0);
+    L.status = take(ffn ? 256 : 0);  // offset 0 of layer and FFN workspaces
     L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
+    // cut down tiles (deep down GEMMs only): arrival counters, then partials
+    const bool split = ffn && D.dn_deep();
+    L.dn_cnt = take(split ? SPLIT_MAX * sizeof(int32_t) : 0);
+    L.dn_part = take(split ? (size_t)SPLIT_MAX * 2 * BM * BN_DN * sizeof(float) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
@@ -192,13 +196,17 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
     bf16_t *h = at<bf16_t>(ws, L.h);
     int32_t *pstart = at<int32_t>(ws, L.pstart);
     bf16_t *xp = at<bf16_t>(ws, L.x_perm);
-    hipError_t e =
-        launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart, s);
+    // cleared per call: the status word and the cut down tiles' counters
+    const int64_t clear_ints = (int64_t)((L.dn_cnt - L.status) / 4) + (D.dn_deep() ? SPLIT_MAX : 0);
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
+                                       at<int32_t>(ws, L.status), clear_ints, s);
     if (e == hipSuccess) e = launch_pack_rows(D, (const bf16_t *)x_perm, offsets, pstart, xp, s);
     if (e == hipSuccess)
         e = launch_gemm_gate_up(D, xp, mt, nmt, (const bf16_t *)w_gate, (const bf16_t *)w_up, h, s);
     if (e == hipSuccess)
-        e = launch_gemm_down(D, h, mt, nmt, (const bf16_t *)w_down, (bf16_t *)y_perm, s);
+        e = launch_gemm_down(D, h, mt, nmt, (const bf16_t *)w_down, (bf16_t *)y_perm,
+                             at<int32_t>(ws, L.dn_cnt), at<float>(ws, L.dn_part), layer_grid_size(),
+                             s);
     return hip_status(e);
 }
 
@@ -266,8 +274,9 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     int32_t *mtile_base = at<int32_t>(ws, L.mtile_base);
     int32_t *inv_perm = at<int32_t>(ws, L.inv_perm);
     bf16_t *x_perm = at<bf16_t>(ws, L.x_perm);
-    const int64_t sched_ints = (int64_t)((L.dn_flag - L.status) / 4) +
-                               D.max_mtiles() * D.nt_dn();
+    const int64_t sched_ints =
+        D.dn_deep() ? (int64_t)((L.dn_cnt - L.status) / 4) + SPLIT_MAX
+                    : (int64_t)((L.dn_flag - L.status) / 4) + D.max_mtiles() * D.nt_dn();
 
     mark(0);
     hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
@@ -300,6 +309,8 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.gu_done = at<int32_t>(ws, L.gu_done);
         a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
         a.dn_flag = at<int32_t>(ws, L.dn_flag);
+        a.dn_cnt = at<int32_t>(ws, L.dn_cnt);
+        a.dn_part = at<float>(ws, L.dn_part);
         a.status = at<int32_t>(ws, L.status);
         a.dn_done = at<int32_t>(ws, L.status) + 32;  // 128 bytes past the status word
         a.out = out;
@@ -321,11 +332,11 @@ moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_byt
     Dims D;
     moe_status st = check_dims(dims, &D);
     if (st != MOE_OK) return st;
-    const Layout L = make_layout(D, LAYOUT_LAYER);
-    if ((st = check_ws((void *)ws, ws_bytes, L.total)) != MOE_OK) return st;
+    // the status word sits at offset 0 of a layer or an FFN workspace
+    if ((st = check_ws((void *)ws, ws_bytes, 256)) != MOE_OK) return st;
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MOE_ERR_HIP;
     int32_t v = 0;
-    if (hipMemcpy(&v, at<int32_t>((void *)ws, L.status), sizeof v, hipMemcpyDeviceToHost) !=
+    if (hipMemcpy(&v, (const int32_t *)ws, sizeof v, hipMemcpyDeviceToHost) !=
         hipSuccess)
         return MOE_ERR_HIP;
     return v == 0 ? MOE_OK : (moe_status)v;
