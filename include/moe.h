@@ -127,7 +127,11 @@ moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_
  *   offsets i32  [E_loc+1]     device-resident segment offsets
  *   w_gate, w_up bf16 [E_loc, f, d];  w_down bf16 [E_loc, d, f]
  *   y_perm  bf16 [T*k, d] out  y = (silu(x Wg^T) * (x Wu^T)) Wd^T per row
- * The intermediate h is rounded to bf16; accumulation is float32.
+ * The intermediate h is rounded to bf16; accumulation is float32.  When
+ * f >= 8192 the down tiles of the schedule's last partial round (as the
+ * persistent kernel of moe_layer runs it) are summed as two K halves added
+ * once in float32, exactly as moe_layer does, so both give the same bits.
+ * The workspace starts with the status word read by moe_device_status.
  */
 size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims);
 moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
@@ -161,8 +165,9 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
                      moe_dtype out_dtype, int32_t *topk_ids_out, float *topk_w_out, void *ws,
                      size_t ws_bytes, void *stream);
 
-/* Synchronises `stream`, then reads the device status word that moe_layer
- * keeps in `ws` (MOE_OK, or MOE_ERR_DEVICE_TIMEOUT if a flag wait gave up). */
+/* Synchronises `stream`, then reads the device status word at offset 0 of a
+ * workspace last used by moe_layer or moe_expert_ffn (MOE_OK, or
+ * MOE_ERR_DEVICE_TIMEOUT if a flag wait gave up).  ws_bytes must be >= 256. */
 moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_bytes, void *stream);
 
 /* ---- Stage timing (measurement aid).  When enabled, moe_layer records HIP
