@@ -92,12 +92,12 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int MT = *n_mtiles;
     const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
-    const int nsp =
-        GATE_UP ? 0 : dn_split_tiles(Dims{0, d, f, 0, 0, 0, 0}.dn_deep(), MT * NT, ds.grid);
-    const int LS = xcd_tile(MT * NT + nsp);
+    const int S = GATE_UP ? 1 : Dims{0, d, f, 0, 0, 0, 0}.dn_parts();
+    const int nsp = dn_split_tiles(S, MT * NT, ds.grid);
+    const int LS = xcd_tile(MT * NT + (S - 1) * nsp);
     if (LS < 0) return;
     int L, part, st;
-    dn_claim(LS, MT * NT, nsp, &L, &part, &st);
+    dn_claim(LS, MT * NT, nsp, S, &L, &part, &st);
     int mt, nt;
     blocked_tile(L, MT, NT, &mt, &nt);
     const MTile t = mtiles[mt];
@@ -108,10 +108,10 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
         gemm_tile_pa<PA_SILU_PACKED>(A + prb * (d / 16) * 512, d / 16, t.rows, (int)d, wg, wu, d,
                                      out + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16, lds);
     } else {
-        // a cut tile computes K half `part`, starting at k = part * f / 2
-        const int64_t Kp = part < 0 ? f : f / 2, k0 = part < 0 ? 0 : part * Kp;
+        // a cut tile computes K part `part`, starting at k = part * f / S
+        const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
         const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
-        const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (2 * BM * BN_DN), part};
+        const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (CUT_MAX * BM * BN_DN), part, S};
         gemm_tile_pa<PA_BF16>(A + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, wd,
                               nullptr, f, out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
                               part < 0 ? nullptr : &sc);
@@ -124,7 +124,8 @@ hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, cons
                        hipStream_t s) {
     const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
     int64_t grid = D.max_mtiles() * NT;
-    if (!GATE_UP && D.dn_deep()) grid += std::min<int64_t>(grid, SPLIT_MAX);  // cut halves
+    if (!GATE_UP && D.dn_parts() > 1)  // extra claims of the cut tiles' parts
+        grid += (D.dn_parts() - 1) * std::min<int64_t>(grid, SPLIT_MAX);
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     if (grid == 0) return hipSuccess;
     hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_kernel<GATE_UP>,

@@ -185,15 +185,17 @@ __device__ __forceinline__ void pa_kloop(f32x16_t (&acc)[4][4], const i32x4_t &r
 
 #pragma clang diagnostic pop
 
-// A down tile whose K depth is cut in two halves, computed by two workgroups
-// (possibly on different XCDs) in either order.  Each stores its float32
-// accumulators as partial `self` of the tile and arrives at *cnt; the later
-// one then forms y = bf16(P0 + P1) from the two partials, which does not
-// depend on the order of arrival.  *cnt starts at zero.
+// A down tile whose K depth is cut into nparts parts, computed by as many
+// workgroups (possibly on different XCDs) in any order.  Each stores its
+// float32 accumulators as partial `self` of the tile and arrives at *cnt;
+// the last one forms y = bf16(((P0 + P1) + P2) + ...) from all partials in
+// part order, which does not depend on the order of arrival.  *cnt starts at
+// zero.
 struct SplitCtl {
     int32_t *cnt;
-    float *part;  // 2 x (256 x 256) floats, each in accumulator-register order
-    int self;     // which half this call computes (0 or 1)
+    float *part;  // nparts x (256 x 256) floats, each in accumulator-register order
+    int self;     // which part this call computes (0 .. nparts-1)
+    int nparts;   // 2 or 4
 };
 
 // Float offset of accumulator vector (wave, i, j, v/4 = g) of lane `lane`:
@@ -208,9 +210,10 @@ __device__ __forceinline__ int y_stage_index(int r, int c) {
     return r * 256 + (((c >> 3) ^ (r & 7)) << 3) + (c & 7);
 }
 
-// Returns false in the first-arriving workgroup.  In the second, the bf16
-// tile y = P0 + P1 is left in LDS (y_stage_index layout).  LDS must be free
-// (the K loop ends with a barrier); the caller copies the tile out.
+// Returns false in all but the last-arriving workgroup.  In the last, the
+// bf16 tile of the part-ordered sum is left in LDS (y_stage_index layout).
+// LDS must be free (the K loop ends with a barrier); the caller copies the
+// tile out.
 __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitCtl &sp, int tid,
                                              int wave, int lane, char *lds) {
     float *mine = sp.part + sp.self * (BM * BN_DN);
@@ -235,40 +238,62 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
         *s_x = old;  // every lane stores the same value
     }
     __syncthreads();
-    const bool last = __builtin_amdgcn_readfirstlane(*s_x) != 0;
+    const bool last = __builtin_amdgcn_readfirstlane(*s_x) == sp.nparts - 1;
     __syncthreads();
     if (!last) return false;
-    // Both partials, read with device-coherent loads: the other one may come
-    // from another XCD, and this XCD's L2 may hold stale lines of the buffer.
+    // All partials, read with device-coherent loads: the others may come from
+    // other XCDs, and this XCD's L2 may hold stale lines of the buffer.
     // Buffer loads with the sc1 cache-policy bit (agent-scope coherence in
-    // gfx950's memory model) miss in that L2.  16 loads per batch in flight.
-    i32x4_t r0 = make_rsrc(sp.part, BM * BN_DN * sizeof(float));
-    i32x4_t r1 = make_rsrc(sp.part + BM * BN_DN, BM * BN_DN * sizeof(float));
+    // gfx950's memory model) miss in that L2.  Up to 16 loads in flight.
+    i32x4_t rs = make_rsrc(sp.part, (uint32_t)(sp.nparts * BM * BN_DN * sizeof(float)));
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        r0[w] = __builtin_amdgcn_readfirstlane(r0[w]);
-        r1[w] = __builtin_amdgcn_readfirstlane(r1[w]);
-    }
+    for (int w = 0; w < 4; ++w) rs[w] = __builtin_amdgcn_readfirstlane(rs[w]);
+    constexpr int PSTRIDE = BM * BN_DN * sizeof(float);  // bytes between partials
     bf16_t *st = reinterpret_cast<bf16_t *>(lds);
-    for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 8) {
-        i32x4_t p0[8], p1[8];
+    auto put = [&](int idx, const float (&v)[4]) {
+        const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) & 3, i = (idx >> 10) & 3,
+                  w = idx >> 12;
+        const int r = (w >> 1) * 128 + i * 32 + 8 * g + 4 * (l >> 5);
+        const int c = (w & 1) * 128 + j * 32 + (l & 31);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = (it + u) * GEMM_THREADS + tid;  // float4 index
-            p0[u] = raw_buffer_load_v4(r0, idx * 16, 0, PA_CPOL_SC1);
-            p1[u] = raw_buffer_load_v4(r1, idx * 16, 0, PA_CPOL_SC1);
+        for (int e = 0; e < 4; ++e) st[y_stage_index(r + e, c)] = f2bf(v[e]);
+    };
+    if (sp.nparts == 2) {
+        for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 8) {
+            i32x4_t p[8][2];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * GEMM_THREADS + tid) * 16 + q * PSTRIDE,
+                                                 0, PA_CPOL_SC1);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = __int_as_float(p[u][0][e]) + __int_as_float(p[u][1][e]);
+                put((it + u) * GEMM_THREADS + tid, v);
+            }
         }
+    } else {
+        for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 4) {
+            i32x4_t p[4][4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int idx = (it + u) * GEMM_THREADS + tid;
-            const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) & 3, i = (idx >> 10) & 3,
-                      w = idx >> 12;
-            const int r = (w >> 1) * 128 + i * 32 + 8 * g + 4 * (l >> 5);
-            const int c = (w & 1) * 128 + j * 32 + (l & 31);
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                st[y_stage_index(r + e, c)] =
-                    f2bf(__int_as_float(p0[u][e]) + __int_as_float(p1[u][e]));
+                for (int q = 0; q < 4; ++q)
+                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * GEMM_THREADS + tid) * 16 + q * PSTRIDE,
+                                                 0, PA_CPOL_SC1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] = ((__int_as_float(p[u][0][e]) + __int_as_float(p[u][1][e])) +
+                            __int_as_float(p[u][2][e])) +
+                           __int_as_float(p[u][3][e]);
+                put((it + u) * GEMM_THREADS + tid, v);
+            }
         }
     }
     (void)acc;
@@ -284,11 +309,11 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
 //   out    PA_SILU_PACKED: packed h at (first row block, first of the 8
 //          k-steps this tile writes), o_kb fragments per h row block;
 //          PA_BF16: y at (row 0, column 0) of the tile, row stride o_ld
-//   sp     PA_BF16 only: this call computes one of two K halves of the tile
-//          (Ap and B0 point at its first k, K is the half's depth); the two
-//          halves meet through sp (see SplitCtl) and the later one writes y.
-// Returns whether this call wrote the tile's output (false only for the
-// earlier half of a split tile).
+//   sp     PA_BF16 only: this call computes one of sp->nparts K parts of the
+//          tile (Ap and B0 point at its first k, K is the part's depth); the
+//          parts meet through sp (see SplitCtl) and the last one writes y.
+// Returns whether this call wrote the tile's output (false only for a part
+// of a cut tile that did not arrive last).
 // LDS: PA_LDS_BYTES at lds, free again when the call returns.
 template <int EPI>
 __device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int64_t a_kb,

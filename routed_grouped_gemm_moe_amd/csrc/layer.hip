@@ -192,16 +192,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
         }
 
     // 2. down tiles; those of the last partial round (of gridDim.x
-    // workgroups) are cut into two K halves, claimed after the whole tiles
+    // workgroups) are cut into S K parts, claimed after the whole tiles
     const int n2 = MT * NT2;
-    const int nsp = dn_split_tiles(D.dn_deep(), n2, (int)gridDim.x);
+    const int S = (int)D.dn_parts();
+    const int nsp = dn_split_tiles(S, n2, (int)gridDim.x);
     if (n2 > 0)
         for (;;) {
-            const int LS = next_tile(a.queues + NUM_XCD * QSTRIDE, n2 + nsp, xcd, &s_claim);
+            const int LS =
+                next_tile(a.queues + NUM_XCD * QSTRIDE, n2 + (S - 1) * nsp, xcd, &s_claim);
             if (LS < 0) break;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             int L, part, st;
-            dn_claim(LS, n2, nsp, &L, &part, &st);
+            dn_claim(LS, n2, nsp, S, &L, &part, &st);
             int mt, nt;
             blocked_tile(L, MT, NT2, &mt, &nt);
             const MTile t = a.mtiles[mt];
@@ -214,15 +216,16 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             else
                 invalidate_l1();
             const int64_t prb = t.prow0 / 32;
-            // a cut tile computes K half `part`, starting at k = part * f / 2
-            const int64_t Kp = part < 0 ? f : f / 2, k0 = part < 0 ? 0 : part * Kp;
+            // a cut tile computes K part `part`, starting at k = part * f / S
+            const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
             const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
-            const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (2 * BM * BN_DN), part};
+            const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
+                              S};
             const bool wrote = gemm_tile_pa<PA_BF16>(
                 a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
                 nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
                 part < 0 ? nullptr : &sc);
-            if (!wrote) {  // the other half writes the tile
+            if (!wrote) {  // the last part to arrive writes the tile
                 trace_tile(a, 4, LS, xcd, t0);
                 continue;
             }

@@ -31,9 +31,9 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     // cut down tiles (deep down GEMMs only): arrival counters, then partials
-    const bool split = ffn && D.dn_deep();
+    const bool split = ffn && D.dn_parts() > 1;
     L.dn_cnt = take(split ? SPLIT_MAX * sizeof(int32_t) : 0);
-    L.dn_part = take(split ? (size_t)SPLIT_MAX * 2 * BM * BN_DN * sizeof(float) : 0);
+    L.dn_part = take(split ? (size_t)SPLIT_MAX * CUT_MAX * BM * BN_DN * sizeof(float) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
@@ -197,7 +197,7 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
     int32_t *pstart = at<int32_t>(ws, L.pstart);
     bf16_t *xp = at<bf16_t>(ws, L.x_perm);
     // cleared per call: the status word and the cut down tiles' counters
-    const int64_t clear_ints = (int64_t)((L.dn_cnt - L.status) / 4) + (D.dn_deep() ? SPLIT_MAX : 0);
+    const int64_t clear_ints = (int64_t)((L.dn_cnt - L.status) / 4) + (D.dn_parts() > 1 ? SPLIT_MAX : 0);
     hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
                                        at<int32_t>(ws, L.status), clear_ints, s);
     if (e == hipSuccess) e = launch_pack_rows(D, (const bf16_t *)x_perm, offsets, pstart, xp, s);
@@ -275,7 +275,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     int32_t *inv_perm = at<int32_t>(ws, L.inv_perm);
     bf16_t *x_perm = at<bf16_t>(ws, L.x_perm);
     const int64_t sched_ints =
-        D.dn_deep() ? (int64_t)((L.dn_cnt - L.status) / 4) + SPLIT_MAX
+        D.dn_parts() > 1 ? (int64_t)((L.dn_cnt - L.status) / 4) + SPLIT_MAX
                     : (int64_t)((L.dn_flag - L.status) / 4) + D.max_mtiles() * D.nt_dn();
 
     mark(0);

@@ -37,45 +37,47 @@ constexpr int COMB_CB = 4;
 constexpr int NUM_XCD = 8;            // MI355X: 8 accelerator complex dies
 constexpr int QSTRIDE = 32;           // ints between queue counters (128 B apart)
 
-// Split down tiles: at most this many per call (their partials are sized
-// for it in the workspace).
+// Cut down tiles: at most this many per call (their partials are sized for
+// it in the workspace), each cut into at most CUT_MAX K parts.
 constexpr int SPLIT_MAX = 256;
+constexpr int CUT_MAX = 4;
 // Of n2 down tiles run by G workgroups, the last n2 % G (the partial last
-// round) are cut into two K halves when the tiles are deep; 0 otherwise.
-__host__ __device__ inline int dn_split_tiles(bool deep, int n2, int G) {
-    if (!deep || G <= 0 || n2 <= G) return 0;
+// round) are cut into K parts when the tiles are deep (parts > 1); 0 otherwise.
+__host__ __device__ inline int dn_split_tiles(int parts, int n2, int G) {
+    if (parts <= 1 || G <= 0 || n2 <= G) return 0;
     const int r = n2 % G;
     return r < SPLIT_MAX ? r : SPLIT_MAX;
 }
-// Down claim index LS -> (tile L in blocked order, part: -1 whole, 0/1 half,
-// st: index of a cut tile among the nsp cut tiles).
-// The n2 + nsp claims form NUM_XCD equal ranges (the per-XCD queues of the
+// Down claim index LS -> (tile L in blocked order, part: -1 whole, else the K
+// part 0..S-1; st: index of a cut tile among the nsp cut tiles).  The
+// n2 + (S-1)*nsp claims form NUM_XCD equal ranges (the per-XCD queues of the
 // persistent kernel, and the per-XCD slices of the standalone launch); range
 // r holds the next run of tiles in blocked order, whole tiles first and then
-// the halves of its share (nsp / NUM_XCD, the first nsp % NUM_XCD ranges one
+// the parts of its share (nsp / NUM_XCD, the first nsp % NUM_XCD ranges one
 // more) of cut tiles, so the cut tiles run last on every XCD.  With n2 > G >
-// nsp every range is long enough for its halves.
-__host__ __device__ inline void dn_claim(int LS, int n2, int nsp, int *L, int *part, int *st) {
-    const int n = n2 + nsp, per = (n + NUM_XCD - 1) / NUM_XCD;
+// nsp every range is long enough for its parts.
+__host__ __device__ inline void dn_claim(int LS, int n2, int nsp, int S, int *L, int *part,
+                                         int *st) {
+    const int n = n2 + (S - 1) * nsp, per = (n + NUM_XCD - 1) / NUM_XCD;
     const int y = LS / per, i = LS - y * per;
     int base = 0, cbase = 0;
     for (int r = 0; r < y; ++r) {
         const int len = min(per, n - r * per);
         const int c = nsp / NUM_XCD + (r < nsp % NUM_XCD ? 1 : 0);
-        base += len - c;  // whole tiles + cut tiles of range r
+        base += len - (S - 1) * c;  // whole tiles + cut tiles of range r
         cbase += c;
     }
     const int len = min(per, n - y * per);
     const int c = nsp / NUM_XCD + (y < nsp % NUM_XCD ? 1 : 0);
-    const int w = len - 2 * c;  // whole tiles of this range
+    const int w = len - S * c;  // whole tiles of this range
     if (i < w) {
         *L = base + i;
         *part = -1;
         *st = -1;
     } else {
-        *L = base + w + (i - w) / 2;
-        *part = (i - w) & 1;
-        *st = cbase + (i - w) / 2;
+        *L = base + w + (i - w) / S;
+        *part = (i - w) % S;
+        *st = cbase + (i - w) / S;
     }
 }
 
@@ -115,9 +117,13 @@ struct Dims {
     __host__ __device__ int64_t pcap() const { return (cap() + EL() * 31 + 31) / 32 * 32; }
     __host__ __device__ int64_t nt_gu() const { return f / BN_GU; }
     __host__ __device__ int64_t nt_dn() const { return d / BN_DN; }
-    // Down tiles deep enough (f >= 8192) to be cut into two K halves; only
-    // the tiles of the schedule's last partial round are cut (dn_split_tiles).
-    __host__ __device__ bool dn_deep() const { return f >= 8192 && f % 256 == 0; }
+    // K parts of a cut down tile: deep down GEMMs (f >= 8192) are cut into 4
+    // (2 when f is not a multiple of 512), each part an even number of
+    // 64-deep stages; only the tiles of the schedule's last partial round are
+    // cut (dn_split_tiles).  1 = never cut.
+    __host__ __device__ int dn_parts() const {
+        return f < 8192 ? 1 : f % 512 == 0 ? 4 : f % 256 == 0 ? 2 : 1;
+    }
     __host__ __device__ int64_t perm_blocks() const { return (T + PERM_TB - 1) / PERM_TB; }
     __host__ __device__ int64_t comb_blocks() const { return (T + COMB_TOK - 1) / COMB_TOK; }
 };
@@ -181,9 +187,9 @@ hipError_t launch_pack_rows(const Dims &D, const bf16_t *x_perm, const int32_t *
 hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
                                const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
                                bf16_t *h, hipStream_t s);
-// Down tiles cut in two (dn_split_tiles with G = grid) meet through dn_cnt
-// (cleared, one int per cut tile) and the float32 partials dn_part (2 x 256
-// KiB per cut tile).
+// Cut down tiles (dn_split_tiles with G = grid) meet through dn_cnt
+// (cleared, one int per cut tile) and the float32 partials dn_part
+// (CUT_MAX x 256 KiB per cut tile).
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
                             const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
                             int32_t *dn_cnt, float *dn_part, int grid, hipStream_t s);
