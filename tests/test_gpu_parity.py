@@ -296,3 +296,29 @@ def test_router_fast_path_on_constructed_ties(pattern):
     ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
     if pattern == "all_equal":
         assert np.array_equal(r_ids[0], np.arange(cfg.k))
+
+
+@pytest.mark.parametrize("f,parts", [(8448, 2), (8192, 4)])
+def test_cut_down_tiles(f, parts):
+    # Deep down GEMMs (f >= 8192) cut the down tiles of the schedule's last
+    # partial round into K parts (2 when f is not a multiple of 512, else 4),
+    # both in moe_layer's persistent kernel and in moe_expert_ffn: more than
+    # 256 down tiles (the MI355X grid) make the last round partial.  Fused
+    # must equal staged bit for bit, and both must match the oracle.
+    cfg = W.CONFIGS["tiny"].scaled(name=f"cut{parts}", T=2400, d=4096, f=f, E=2, k=2, seed=17)
+    say(f"generate cut-tile case f={f}")
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    counts = np.diff(ro)
+    n_down_tiles = int(sum((c + 255) // 256 for c in counts)) * (cfg.d // 256)
+    assert n_down_tiles > 256 and n_down_tiles % 256 > 0, n_down_tiles
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=10, replace=False)]))
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N, rows=rows)
+    staged = _staged(cfg, t, y, inv, gates)
+    toks = sample_tokens(cfg.T, 24, seed=4, must=[0, cfg.T - 1])
+    _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
+    del t, xp, y, staged
+    torch.cuda.empty_cache()
