@@ -91,6 +91,8 @@ def main() -> None:
     ap.add_argument("--mode", default="layer", choices=["layer", "copy"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
+                    help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -117,6 +119,7 @@ def main() -> None:
     wg, wu, wd = dev(arrs["w_gate"]), dev(arrs["w_up"]), dev(arrs["w_down"])
     bias = torch.from_numpy(arrs["bias"]).to("cuda") if arrs["bias"] is not None else None
     D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    M.moe_set_gather_dispatch(args.dispatch == "gather")
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
@@ -175,6 +178,7 @@ def main() -> None:
         "data": "synthetic (seeded Gaussian activations and weights, Gaussian router)",
         "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi],
+                   "dispatch": args.dispatch,
                    "parallelism": "none (one GPU)"},
         "grouped_gemm_tflops": round(ffn_tflops, 2),
         "grouped_gemm_pct_mfma_peak": round(100 * ffn_tflops / PEAK_BF16_TFLOPS, 2),

@@ -185,7 +185,8 @@ int moe_timing_read(float *stage_ms, int n_stages);
  *   int64 buf[1 + 4*n_records], buf[0] = records written (the caller zeroes it;
  *   it can exceed n_records, extra records are dropped), then per record
  *   {kind << 32 | tile index, workgroup << 8 | XCD, start tick, end tick},
- *   kind 1 = gate/up, 2 = down, 3 = combine; ticks of the device's constant
+ *   kind 1 = gate/up, 2 = down, 4 = a K part of a cut down tile, 3 = combine;
+ *   ticks of the device's constant
  *   wall clock, moe_wall_clock_hz() per second.
  * buf is device memory owned by the caller; NULL (or n_records < 1) turns the
  * trace off.  Not thread-safe; for profiling only. */
@@ -198,6 +199,16 @@ int64_t moe_wall_clock_hz(void);
  * return at once, so the launch still drains.  Used by tests to exercise the
  * timeout path. */
 void moe_set_wait_timeout_us(int64_t us);
+
+/* Dispatch mode of moe_layer (process-wide; default off).  Off: the permute
+ * writes x_perm in the packed MFMA-fragment layout and the gate/up tiles load
+ * it straight into registers.  On: gather-on-load dispatch -- x_perm is never
+ * written; each gate/up tile fetches its rows of x through perm_src into LDS
+ * (Weave §4 overlaps dispatch with the first GEMM; on one GPU the dispatch is
+ * this gather).  Both modes give the same bits: the tiles share one k-order.
+ * Inputs of 2 GiB or more (T*d*2 bytes) always use the packed mode.  Not
+ * thread-safe with concurrent moe_layer calls. */
+void moe_set_gather_dispatch(int on);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ __all__ = [
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
     "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "moe_set_trace",
+    "moe_set_gather_dispatch",
     "moe_wall_clock_hz", "MoEError",
     "MOE_BF16", "MOE_F32",
 ]
@@ -85,6 +86,7 @@ def load():
         "moe_timing_enable": ([i32], None),
         "moe_timing_read": ([C.POINTER(C.c_float), i32], i32),
         "moe_set_wait_timeout_us": ([i64], None),
+        "moe_set_gather_dispatch": ([i32], None),
         "moe_set_trace": ([vp, i64], None),
         "moe_wall_clock_hz": ([], i64),
     }
@@ -303,6 +305,11 @@ def moe_timing_read() -> Tuple[int, Tuple[float, float, float]]:
 
 def moe_set_wait_timeout_us(us: int) -> None:
     load().moe_set_wait_timeout_us(int(us))
+
+
+def moe_set_gather_dispatch(on: bool = True) -> None:
+    """moe_layer dispatch mode: gather rows of x on load (True) or packed x_perm (False)."""
+    load().moe_set_gather_dispatch(1 if on else 0)
 
 
 def moe_set_trace(buf=None, n_records: int = 0) -> None:

@@ -93,21 +93,27 @@ __host__ __device__ __forceinline__ void blocked_tile(int L, int MT, int NT, int
     *mt = g * GM_GROUP + (r - *nt * s);
 }
 
-// Epilogues: h = silu(g) * u as bf16 (gate/up, dual B), y as bf16 (down),
-// or the raw float32 accumulators (router logit partials; columns >= out_cols
-// are not stored).
-enum { EPI_SILU_BF16 = 0, EPI_BF16 = 1, EPI_F32 = 2 };
+// Epilogues: h = silu(g) * u as bf16 (gate/up, dual B) in rows or in the
+// packed fragment layout of gemm_pa.h, y as bf16 (down), or the raw float32
+// accumulators (router logit partials; columns >= out_cols are not stored).
+enum { EPI_SILU_BF16 = 0, EPI_BF16 = 1, EPI_F32 = 2, EPI_SILU_PACKED = 3 };
 
-// A: a_rows rows from a_row0, stride lda; B0 (and B1 for the dual-B tile):
-// b_rows valid rows each, stride ldb; K columns of both are used.  The buffer
-// descriptors cover exactly the bytes those rows and columns span.
+// A: a_rows rows from a_row0, stride lda -- or, with a_src != nullptr,
+// gathered rows: row r of the tile is row a_src[r] of A, which then holds
+// a_src_rows rows (the dispatch done on load, x_perm never written); B0 (and
+// B1 for the dual-B tile): b_rows valid rows each, stride ldb; K columns of
+// both are used.  The buffer descriptors cover exactly the bytes those rows
+// and columns span.  EPI_SILU_PACKED: out is the packed h at the tile's first
+// row block and first of its 8 k-steps, ldo its fragments per row block.
 template <int EPI>
 __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t lda, int64_t a_row0,
                                           int a_rows, const bf16_t *__restrict__ B0,
                                           const bf16_t *__restrict__ B1, int64_t ldb, int b_rows,
                                           int K, void *__restrict__ out, int64_t ldo,
-                                          int64_t out_col0, int out_cols, char *lds) {
-    constexpr bool GATE_UP = EPI == EPI_SILU_BF16;
+                                          int64_t out_col0, int out_cols, char *lds,
+                                          const int32_t *__restrict__ a_src = nullptr,
+                                          int64_t a_src_rows = 0) {
+    constexpr bool GATE_UP = EPI == EPI_SILU_BF16 || EPI == EPI_SILU_PACKED;
     // An opaque copy of the thread index: inside a persistent tile loop this
     // keeps the compiler from hoisting every lane-dependent address out of the
     // loop (which would hold them live across the accumulators and spill).
@@ -126,12 +132,14 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
     for (int i = 0; i < 4; ++i) {
         const int r = (wave * 4 + i) * 16 + (lane >> 2);
         const int c = pc ^ swz(r);
-        voffA[i] = min(r, a_rows - 1) * (int)lda * 2 + c * 16;
+        const int ar = min(r, a_rows - 1);
+        voffA[i] = (a_src ? a_src[ar] : ar) * (int)lda * 2 + c * 16;
         const int br = GATE_UP ? (r & 127) : r;
         voffB[i] = min(br, b_rows - 1) * (int)ldb * 2 + c * 16;
     }
     const i32x4_t rsA =
-        make_rsrc(A + a_row0 * lda, (uint32_t)(((int64_t)(a_rows - 1) * lda + K) * 2));
+        a_src ? make_rsrc(A, (uint32_t)(((a_src_rows - 1) * lda + K) * 2))
+              : make_rsrc(A + a_row0 * lda, (uint32_t)(((int64_t)(a_rows - 1) * lda + K) * 2));
     const bf16_t *Bw = (GATE_UP && wave >= 2) ? B1 : B0;  // waves 2,3 stage the up rows
     const i32x4_t rsB = make_rsrc(Bw, (uint32_t)(((int64_t)(b_rows - 1) * ldb + K) * 2));
     const int ldsA_w = wave * 4 * 1024;
@@ -232,6 +240,36 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
 
     // Epilogue.  Accumulator v of lane l in a 32x32 tile sits at
     // row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+    if (EPI == EPI_SILU_PACKED) {
+        // h tile (256 rows x 128 columns) staged in LDS as 8 row blocks x 8
+        // packed fragments, then copied out as 8 KiB contiguous runs; blocks
+        // past the tile's last valid row belong to the next segment.
+        __syncthreads();  // every wave is done reading the ring
+        bf16_t *st = reinterpret_cast<bf16_t *>(lds);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = wn * 64 + j * 32 + l32;
+                const int fo = ((col >> 4) * 64 + 32 * ((col >> 3) & 1)) * 8 + (col & 7);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r32 = 8 * (v >> 2) + 4 * khalf + (v & 3);
+                    const float g = acc[i][j][v];
+                    const float u = acc[i][j + 2][v];
+                    st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g / (1.0f + __expf(-g)) * u);
+                }
+            }
+        __syncthreads();
+        const int nb_all = (a_rows + 31) >> 5;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
+        bf16_t *o = reinterpret_cast<bf16_t *>(out);
+        for (int g = tid; g < nb_all * 512; g += GEMM_THREADS) {
+            const int rb = g >> 9;
+            reinterpret_cast<u32x4_t *>(o + rb * ldo * 512)[g & 511] = src[g];
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll

@@ -183,10 +183,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             const MTile t = a.mtiles[mt];
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
             const int64_t prb = t.prow0 / 32;  // first packed row block
-            gemm_tile_pa<PA_SILU_PACKED>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows, (int)d,
-                                         a.w_gate + wo, a.w_up + wo, d,
-                                         a.h + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16,
-                                         lds);
+            bf16_t *ho = a.h + (prb * (f / 16) + nt * (BN_GU / 16)) * 512;
+            if (a.gather)  // rows of x fetched through perm_src, both operands via LDS
+                gemm_tile<EPI_SILU_PACKED>(a.x, d, 0, t.rows, a.w_gate + wo, a.w_up + wo, d, BN_GU,
+                                           (int)d, ho, f / 16, 0, 0, lds, a.perm_src + t.row0,
+                                           D.T);
+            else
+                gemm_tile_pa<PA_SILU_PACKED>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
+                                             (int)d, a.w_gate + wo, a.w_up + wo, d, ho, f / 16,
+                                             lds);
             publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
             trace_tile(a, 1, L, xcd, t0);
         }

@@ -68,6 +68,7 @@ int64_t g_wait_us = 2000000;  // device flag-wait timeout
 int64_t *g_trace = nullptr;   // per-tile trace buffer of moe_layer (device), or null
 int64_t g_trace_cap = 0;
 bool g_timing = false;
+bool g_gather = false;  // gather-on-load dispatch in moe_layer
 struct CallEvents {
     hipEvent_t ev[4];
 };
@@ -250,13 +251,15 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     if (grid <= 0) return MOE_ERR_HIP;
     int64_t wait_us;
     CallEvents ce{};
-    bool timing;
+    bool timing, gather;
     int64_t *trace;
     int64_t trace_cap;
     {
         std::lock_guard<std::mutex> lk(g_mu);
         wait_us = g_wait_us;
         timing = g_timing;
+        // 32-bit buffer offsets address x in gather mode
+        gather = g_gather && D.T * D.d * 2 < ((int64_t)1 << 31);
         trace = g_trace;
         trace_cap = g_trace_cap;
         if (timing)
@@ -284,7 +287,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     mark(1);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
-                           at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
+                           at<int32_t>(ws, L.perm_src), inv_perm, gather ? nullptr : x_perm,
                            at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
                            at<int32_t>(ws, L.pstart), mt, nmt, mtile_base,
                            at<int32_t>(ws, L.status), sched_ints, s);
@@ -293,6 +296,9 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         LayerArgs a;
         a.D = D;
         a.x_perm = x_perm;
+        a.gather = gather ? 1 : 0;
+        a.x = (const bf16_t *)x;
+        a.perm_src = at<int32_t>(ws, L.perm_src);
         a.w_gate = (const bf16_t *)w_gate;
         a.w_up = (const bf16_t *)w_up;
         a.w_down = (const bf16_t *)w_down;
@@ -385,6 +391,11 @@ void moe_set_trace(void *buf, int64_t n_records) {
 }
 
 int64_t moe_wall_clock_hz(void) { return wall_clock_hz(); }
+
+void moe_set_gather_dispatch(int on) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_gather = on != 0;
+}
 
 void moe_set_wait_timeout_us(int64_t us) {
     std::lock_guard<std::mutex> lk(g_mu);

@@ -165,8 +165,9 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
 
 // Permute.  With pstart != NULL (the fused layer) x_perm is written in the
 // packed fragment layout of gemm_pa.h at the 32-aligned segment starts
-// pstart[], and the GEMM m-tile table is built and the scheduler state of the
-// persistent kernel cleared; otherwise x_perm is row-major at offsets[].
+// pstart[] (not at all when x_perm is NULL: gather-on-load dispatch), and the
+// GEMM m-tile table is built and the scheduler state of the persistent kernel
+// cleared; otherwise x_perm is row-major at offsets[].
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
                           int32_t *blk_counts, int32_t *blk_base, int32_t *pstart,
@@ -200,6 +201,11 @@ hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *in
 struct LayerArgs {
     Dims D;
     const bf16_t *x_perm, *w_gate, *w_up, *w_down;
+    // gather-on-load dispatch: gate/up tiles read their rows of x through
+    // perm_src (x_perm is not written); 0 = packed x_perm from the permute
+    int gather;
+    const bf16_t *x;
+    const int32_t *perm_src;
     bf16_t *h, *y;
     const int32_t *ids, *inv_perm, *offsets, *mtile_base, *n_mtiles;
     const float *gates;

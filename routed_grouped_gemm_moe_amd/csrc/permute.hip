@@ -252,7 +252,7 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
                            offsets, blk_base, perm_src, inv_perm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (pstart) {
-            e = launch_pack(D, x, perm_src, offsets, pstart, x_perm, s);
+            if (x_perm) e = launch_pack(D, x, perm_src, offsets, pstart, x_perm, s);
         } else {
             const unsigned g = (unsigned)((D.T + GATHER_TOK - 1) / GATHER_TOK);
             hipLaunchKernelGGL(gather_kernel, dim3(g), dim3(GATHER_THREADS), 0, s, D.T, D.d, D.k, x,

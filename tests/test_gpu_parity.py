@@ -322,3 +322,41 @@ def test_cut_down_tiles(f, parts):
     _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
     del t, xp, y, staged
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_T300", "local_subset_e16k4", "e128k8", "mixtral"])
+def test_gather_on_load_dispatch(name):
+    # Gather-on-load dispatch: gate/up tiles fetch their rows of x through
+    # perm_src (x_perm never written).  Same tile k-order as the packed path,
+    # so the layer output must equal the packed-dispatch output bit for bit,
+    # and match the oracle.
+    cfg = SMALL[name] if name in SMALL else W.CONFIGS[name]
+    D = _dims(cfg)
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    say(f"moe_layer packed dispatch {cfg.name}")
+    packed = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
+                         out_dtype=dt)
+    torch.cuda.synchronize()
+    try:
+        M.moe_set_gather_dispatch(True)
+        say(f"moe_layer gather dispatch {cfg.name}")
+        ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)  # a packed x_perm left from elsewhere must not be read
+        out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
+                          t["bias"], out_dtype=dt, ws=ws)
+        torch.cuda.synchronize()
+        assert M.moe_device_status(D, ws) == 0
+    finally:
+        M.moe_set_gather_dispatch(False)
+    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
+    assert torch.equal(out.view(bits), packed.view(bits)), "gather != packed dispatch"
+    toks = sample_tokens(cfg.T, 32, seed=5)
+    ref, _, _ = oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"], arrs["w_up"],
+                                    arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi, bias=arrs["bias"])
+    err = rel_err(host_f32(out[torch.as_tensor(toks, device="cuda")]), ref)
+    say(f"  gather dispatch rel err {err:.3e}")
+    assert err <= TOL_LAYER
+    del t
+    torch.cuda.empty_cache()
