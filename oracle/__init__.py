@@ -20,6 +20,18 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
   expert_rows     pinned: E=1 equals a dense SwiGLU written with numpy float64
                   matmuls; a hand-worked 2x2 case.
   combine         pinned: hand-worked small case; linearity in the gates.
+  e4m3_value      pinned: values the OCP 8-bit float definition fixes (1, 2,
+                  448, 2^-6, 2^-9, NaN pattern, signed zero), monotone order.
+  e4m3_encode     pinned: every finite value round-trips; midpoints go to the
+                  even code; a closed-form rounding (numpy half-to-even on the
+                  value's own quantum) agrees on a dense sweep; saturation.
+  quantize_rows_e4m3  pinned: the scale is the smallest admissible power of
+                  two; exact when the row is already E4M3 times 2^e; error
+                  within half a code step.
+  expert_rows_fp8 pinned: with inputs exact in E4M3 it equals the float64
+                  dense SwiGLU of the decoded operands (numpy matmuls) up to
+                  the bf16/E4M3 rounding of h; per-row and per-channel scales
+                  land on their own axes (non-uniform scales).
   layer_tokens    pinned: k=1 one-hot reduces to one expert's FFN; identical
                   experts reduce to the dense FFN (gates sum to 1); sum of
                   expert-parallel shard partials equals the unsharded layer.
@@ -67,6 +79,15 @@ def _load():
         lib.oracle_combine.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         lib.oracle_layer_tokens.argtypes = [i64, vp, i64, i64, i64, i64, i64, i64, i64, vp, vp,
                                             vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_e4m3_value.argtypes = [C.c_int32]
+        lib.oracle_e4m3_value.restype = C.c_double
+        lib.oracle_e4m3_encode.argtypes = [C.c_float]
+        lib.oracle_e4m3_encode.restype = C.c_int32
+        lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, vp, vp, vp]
+        lib.oracle_quantize_rows_e4m3.restype = C.c_int
+        lib.oracle_expert_rows_fp8.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                               vp, vp]
+        lib.oracle_expert_rows_fp8.restype = C.c_int
         lib.oracle_num_threads.restype = C.c_int
         for name in ("oracle_router_logits", "oracle_router_logits_f64", "oracle_topk_gates",
                      "oracle_route", "oracle_permute", "oracle_expert_rows", "oracle_combine",
@@ -216,3 +237,45 @@ def layer_full(x, w_router, w_gate, w_up, w_down, k: int, e_lo: int = 0,
     out = combine(y, inv, g)
     return dict(ids=ids, gates=g, counts=counts, offsets=offsets, perm_src=perm, inv_perm=inv,
                 y_perm=y, out=out)
+
+
+# ------------------------------------------------------------ W8A8 (fp8)
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 code (0..255)."""
+    return float(_load().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest E4M3 code of a float32 value (ties to even, saturating)."""
+    return int(_load().oracle_e4m3_encode(float(np.float32(v))))
+
+
+def quantize_rows_e4m3(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row power-of-two scaled E4M3 codes of a bf16 matrix [rows, cols]:
+    (codes uint8 [rows, cols], scales float32 [rows])."""
+    x = _u16(x)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty(rows, dtype=np.float32)
+    _check(_load().oracle_quantize_rows_e4m3(rows, cols, _p(x), _p(q), _p(s)), "quantize_rows_e4m3")
+    return q, s
+
+
+def expert_rows_fp8(x_rows, expert_of_row, wq_gate, s_gate, wq_up, s_up, wq_down, s_down,
+                    want_h: bool = False):
+    """W8A8 SwiGLU FFN of rows (float64 y; h as its bf16-rounded values)."""
+    x_rows = _u16(x_rows)
+    e = np.ascontiguousarray(expert_of_row, dtype=np.int32)
+    u8 = lambda a: np.ascontiguousarray(a, dtype=np.uint8)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    wg, wu, wd = u8(wq_gate), u8(wq_up), u8(wq_down)
+    sg, su, sd = f32(s_gate), f32(s_up), f32(s_down)
+    n, d = x_rows.shape
+    EL, f, _ = wg.shape
+    y = np.empty((n, d), dtype=np.float64)
+    h = np.empty((n, f), dtype=np.float64) if want_h else None
+    _check(_load().oracle_expert_rows_fp8(n, d, f, EL, _p(x_rows), _p(e), _p(wg), _p(sg), _p(wu),
+                                          _p(su), _p(wd), _p(sd), _p(y), _p(h)),
+           "expert_rows_fp8")
+    return (y, h) if want_h else y

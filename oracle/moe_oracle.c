@@ -327,3 +327,153 @@ int oracle_layer_tokens(int64_t n, const int64_t *tokens, int64_t T, int64_t d, 
     }
     return rc;
 }
+
+/* ------------------------------------------------ W8A8 (fp8) expert FFN */
+/*
+ * The W8A8 variant of the expert FFN that X-Stage ("Modeling Post-Issue
+ * Backpressure in GPU Communication-Computation Fusion", §5.3) evaluates for
+ * MegaMoE.  The pages name the precision only, so the recipe is a reading:
+ *  - element format: OCP 8-bit floating point E4M3 ("fn": no infinities, one
+ *    NaN pattern per sign, largest finite magnitude 448); a code is
+ *    sign(1) | exponent(4, bias 7) | mantissa(3), exponent field 0 holding
+ *    the subnormals M/8 * 2^-6;
+ *  - one scale per row of each operand: per token for activations, per
+ *    output channel for weights.  The scale of a row is the smallest power of
+ *    two 2^e with max|row| <= 448 * 2^e (e clamped to >= -126; 1 for an
+ *    all-zero row).  Dividing by a power of two is exact, so the code of an
+ *    element is the only rounding: the E4M3 value nearest to x / 2^e, ties to
+ *    the even code, magnitudes above 448 saturating to 448;
+ *  - GEMM0: g = sx * sg[c] * sum_i dec(xq_i) dec(wgq[c,i]) (likewise u), all
+ *    in double; h = silu(g) * u, rounded to bf16 (h is materialised in bf16
+ *    between the two GEMMs, as in the bf16 path), then quantised per row like
+ *    the activations;
+ *  - GEMM1: y[o] = sh * sd[o] * sum_n dec(hq_n) dec(wdq[o,n]), in double.
+ */
+
+/* Value of an E4M3 code, from the format's definition (NaN for 0x7F/0xFF). */
+double oracle_e4m3_value(int32_t code) {
+    const int s = (code >> 7) & 1, E = (code >> 3) & 15, M = code & 7;
+    if (E == 15 && M == 7) return NAN;
+    const double mag = E == 0 ? ldexp((double)M / 8.0, -6) : ldexp(1.0 + (double)M / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/* Code of the E4M3 value nearest to v (v finite): a search over the 127
+ * finite magnitudes, ties to the even code, saturating at 448.  The sign bit
+ * is the sign bit of v. */
+static uint8_t e4m3_encode(float v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);  /* saturation */
+    int best = 0;
+    double bd = a;  /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        const double dist = fabs(oracle_e4m3_value(c) - a);
+        if (dist < bd || (dist == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            bd = dist;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Exported for the tests. */
+int32_t oracle_e4m3_encode(float v) { return e4m3_encode(v); }
+
+/* Exponent e of the row scale 2^e for a row whose largest magnitude is amax. */
+static int row_scale_exp(double amax) {
+    if (amax == 0.0) return 0;
+    int e = -126;
+    while (amax > ldexp(448.0, e)) ++e;
+    return e;
+}
+
+/* Quantise one row of n float values (already exact floats). */
+static void quant_row(int64_t n, const float *x, uint8_t *q, float *scale) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) amax = fmax(amax, fabs((double)x[i]));
+    const int e = row_scale_exp(amax);
+    *scale = (float)ldexp(1.0, e);
+    for (int64_t i = 0; i < n; ++i) q[i] = e4m3_encode((float)ldexp((double)x[i], -e));
+}
+
+/* rows x cols bf16 -> codes [rows, cols] and one float scale per row. */
+int oracle_quantize_rows_e4m3(int64_t rows, int64_t cols, const uint16_t *x, uint8_t *q,
+                              float *scale) {
+    if (rows < 0 || cols <= 0 || !x || !q || !scale) return ORACLE_EINVAL;
+    int rc = ORACLE_OK;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)cols);
+        if (!row) { rc = ORACLE_EINVAL; continue; }
+        for (int64_t i = 0; i < cols; ++i) row[i] = bf(x[r * cols + i]);
+        quant_row(cols, row, q + r * cols, scale + r);
+        free(row);
+    }
+    return rc;
+}
+
+/* Nearest bf16 value to a double (ties to even), as a float. */
+static float bf16_round(double v) {
+    if (v == 0.0 || !isfinite(v)) return (float)v;
+    int p;
+    (void)frexp(v, &p);                 /* |v| in [2^(p-1), 2^p) */
+    int q = p - 8;                      /* quantum of an 8-significant-bit value */
+    if (q < -133) q = -133;             /* bf16 subnormal quantum */
+    return (float)ldexp(nearbyint(ldexp(v, -q)), q);
+}
+
+/* W8A8 FFN of n rows; row r goes through local expert expert_of_row[r].
+ * x_rows [n,d] bf16; wq_gate, wq_up [E_loc,f,d] and wq_down [E_loc,d,f] E4M3
+ * codes with scales s_gate, s_up [E_loc,f] and s_down [E_loc,d]; y [n,d]
+ * double; h_out [n,f] (optional) receives the bf16-rounded h. */
+int oracle_expert_rows_fp8(int64_t n, int64_t d, int64_t f, int64_t E_loc,
+                           const uint16_t *x_rows, const int32_t *expert_of_row,
+                           const uint8_t *wq_gate, const float *s_gate, const uint8_t *wq_up,
+                           const float *s_up, const uint8_t *wq_down, const float *s_down,
+                           double *y, double *h_out) {
+    if (n < 0 || d <= 0 || f <= 0 || E_loc <= 0 || !x_rows || !expert_of_row || !wq_gate ||
+        !s_gate || !wq_up || !s_up || !wq_down || !s_down || !y)
+        return ORACLE_EINVAL;
+    for (int64_t r = 0; r < n; ++r)
+        if (expert_of_row[r] < 0 || expert_of_row[r] >= E_loc) return ORACLE_EINVAL;
+    double lut[256];
+    for (int c = 0; c < 256; ++c) lut[c] = oracle_e4m3_value(c);
+    int rc = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t e = expert_of_row[r];
+        float *xr = (float *)malloc(sizeof(float) * (size_t)d);
+        float *hb = (float *)malloc(sizeof(float) * (size_t)f);
+        uint8_t *xq = (uint8_t *)malloc((size_t)d);
+        uint8_t *hq = (uint8_t *)malloc((size_t)f);
+        if (!xr || !hb || !xq || !hq) {
+            rc = ORACLE_EINVAL;
+        } else {
+            float sx, sh;
+            for (int64_t i = 0; i < d; ++i) xr[i] = bf(x_rows[r * d + i]);
+            quant_row(d, xr, xq, &sx);
+            for (int64_t c = 0; c < f; ++c) {
+                const uint8_t *rg = wq_gate + (e * f + c) * d, *ru = wq_up + (e * f + c) * d;
+                double g = 0.0, u = 0.0;
+                for (int64_t i = 0; i < d; ++i) {
+                    g += lut[xq[i]] * lut[rg[i]];
+                    u += lut[xq[i]] * lut[ru[i]];
+                }
+                g *= (double)sx * (double)s_gate[e * f + c];
+                u *= (double)sx * (double)s_up[e * f + c];
+                hb[c] = bf16_round(g / (1.0 + exp(-g)) * u);
+                if (h_out) h_out[r * f + c] = hb[c];
+            }
+            quant_row(f, hb, hq, &sh);
+            for (int64_t o = 0; o < d; ++o) {
+                const uint8_t *rd = wq_down + (e * d + o) * f;
+                double s = 0.0;
+                for (int64_t c = 0; c < f; ++c) s += lut[hq[c]] * lut[rd[c]];
+                y[r * d + o] = s * (double)sh * (double)s_down[e * d + o];
+            }
+        }
+        free(xr); free(hb); free(xq); free(hq);
+    }
+    return rc;
+}
