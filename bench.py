@@ -11,6 +11,11 @@ entry and the CPU oracle timed on a bounded sample of the same workload.
 
 --mode copy runs a plain device-to-device copy of known size (used to scale
 the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
+
+--mode ffn_fp8 / ffn_bf16 time the staged expert FFN alone (moe_expert_ffn_fp8
+on E4M3 weights quantised once beforehand, or moe_expert_ffn in bf16) on the
+same workload's routed rows, and print one JSON line in TFLOP/s of 6*d*f per
+routed row against the MFMA peak of that precision.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_kernel_mixtral_traffic.txt")
 
@@ -82,13 +88,52 @@ def cpu_baseline(cfg, arrs, n_tokens: int):
                       f"({dt:.1f} s)"}
 
 
+def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
+    """Time the staged expert FFN (fp8 or bf16) on the workload's routed rows."""
+    ids, _, _ = M.moe_route(D, x, wr, bias)
+    _, offsets, _, _, xp = M.moe_permute(D, x, ids)
+    n_rows = int(offsets[-1].item())
+    flops = 6.0 * cfg.d * cfg.f * n_rows
+    y = torch.empty((max(cfg.T * cfg.k, 1), cfg.d), dtype=torch.bfloat16, device="cuda")
+    fp8 = args.mode == "ffn_fp8"
+    if fp8:
+        (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
+        ws = torch.empty(M.moe_expert_ffn_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        step = lambda: M.moe_expert_ffn_fp8(D, xp, offsets, gq, gs, uq, us, dq, ds, y_perm=y, ws=ws)
+    else:
+        ws = torch.empty(M.moe_expert_ffn_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        step = lambda: M.moe_expert_ffn(D, xp, offsets, wg, wu, wd, y_perm=y, ws=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+    print(json.dumps({
+        "mode": args.mode,
+        "metric": "staged expert-FFN TFLOP/s (" + ("W8A8 E4M3" if fp8 else "bf16") + "), 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 4),
+        "steps": args.steps, "warmup": args.warmup, "peak": peak, "frac": round(tflops / peak, 4),
+        "dtype": "fp8_e4m3" if fp8 else "bf16", "routed_rows": n_rows,
+        "flops_per_call": flops,
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi]},
+    }), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--mode", default="layer", choices=["layer", "copy"])
+    ap.add_argument("--mode", default="layer", choices=["layer", "copy", "ffn_fp8", "ffn_bf16"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
@@ -119,6 +164,9 @@ def main() -> None:
     wg, wu, wd = dev(arrs["w_gate"]), dev(arrs["w_up"]), dev(arrs["w_down"])
     bias = torch.from_numpy(arrs["bias"]).to("cuda") if arrs["bias"] is not None else None
     D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    if args.mode in ("ffn_fp8", "ffn_bf16"):
+        ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
+        return
     M.moe_set_gather_dispatch(args.dispatch == "gather")
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16

@@ -138,6 +138,41 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
                           const void *w_gate, const void *w_up, const void *w_down, void *y_perm,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* ---- W8A8 expert FFN (X-Stage, §5.3, evaluates MegaMoE in W8A8; the
+ * pages give no recipe, so this one is a stated choice).  Element format:
+ * OCP 8-bit float E4M3 (bias 7, 3 mantissa bits, no infinities, largest
+ * finite 448).  Each row of an operand -- a token's activations, a weight
+ * matrix's output channel -- has one scale, the smallest power of two 2^e
+ * (e >= -126) with max|row| <= 448 * 2^e (1 for an all-zero row); an element's
+ * code is the E4M3 value nearest to x / 2^e, ties to the even code,
+ * saturating at 448.  Dequantisation multiplies by the scales, exactly.
+ *
+ * moe_quantize_fp8: x bf16 [rows, cols] (device, row-major, 16-byte aligned,
+ *   cols a multiple of 16) -> q uint8 [rows, cols] codes (16-byte aligned)
+ *   and scale f32 [rows].  Used for weights ([E_loc, out, K] as E_loc*out
+ *   rows of K) and activations.  Caller-owned device buffers; no workspace.
+ *   MOE_ERR_INVALID_ARG on bad sizes, null or misaligned pointers. */
+moe_status moe_quantize_fp8(const void *x, int64_t rows, int64_t cols, void *q, float *scale,
+                            void *stream);
+
+/* moe_expert_ffn_fp8: the grouped SwiGLU FFN of moe_expert_ffn on E4M3
+ * operands with float32 accumulation on the fp8 matrix cores.
+ *   x_perm   bf16 [T*k, d] rows, expert-contiguous (quantised per row inside)
+ *   offsets  i32 [E_loc+1]  device-resident segment offsets
+ *   wq_gate, wq_up uint8 [E_loc, f, d], s_gate, s_up f32 [E_loc, f]
+ *   wq_down  uint8 [E_loc, d, f], s_down f32 [E_loc, d]   (moe_quantize_fp8)
+ *   y_perm   bf16 [T*k, d] out
+ * g = sx * sg * (xq . wgq), u likewise, h = silu(g) * u rounded to bf16 and
+ * re-quantised per row, y = sh * sd * (hq . wdq) rounded to bf16.  Requires
+ * f % 256 == 0 (else MOE_ERR_UNSUPPORTED).  Kernels: per-row quantisation
+ * into the packed fragment layout, the gate/up GEMM, quantisation of h, the
+ * down GEMM; no device-side waits and no status word. */
+size_t moe_expert_ffn_fp8_workspace_bytes(const moe_dims *dims);
+moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                              const void *wq_gate, const float *s_gate, const void *wq_up,
+                              const float *s_up, const void *wq_down, const float *s_down,
+                              void *y_perm, void *ws, size_t ws_bytes, void *stream);
+
 /* ---- moe_combine: gate-weighted sum back to token order (Weave §2.1 stage 5).
  *   y_perm   bf16 [T*k, d]  expert outputs by row
  *   inv_perm i32  [T, k]    row of each (token, slot), -1 = skip

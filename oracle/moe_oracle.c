@@ -358,22 +358,22 @@ double oracle_e4m3_value(int32_t code) {
     return s ? -mag : mag;
 }
 
-/* Code of the E4M3 value nearest to v (v finite): a search over the 127
- * finite magnitudes, ties to the even code, saturating at 448.  The sign bit
- * is the sign bit of v. */
+/* Code of the E4M3 value nearest to v (v finite), ties to the even code,
+ * saturating at 448.  Finite non-negative codes 0..0x7E are in increasing
+ * order of value, so a binary search finds the neighbours of |v|.  The sign
+ * bit is the sign bit of v. */
 static uint8_t e4m3_encode(float v) {
     const uint8_t sign = signbit(v) ? 0x80 : 0x00;
     const double a = fabs((double)v);
     if (a >= 448.0) return (uint8_t)(sign | 0x7E);  /* saturation */
-    int best = 0;
-    double bd = a;  /* distance to code 0 (value 0) */
-    for (int c = 1; c <= 0x7E; ++c) {
-        const double dist = fabs(oracle_e4m3_value(c) - a);
-        if (dist < bd || (dist == bd && (c & 1) == 0 && (best & 1) == 1)) {
-            best = c;
-            bd = dist;
-        }
+    int lo = 0, hi = 0x7E;  /* value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (oracle_e4m3_value(mid) <= a) lo = mid;
+        else hi = mid;
     }
+    const double dl = a - oracle_e4m3_value(lo), dh = oracle_e4m3_value(hi) - a;
+    const int best = dl < dh ? lo : dh < dl ? hi : ((lo & 1) == 0 ? lo : hi);
     return (uint8_t)(sign | best);
 }
 

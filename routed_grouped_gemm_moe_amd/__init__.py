@@ -79,6 +79,9 @@ def load():
         "moe_permute": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_expert_ffn_workspace_bytes": ([dp], sz),
         "moe_expert_ffn": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_quantize_fp8": ([vp, i64, i64, vp, vp, vp], i32),
+        "moe_expert_ffn_fp8_workspace_bytes": ([dp], sz),
+        "moe_expert_ffn_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_combine": ([dp, vp, vp, vp, vp, i32, vp], i32),
         "moe_layer_workspace_bytes": ([dp], sz),
         "moe_layer": ([dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
@@ -243,6 +246,53 @@ def moe_expert_ffn(dims, x_perm, offsets, w_gate, w_up, w_down, y_perm=None, ws=
                                _ptr(w_down), _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream))
     _check(rc, "moe_expert_ffn")
+    return y_perm
+
+
+def moe_quantize_fp8(x, q=None, scale=None, stream=None):
+    """Per-row E4M3 codes of a bf16 matrix [..., K] with power-of-two row
+    scales.  Returns (q uint8 [..., K], scale f32 [...])."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous bf16 tensor")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if scale is None else scale
+    _check(load().moe_quantize_fp8(_ptr(x), rows, cols, _ptr(q), _ptr(scale), _stream(stream)),
+           "moe_quantize_fp8")
+    return q, scale
+
+
+def moe_expert_ffn_fp8_workspace_bytes(dims) -> int:
+    return int(load().moe_expert_ffn_fp8_workspace_bytes(C.byref(_dims(dims))))
+
+
+def moe_expert_ffn_fp8(dims, x_perm, offsets, wq_gate, s_gate, wq_up, s_up, wq_down, s_down,
+                       y_perm=None, ws=None, stream=None):
+    """W8A8 grouped SwiGLU FFN over expert-contiguous bf16 rows (E4M3 weights
+    from moe_quantize_fp8).  Returns y_perm bf16 [T*k, d]."""
+    import torch
+    D = _dims(dims)
+    dev = x_perm.device
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(wq_gate, torch.uint8, (EL, D.f, D.d), "wq_gate")
+    _require(wq_up, torch.uint8, (EL, D.f, D.d), "wq_up")
+    _require(wq_down, torch.uint8, (EL, D.d, D.f), "wq_down")
+    _require(s_gate, torch.float32, (EL, D.f), "s_gate")
+    _require(s_up, torch.float32, (EL, D.f), "s_up")
+    _require(s_down, torch.float32, (EL, D.d), "s_down")
+    _require(offsets, torch.int32, (EL + 1,), "offsets")
+    if x_perm.dtype != torch.bfloat16 or x_perm.shape[0] < cap or x_perm.shape[1] != D.d:
+        raise ValueError("x_perm must be bf16 with at least T*k rows of d")
+    y_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if y_perm is None else y_perm
+    need = moe_expert_ffn_fp8_workspace_bytes(D)
+    ws = _workspace(need, dev) if ws is None else ws
+    rc = load().moe_expert_ffn_fp8(C.byref(D), _ptr(x_perm), _ptr(offsets), _ptr(wq_gate),
+                                   _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(wq_down),
+                                   _ptr(s_down), _ptr(y_perm), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_expert_ffn_fp8")
     return y_perm
 
 

@@ -1,0 +1,237 @@
+// W8A8 path (X-Stage, §5.3, evaluates MegaMoE in W8A8): per-row E4M3
+// quantisation and the grouped E4M3 expert GEMMs of the staged fp8 FFN.
+//
+// Quantisation of a row: its scale is the smallest power of two 2^e with
+// max|x| <= 448 * 2^e (e >= -126; 1 for an all-zero row), and each element's
+// code is the E4M3 value nearest to x * 2^-e (exact: a power-of-two scaling),
+// ties to the even code, saturating at 448.  E4M3 here is the OCP 8-bit float
+// with 4 exponent bits (bias 7) and 3 mantissa bits, no infinities.
+#include <algorithm>
+
+#include "gemm_f8.h"
+
+namespace moe {
+namespace {
+
+// E4M3 code of a finite float (bit arithmetic on the float32 encoding).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448: saturate
+    if (a < 0x3C800000u) {                       // |v| < 2^-6: multiples of 2^-9
+        const float t = __uint_as_float(a) * 512.0f;  // exact
+        return sign | (uint32_t)__builtin_rintf(t);   // 0..8 (8 is the smallest normal)
+    }
+    // normal: biased E4M3 exponent (a >> 23) - 120, top 3 mantissa bits, the
+    // 20 bits below rounded to nearest even (a carry moves into the exponent)
+    const uint32_t m = a & 0x7FFFFFu;
+    uint32_t code = (((a >> 23) - 120u) << 3) | (m >> 20);
+    const uint32_t rem = m & 0xFFFFFu;
+    code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+    return sign | code;
+}
+
+// Exponent of the row scale for a row whose largest magnitude is amax.
+__device__ __forceinline__ int row_scale_exp(float amax) {
+    if (amax == 0.0f) return 0;
+    const uint32_t b = __float_as_uint(amax);
+    const int E = (int)(b >> 23) - 127;  // amax = 1.m * 2^E (subnormal amax: clamped below)
+    // 448 * 2^e = 1.75 * 2^(e+8) >= 1.m * 2^E  <=>  e >= E - 8, or E - 7 if 1.m > 1.75
+    const int e = (b & 0x7FFFFFu) > 0x600000u ? E - 7 : E - 8;
+    return e < -126 ? -126 : e;
+}
+
+__device__ __forceinline__ float amax8(const u32x4_t &v, float m) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(bf16x8_elem(v, q)));
+    return m;
+}
+
+// 8 bf16 values times 2^-e -> 8 codes (two 32-bit words).
+__device__ __forceinline__ uint2 encode8(const u32x4_t &v, float inv) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q >> 2] |= e4m3_code(bf16x8_elem(v, q) * inv) << (8 * (q & 3));
+    return make_uint2(w[0], w[1]);
+}
+
+// Row-major quantisation: one wave per row, 4 rows per workgroup.
+__global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int64_t cols,
+                                                         const bf16_t *__restrict__ x,
+                                                         uint8_t *__restrict__ q,
+                                                         float *__restrict__ scale) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= rows) return;
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + r * cols);
+    const int64_t nc = cols / 8;
+    float m = 0.0f;
+    for (int64_t c = lane; c < nc; c += 64) m = amax8(src[c], m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const int e = row_scale_exp(m);
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-126, 127]
+    if (lane == 0) scale[r] = __uint_as_float((uint32_t)(127 + e) << 23);
+    uint2 *dst = reinterpret_cast<uint2 *>(q + r * cols);
+    for (int64_t c = lane; c < nc; c += 64) dst[c] = encode8(src[c], inv);
+}
+
+// Rows of a row-major bf16 matrix, grouped in expert segments (offsets[]),
+// quantised into the packed E4M3 layout (segments start at pstart[], a
+// multiple of 32; padding rows get zero codes and scale 1).  One workgroup
+// per packed row block of 32 rows.  Pass 1: row maxima (8 threads per row);
+// pass 2: each wave writes whole 1 KiB fragments, lane l holding row l % 32,
+// bytes 32 kk + 16 (l / 32) .. + 15 of fragment kk.
+__global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
+                                                         const bf16_t *__restrict__ src,
+                                                         const int32_t *__restrict__ offsets,
+                                                         const int32_t *__restrict__ pstart,
+                                                         uint8_t *__restrict__ dst,
+                                                         float *__restrict__ scale) {
+    __shared__ int32_t s_row[32];
+    __shared__ float s_inv[32];
+    const int64_t rb = blockIdx.x;
+    const int64_t prow0 = rb * 32;
+    if (prow0 >= pstart[EL]) return;  // past the last segment (uniform)
+    const int tid = threadIdx.x;
+    if (tid < 32) {
+        int64_t lo = 0, hi = EL - 1;  // segment holding prow0: last e with pstart[e] <= prow0
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (pstart[mid] <= prow0) lo = mid;
+            else hi = mid - 1;
+        }
+        const int64_t local = prow0 + tid - pstart[lo];
+        const int64_t cnt = offsets[lo + 1] - offsets[lo];
+        s_row[tid] = local < cnt ? (int32_t)(offsets[lo] + local) : -1;
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 3, u = tid & 7;
+        const int32_t sr = s_row[r];
+        float m = 0.0f;
+        if (sr >= 0) {
+            const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)sr * K);
+            for (int64_t c = u; c < K / 8; c += 8) m = amax8(row[c], m);
+        }
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        if (u == 0) {
+            const int e = row_scale_exp(m);
+            s_inv[r] = __uint_as_float((uint32_t)(127 - e) << 23);
+            scale[prow0 + r] = __uint_as_float((uint32_t)(127 + e) << 23);
+        }
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 31;
+    const int32_t sr = s_row[r];
+    const float inv = s_inv[r];
+    const int64_t kb = K / 32;  // fragments per row block
+    u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + rb * kb * 1024);
+    for (int64_t kk = wave; kk < kb; kk += 4) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (sr >= 0) {
+            const u32x4_t *p =
+                reinterpret_cast<const u32x4_t *>(src + (int64_t)sr * K + kk * 32 + (lane >> 5) * 16);
+            const uint2 lo = encode8(p[0], inv), hi = encode8(p[1], inv);
+            w = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+        o[kk * 64 + lane] = w;
+    }
+}
+
+// Map workgroup b to tile L in [0, n): XCD x = b % 8 takes [x*per, x*per+per).
+__device__ __forceinline__ int xcd_tile_f8(int n) {
+    const int b = blockIdx.x;
+    const int per = (n + NUM_XCD - 1) / NUM_XCD;
+    const int j = b / NUM_XCD;
+    if (j >= per) return -1;
+    const int L = (b % NUM_XCD) * per + j;
+    return L < n ? L : -1;
+}
+
+// One workgroup per (m-tile, n-tile) in the blocked order of gemm_tile.h,
+// each XCD taking one contiguous eighth.  GATE_UP: A = packed x codes (K =
+// d), W0/W1 = gate/up codes [E_loc][f][d], out = h rows [cap][f].  Down: A =
+// packed h codes (K = f), W0 = down codes [E_loc][d][f], out = y rows
+// [cap][d].
+template <bool GATE_UP>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
+    int64_t d, int64_t f, const uint8_t *__restrict__ A, const float *__restrict__ sa,
+    const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
+    const uint8_t *__restrict__ W0, const float *__restrict__ s0, const uint8_t *__restrict__ W1,
+    const float *__restrict__ s1, bf16_t *__restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int MT = *n_mtiles;
+    const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
+    const int L = xcd_tile_f8(MT * NT);
+    if (L < 0) return;
+    int mt, nt;
+    blocked_tile(L, MT, NT, &mt, &nt);
+    const MTile t = mtiles[mt];
+    const int64_t prb = t.prow0 / 32;
+    if (GATE_UP) {
+        const int64_t wo = (int64_t)t.e * f + (int64_t)nt * BN_GU;
+        gemm_tile_f8<F8_SILU_ROWS>(A + prb * (d / 32) * 1024, d / 32, t.rows, (int)d, sa + t.prow0,
+                                   W0 + wo * d, W1 + wo * d, s0 + wo, s1 + wo,
+                                   out + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds);
+    } else {
+        const int64_t wo = (int64_t)t.e * d + (int64_t)nt * BN_DN;
+        gemm_tile_f8<F8_BF16>(A + prb * (f / 32) * 1024, f / 32, t.rows, (int)f, sa + t.prow0,
+                              W0 + wo * f, nullptr, s0 + wo, nullptr,
+                              out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
+    }
+}
+
+template <bool GATE_UP>
+hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, const MTile *mtiles,
+                          const int32_t *n_mtiles, const uint8_t *W0, const float *s0,
+                          const uint8_t *W1, const float *s1, bf16_t *out, hipStream_t s) {
+    const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
+    int64_t grid = D.max_mtiles() * NT;
+    grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
+    if (grid == 0) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_f8_kernel<GATE_UP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((grouped_gemm_f8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
+                       PA_LDS_BYTES, s, D.d, D.f, A, sa, mtiles, n_mtiles, W0, s0, W1, s1, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_t *q,
+                             float *scale, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, rows,
+                       cols, x, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
+                             const int32_t *pstart, uint8_t *dst, float *scale, hipStream_t s) {
+    const int64_t nrb = D.pcap() / 32;
+    if (nrb == 0 || D.EL() == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_pack_kernel, dim3((unsigned)nrb), dim3(256), 0, s, K, D.EL(), src,
+                       offsets, pstart, dst, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
+                                  const MTile *mtiles, const int32_t *n_mtiles,
+                                  const uint8_t *wg, const float *sg, const uint8_t *wu,
+                                  const float *su, bf16_t *h, hipStream_t s) {
+    return launch_gemm_f8<true>(D, xq, sx, mtiles, n_mtiles, wg, sg, wu, su, h, s);
+}
+
+hipError_t launch_gemm_down_f8(const Dims &D, const uint8_t *hq, const float *sh,
+                               const MTile *mtiles, const int32_t *n_mtiles, const uint8_t *wd,
+                               const float *sd, bf16_t *y, hipStream_t s) {
+    return launch_gemm_f8<false>(D, hq, sh, mtiles, n_mtiles, wd, sd, nullptr, nullptr, y, s);
+}
+
+}  // namespace moe

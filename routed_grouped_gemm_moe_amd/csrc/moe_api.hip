@@ -211,6 +211,93 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
     return hip_status(e);
 }
 
+moe_status moe_quantize_fp8(const void *x, int64_t rows, int64_t cols, void *q, float *scale,
+                            void *stream) {
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows * cols >= ((int64_t)1 << 40))
+        return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!x || !q || !scale || !aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_rows(rows, cols, (const bf16_t *)x, (uint8_t *)q, scale,
+                                        (hipStream_t)stream));
+}
+
+namespace {
+// Workspace of moe_expert_ffn_fp8 (256-byte aligned regions).
+struct Layout8 {
+    size_t mtiles, n_mtiles, mtile_base, pstart, xq, sx, h, hq, sh, total;
+};
+Layout8 make_layout8(const Dims &D) {
+    Layout8 L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t MT = (size_t)D.max_mtiles(), EL = (size_t)D.EL(), pcap = (size_t)D.pcap();
+    L.mtiles = take(MT * sizeof(MTile));
+    L.n_mtiles = take(sizeof(int32_t));
+    L.mtile_base = take(EL * sizeof(int32_t));
+    L.pstart = take((EL + 1) * sizeof(int32_t));
+    L.xq = take(pcap * (size_t)D.d);
+    L.sx = take(pcap * sizeof(float));
+    L.h = take((size_t)D.cap() * (size_t)D.f * 2);
+    L.hq = take(pcap * (size_t)D.f);
+    L.sh = take(pcap * sizeof(float));
+    L.total = off;
+    return L;
+}
+moe_status check_dims_fp8(const moe_dims *dims, Dims *D) {
+    moe_status st = check_dims(dims, D);
+    if (st != MOE_OK) return st;
+    if (D->f % 256 != 0) return MOE_ERR_UNSUPPORTED;  // K of both GEMMs: whole 256-byte stage pairs
+    return MOE_OK;
+}
+}  // namespace
+
+size_t moe_expert_ffn_fp8_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims_fp8(dims, &D) != MOE_OK) return 0;
+    return make_layout8(D).total;
+}
+
+moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                              const void *wq_gate, const float *s_gate, const void *wq_up,
+                              const float *s_up, const void *wq_down, const float *s_down,
+                              void *y_perm, void *ws, size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims_fp8(dims, &D);
+    if (st != MOE_OK) return st;
+    if (D.T == 0) return MOE_OK;
+    if (!x_perm || !offsets || !wq_gate || !s_gate || !wq_up || !s_up || !wq_down || !s_down ||
+        !y_perm)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm) || !aligned16(wq_gate) || !aligned16(wq_up) || !aligned16(wq_down) ||
+        !aligned16(y_perm))
+        return MOE_ERR_INVALID_ARG;
+    const Layout8 L = make_layout8(D);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    int32_t *pstart = at<int32_t>(ws, L.pstart);
+    uint8_t *xq = at<uint8_t>(ws, L.xq), *hq = at<uint8_t>(ws, L.hq);
+    float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh);
+    bf16_t *h = at<bf16_t>(ws, L.h);
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
+                                       nullptr, 0, s);
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, pstart, xq, sx, s);
+    if (e == hipSuccess)
+        e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, (const uint8_t *)wq_gate, s_gate,
+                                   (const uint8_t *)wq_up, s_up, h, s);
+    if (e == hipSuccess) e = launch_quant_pack(D, D.f, h, offsets, pstart, hq, sh, s);
+    if (e == hipSuccess)
+        e = launch_gemm_down_f8(D, hq, sh, mt, nmt, (const uint8_t *)wq_down, s_down,
+                                (bf16_t *)y_perm, s);
+    return hip_status(e);
+}
+
 moe_status moe_combine(const moe_dims *dims, const void *y_perm, const int32_t *inv_perm,
                        const float *topk_w, void *out, moe_dtype out_dtype, void *stream) {
     Dims D;

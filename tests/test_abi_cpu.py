@@ -113,3 +113,26 @@ def test_empty_batch_is_a_no_op():
     assert lib.moe_combine(C.byref(D), None, None, None, None, 0, None) == OK
     assert lib.moe_layer(C.byref(D), None, None, None, None, None, None, None, 0, None, None, None,
                          0, None) == OK
+
+
+def test_fp8_entry_points_check_arguments_before_any_gpu_call():
+    lib = M.load()
+    D = dims()
+    need = M.moe_expert_ffn_fp8_workspace_bytes(D)
+    # E4M3 codes of x, h (T*k rows each, padded per expert) and h in bf16
+    assert need >= 256 * 2 * (512 + 1024 + 1024 * 2)
+    # f must be a multiple of 256 (two 128-byte K stages per loop step)
+    assert M.moe_expert_ffn_fp8_workspace_bytes(dims(f=384)) == 0
+    D384 = dims(f=384)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS, 1 << 40, None)
+    assert lib.moe_expert_ffn_fp8(C.byref(D384), *args) == -2
+    assert lib.moe_expert_ffn_fp8(C.byref(D), None, *args[1:]) == INVALID
+    assert lib.moe_expert_ffn_fp8(C.byref(D), C.c_void_p(0x10002), *args[1:]) == INVALID
+    assert lib.moe_expert_ffn_fp8(C.byref(D), *args[:9], FAKE_WS, need - 1, None) == WORKSPACE
+    assert lib.moe_expert_ffn_fp8(C.byref(dims(T=0)), None, None, None, None, None, None, None,
+                                  None, None, None, 0, None) == OK
+    # quantiser: columns a multiple of 16, aligned pointers, empty is a no-op
+    assert lib.moe_quantize_fp8(FAKE, 4, 24, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_fp8(C.c_void_p(0x10002), 4, 32, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_fp8(None, 4, 32, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_fp8(None, 0, 32, None, None, None) == OK

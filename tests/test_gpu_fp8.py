@@ -1,0 +1,113 @@
+"""GPU parity of the W8A8 (E4M3) path against the oracle.
+
+The quantiser decides integers (codes) from exact inputs, so its codes and
+scales must equal the oracle's bit for bit.  The fp8 FFN is compared with the
+oracle's float64 evaluation of the same quantised operands.  The fp8 matrix
+cores do not add a 64-product step exactly: measured on gfx950, one
+v_mfma_f32_32x32x64_f8f6f4 is off by up to 2.8e-4 of the sum of the
+products' magnitudes (about 12-bit alignment).  That error moves a few h
+values across an E4M3 rounding boundary (about 0.2% of h codes differ from
+the oracle's), and each such code moves y by one E4M3 step of that h element
+times its weights.  Bounds: 6e-2 per token (the rel_err metric of the bf16
+path; 2.9e-2 measured at f = 1024, where one code weighs most) and 6e-3 for
+the root-mean-square error over all checked outputs (a wrong operand, scale
+or k-step gives errors of 1e-1 and more).
+Inputs: the seeded workloads; the permutation is the oracle's own.
+"""
+import numpy as np
+import pytest
+
+import moe_workloads as W
+import oracle
+from gpu_util import dev, dev_bf16, host_f32, rel_err, say
+
+TOL_FP8_TOKEN = 6e-2
+TOL_FP8_RMS = 6e-3
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import routed_grouped_gemm_moe_amd as M
+
+
+def _quant_both(name, w_bits):
+    """Quantise a bf16 weight tensor [EL, out, K] on the GPU and in the
+    oracle; assert equal codes and scales; return both sides."""
+    EL, n_out, K = w_bits.shape
+    say(f"moe_quantize_fp8 {name} {EL}x{n_out}x{K}")
+    q, s = M.moe_quantize_fp8(dev_bf16(w_bits))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_rows_e4m3(w_bits.reshape(-1, K))
+    assert np.array_equal(q.cpu().numpy().reshape(-1, K), rq), f"{name} codes"
+    assert np.array_equal(s.cpu().numpy().reshape(-1).view(np.uint32), rs.view(np.uint32)), \
+        f"{name} scales"
+    return (q, s), (rq.reshape(EL, n_out, K), rs.reshape(EL, n_out))
+
+
+def test_quantizer_bit_exact_on_edge_rows():
+    rng = np.random.default_rng(21)
+    rows, cols = 64, 512
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= (2.0 ** rng.integers(-30, 30, (rows, 1))).astype(np.float32)
+    x[0] = 0.0                                   # all-zero row: scale 1, codes 0
+    x[1] = 0.0
+    x[1, 7] = 448.0                              # exact maximum
+    x[2, :] = 1e-38                              # tiny row (scale clamped at 2^-126)
+    x[3, 5] = 3.0e38                             # huge element
+    x[4] = np.linspace(-1, 1, cols)              # many exact midpoints after scaling
+    x[5, ::2] = -0.0
+    xb = W.f32_to_bf16_bits(x)
+    say("moe_quantize_fp8 edge rows")
+    q, s = M.moe_quantize_fp8(dev_bf16(xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_rows_e4m3(xb)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+FP8_CASES = {
+    "tiny": W.CONFIGS["tiny"],
+    "ragged_T300": W.CONFIGS["tiny"].scaled(T=300, d=256, f=512, seed=3),
+    "local_subset_e16k4": W.CONFIGS["tiny"].scaled(T=200, d=512, f=256, E=16, k=4, e_lo=3,
+                                                   e_hi=11, out_fp32=True, seed=4),
+    "e128k8": W.CONFIGS["tiny"].scaled(T=160, d=256, f=256, E=128, k=8, seed=7),
+    "multi_tile_rows": W.CONFIGS["tiny"].scaled(T=1000, d=256, f=256, E=4, k=2, seed=10),
+    "mixtral": W.CONFIGS["mixtral"],
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_fp8_ffn_matches_oracle(name):
+    cfg = FP8_CASES[name].scaled(name=name)
+    arrs = W.generate(cfg)
+    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    r_ids, _ = oracle.route(arrs["x"], arrs["w_router"], cfg.k, bias=arrs["bias"])
+    _, ro, rp, _ = oracle.permute(r_ids, cfg.E, cfg.e_lo, cfg.E_hi)
+    N = int(ro[-1])
+    (gq, gs), (rgq, rgs) = _quant_both("w_gate", arrs["w_gate"])
+    (uq, us), (ruq, rus) = _quant_both("w_up", arrs["w_up"])
+    (dq, ds), (rdq, rds) = _quant_both("w_down", arrs["w_down"])
+    cap = cfg.T * cfg.k
+    xp = np.zeros((max(cap, 1), cfg.d), np.uint16)
+    xp[:N] = arrs["x"][rp]
+    say(f"moe_expert_ffn_fp8 {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} N={N}")
+    y = M.moe_expert_ffn_fp8(D, dev_bf16(xp), dev(ro.astype(np.int32)), gq, gs, uq, us, dq, ds)
+    torch.cuda.synchronize()
+    if N == 0:
+        return
+    rows = np.arange(N) if N <= 1200 else np.unique(
+        np.concatenate([[0, N - 1], ro[1:-1].clip(0, N - 1),
+                        np.random.default_rng(1).choice(N, 40, replace=False)]))
+    expert_of_row = (np.searchsorted(ro, rows, side="right") - 1).astype(np.int32)
+    ref = oracle.expert_rows_fp8(arrs["x"][rp[rows]], expert_of_row, rgq, rgs, ruq, rus, rdq, rds)
+    got = host_f32(y[torch.as_tensor(rows, device="cuda")])
+    err = rel_err(got, ref)
+    rms = float(np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2)))
+    say(f"  fp8 ffn rel err {err:.3e}, rms err {rms:.3e} over {len(rows)} rows")
+    assert err <= TOL_FP8_TOKEN
+    assert rms <= TOL_FP8_RMS
+    # repeatable: a second call gives the same bits
+    y2 = M.moe_expert_ffn_fp8(D, dev_bf16(xp), dev(ro.astype(np.int32)), gq, gs, uq, us, dq, ds)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:N].view(torch.int16), y2[:N].view(torch.int16))
