@@ -77,14 +77,34 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int64_t c
     for (int64_t c = lane; c < nc; c += 64) dst[c] = encode8(src[c], inv);
 }
 
-// Rows of a row-major bf16 matrix, grouped in expert segments (offsets[]),
-// quantised into the packed E4M3 layout (segments start at pstart[], a
-// multiple of 32; padding rows get zero codes and scale 1).  One workgroup
-// per packed row block of 32 rows.  Pass 1: row maxima (8 threads per row);
-// pass 2: each wave writes whole 1 KiB fragments, lane l holding row l % 32,
-// bytes 32 kk + 16 (l / 32) .. + 15 of fragment kk.
+// Largest magnitude of each routed row (rows below offsets[EL]) of a
+// row-major bf16 matrix: one wave per row, 4 rows per workgroup.
+__global__ __launch_bounds__(256) void row_amax_kernel(int64_t K, int64_t EL,
+                                                       const bf16_t *__restrict__ src,
+                                                       const int32_t *__restrict__ offsets,
+                                                       float *__restrict__ amax) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= offsets[EL]) return;
+    const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + r * K);
+    float m = 0.0f;
+    for (int64_t c = lane; c < K / 8; c += 64) m = amax8(row[c], m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) amax[r] = m;
+}
+
+// Rows of a row-major bf16 matrix with K columns, grouped in expert segments
+// (offsets[]), quantised into the packed E4M3 layout (segments start at
+// pstart[], a multiple of 32; padding rows get zero codes and scale 1), with
+// the row maxima of row_amax_kernel.  Workgroup (row block, y) writes
+// fragments y*PACK_FR .. y*PACK_FR + PACK_FR - 1 of its 32 rows; each wave
+// writes whole 1 KiB fragments, lane l holding row l % 32, bytes
+// 32 kk + 16 (l / 32) .. + 15 of fragment kk.
+constexpr int PACK_FR = 8;
 __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
                                                          const bf16_t *__restrict__ src,
+                                                         const float *__restrict__ amax,
                                                          const int32_t *__restrict__ offsets,
                                                          const int32_t *__restrict__ pstart,
                                                          uint8_t *__restrict__ dst,
@@ -104,25 +124,11 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
         }
         const int64_t local = prow0 + tid - pstart[lo];
         const int64_t cnt = offsets[lo + 1] - offsets[lo];
-        s_row[tid] = local < cnt ? (int32_t)(offsets[lo] + local) : -1;
-    }
-    __syncthreads();
-    {
-        const int r = tid >> 3, u = tid & 7;
-        const int32_t sr = s_row[r];
-        float m = 0.0f;
-        if (sr >= 0) {
-            const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + (int64_t)sr * K);
-            for (int64_t c = u; c < K / 8; c += 8) m = amax8(row[c], m);
-        }
-        m = fmaxf(m, __shfl_xor(m, 1));
-        m = fmaxf(m, __shfl_xor(m, 2));
-        m = fmaxf(m, __shfl_xor(m, 4));
-        if (u == 0) {
-            const int e = row_scale_exp(m);
-            s_inv[r] = __uint_as_float((uint32_t)(127 - e) << 23);
-            scale[prow0 + r] = __uint_as_float((uint32_t)(127 + e) << 23);
-        }
+        const int32_t sr = local < cnt ? (int32_t)(offsets[lo] + local) : -1;
+        const int e = row_scale_exp(sr >= 0 ? amax[sr] : 0.0f);
+        s_row[tid] = sr;
+        s_inv[tid] = __uint_as_float((uint32_t)(127 - e) << 23);
+        if (blockIdx.y == 0) scale[prow0 + tid] = __uint_as_float((uint32_t)(127 + e) << 23);
     }
     __syncthreads();
     const int lane = tid & 63, wave = tid >> 6;
@@ -130,8 +136,9 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
     const int32_t sr = s_row[r];
     const float inv = s_inv[r];
     const int64_t kb = K / 32;  // fragments per row block
+    const int64_t k_end = min<int64_t>(kb, (int64_t)(blockIdx.y + 1) * PACK_FR);
     u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + rb * kb * 1024);
-    for (int64_t kk = wave; kk < kb; kk += 4) {
+    for (int64_t kk = (int64_t)blockIdx.y * PACK_FR + wave; kk < k_end; kk += 4) {
         u32x4_t w = {0u, 0u, 0u, 0u};
         if (sr >= 0) {
             const u32x4_t *p =
@@ -213,11 +220,18 @@ hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_
 }
 
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
-                             const int32_t *pstart, uint8_t *dst, float *scale, hipStream_t s) {
-    const int64_t nrb = D.pcap() / 32;
+                             const int32_t *pstart, float *amax, uint8_t *dst, float *scale,
+                             hipStream_t s) {
+    const int64_t nrb = D.pcap() / 32, rows = D.cap();
     if (nrb == 0 || D.EL() == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_pack_kernel, dim3((unsigned)nrb), dim3(256), 0, s, K, D.EL(), src,
-                       offsets, pstart, dst, scale);
+    // row maxima of the routed rows (grid sized for every row a segment may hold)
+    hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, K,
+                       D.EL(), src, offsets, amax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned ny = (unsigned)((K / 32 + PACK_FR - 1) / PACK_FR);
+    hipLaunchKernelGGL(quant_pack_kernel, dim3((unsigned)nrb, ny), dim3(256), 0, s, K, D.EL(), src,
+                       amax, offsets, pstart, dst, scale);
     return hipGetLastError();
 }
 

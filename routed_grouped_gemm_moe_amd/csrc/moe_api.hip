@@ -224,7 +224,7 @@ moe_status moe_quantize_fp8(const void *x, int64_t rows, int64_t cols, void *q, 
 namespace {
 // Workspace of moe_expert_ffn_fp8 (256-byte aligned regions).
 struct Layout8 {
-    size_t mtiles, n_mtiles, mtile_base, pstart, xq, sx, h, hq, sh, total;
+    size_t mtiles, n_mtiles, mtile_base, pstart, amax, xq, sx, h, hq, sh, total;
 };
 Layout8 make_layout8(const Dims &D) {
     Layout8 L{};
@@ -239,6 +239,7 @@ Layout8 make_layout8(const Dims &D) {
     L.n_mtiles = take(sizeof(int32_t));
     L.mtile_base = take(EL * sizeof(int32_t));
     L.pstart = take((EL + 1) * sizeof(int32_t));
+    L.amax = take((size_t)D.cap() * sizeof(float));
     L.xq = take(pcap * (size_t)D.d);
     L.sx = take(pcap * sizeof(float));
     L.h = take((size_t)D.cap() * (size_t)D.f * 2);
@@ -287,11 +288,13 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const in
     hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
                                        nullptr, 0, s);
     if (e == hipSuccess)
-        e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, pstart, xq, sx, s);
+        e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, pstart, at<float>(ws, L.amax),
+                              xq, sx, s);
     if (e == hipSuccess)
         e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, (const uint8_t *)wq_gate, s_gate,
                                    (const uint8_t *)wq_up, s_up, h, s);
-    if (e == hipSuccess) e = launch_quant_pack(D, D.f, h, offsets, pstart, hq, sh, s);
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.amax), hq, sh, s);
     if (e == hipSuccess)
         e = launch_gemm_down_f8(D, hq, sh, mt, nmt, (const uint8_t *)wq_down, s_down,
                                 (bf16_t *)y_perm, s);

@@ -205,7 +205,8 @@ hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *in
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_t *q,
                              float *scale, hipStream_t s);
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
-                             const int32_t *pstart, uint8_t *dst, float *scale, hipStream_t s);
+                             const int32_t *pstart, float *amax, uint8_t *dst, float *scale,
+                             hipStream_t s);
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
                                   const uint8_t *wg, const float *sg, const uint8_t *wu,
