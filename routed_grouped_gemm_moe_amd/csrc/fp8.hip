@@ -170,7 +170,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
     int64_t d, int64_t f, const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
     const uint8_t *__restrict__ W0, const float *__restrict__ s0, const uint8_t *__restrict__ W1,
-    const float *__restrict__ s1, bf16_t *__restrict__ out) {
+    const float *__restrict__ s1, bf16_t *__restrict__ out, uint32_t *__restrict__ rowmax) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int MT = *n_mtiles;
     const int NT = GATE_UP ? (int)(f / BN_GU) : (int)(d / BN_DN);
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
         const int64_t wo = (int64_t)t.e * f + (int64_t)nt * BN_GU;
         gemm_tile_f8<F8_SILU_ROWS>(A + prb * (d / 32) * 1024, d / 32, t.rows, (int)d, sa + t.prow0,
                                    W0 + wo * d, W1 + wo * d, s0 + wo, s1 + wo,
-                                   out + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds);
+                                   out + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds,
+                                   rowmax + t.row0);
     } else {
         const int64_t wo = (int64_t)t.e * d + (int64_t)nt * BN_DN;
         gemm_tile_f8<F8_BF16>(A + prb * (f / 32) * 1024, f / 32, t.rows, (int)f, sa + t.prow0,
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
 template <bool GATE_UP>
 hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, const MTile *mtiles,
                           const int32_t *n_mtiles, const uint8_t *W0, const float *s0,
-                          const uint8_t *W1, const float *s1, bf16_t *out, hipStream_t s) {
+                          const uint8_t *W1, const float *s1, bf16_t *out, uint32_t *rowmax,
+                          hipStream_t s) {
     const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
     int64_t grid = D.max_mtiles() * NT;
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
@@ -205,7 +207,8 @@ hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, cons
                                        hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_f8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       PA_LDS_BYTES, s, D.d, D.f, A, sa, mtiles, n_mtiles, W0, s0, W1, s1, out);
+                       PA_LDS_BYTES, s, D.d, D.f, A, sa, mtiles, n_mtiles, W0, s0, W1, s1, out,
+                       rowmax);
     return hipGetLastError();
 }
 
@@ -220,15 +223,17 @@ hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_
 }
 
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
-                             const int32_t *pstart, float *amax, uint8_t *dst, float *scale,
-                             hipStream_t s) {
+                             const int32_t *pstart, float *amax, bool have_amax, uint8_t *dst,
+                             float *scale, hipStream_t s) {
     const int64_t nrb = D.pcap() / 32, rows = D.cap();
     if (nrb == 0 || D.EL() == 0) return hipSuccess;
-    // row maxima of the routed rows (grid sized for every row a segment may hold)
-    hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, K,
-                       D.EL(), src, offsets, amax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!have_amax) {
+        // row maxima of the routed rows (grid sized for every row a segment may hold)
+        hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, K,
+                           D.EL(), src, offsets, amax);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const unsigned ny = (unsigned)((K / 32 + PACK_FR - 1) / PACK_FR);
     hipLaunchKernelGGL(quant_pack_kernel, dim3((unsigned)nrb, ny), dim3(256), 0, s, K, D.EL(), src,
                        amax, offsets, pstart, dst, scale);
@@ -238,14 +243,15 @@ hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const 
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
                                   const uint8_t *wg, const float *sg, const uint8_t *wu,
-                                  const float *su, bf16_t *h, hipStream_t s) {
-    return launch_gemm_f8<true>(D, xq, sx, mtiles, n_mtiles, wg, sg, wu, su, h, s);
+                                  const float *su, bf16_t *h, uint32_t *hmax, hipStream_t s) {
+    return launch_gemm_f8<true>(D, xq, sx, mtiles, n_mtiles, wg, sg, wu, su, h, hmax, s);
 }
 
 hipError_t launch_gemm_down_f8(const Dims &D, const uint8_t *hq, const float *sh,
                                const MTile *mtiles, const int32_t *n_mtiles, const uint8_t *wd,
                                const float *sd, bf16_t *y, hipStream_t s) {
-    return launch_gemm_f8<false>(D, hq, sh, mtiles, n_mtiles, wd, sd, nullptr, nullptr, y, s);
+    return launch_gemm_f8<false>(D, hq, sh, mtiles, n_mtiles, wd, sd, nullptr, nullptr, y, nullptr,
+                                 s);
 }
 
 }  // namespace moe

@@ -156,6 +156,9 @@ enum { F8_SILU_ROWS = 0, F8_BF16 = 1 };
 //          apart; sb0/sb1: their scales
 //   out    F8_SILU_ROWS: h = bf16(silu(g) * u) for 128 columns, rows of o_ld
 //          elements; F8_BF16: y = bf16(acc * sa * sb), 256 columns
+//   rowmax F8_SILU_ROWS: per output row, the float bits of the largest |h|
+//          written so far (atomic max; non-negative floats order as their
+//          bits); zero before the first tile of a row
 // LDS: PA_LDS_BYTES at lds, free again when the call returns.
 template <int EPI>
 __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int64_t a_kb,
@@ -163,7 +166,7 @@ __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int
                                              const uint8_t *__restrict__ B0,
                                              const uint8_t *__restrict__ B1, const float *sb0,
                                              const float *sb1, bf16_t *__restrict__ out,
-                                             int64_t o_ld, char *lds) {
+                                             int64_t o_ld, char *lds, uint32_t *rowmax = nullptr) {
     constexpr bool GATE_UP = EPI == F8_SILU_ROWS;
     int tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
@@ -236,6 +239,14 @@ __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int
         for (int g = tid; g < a_rows * 16; g += GEMM_THREADS) {
             const int r = g >> 4, c = g & 15;
             reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld)[c] = src[r * 16 + (c ^ (r & 15))];
+        }
+        if (rowmax && tid < a_rows) {  // one thread per row: max |h| over the tile's columns
+            float m = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf16x8_elem(src[tid * 16 + c], e)));
+            atomicMax(rowmax + tid, __float_as_uint(m));
         }
     } else {
 #pragma unroll

@@ -224,7 +224,7 @@ moe_status moe_quantize_fp8(const void *x, int64_t rows, int64_t cols, void *q, 
 namespace {
 // Workspace of moe_expert_ffn_fp8 (256-byte aligned regions).
 struct Layout8 {
-    size_t mtiles, n_mtiles, mtile_base, pstart, amax, xq, sx, h, hq, sh, total;
+    size_t mtiles, n_mtiles, mtile_base, pstart, amax, hmax, xq, sx, h, hq, sh, total;
 };
 Layout8 make_layout8(const Dims &D) {
     Layout8 L{};
@@ -240,6 +240,7 @@ Layout8 make_layout8(const Dims &D) {
     L.mtile_base = take(EL * sizeof(int32_t));
     L.pstart = take((EL + 1) * sizeof(int32_t));
     L.amax = take((size_t)D.cap() * sizeof(float));
+    L.hmax = take((size_t)D.cap() * sizeof(float));
     L.xq = take(pcap * (size_t)D.d);
     L.sx = take(pcap * sizeof(float));
     L.h = take((size_t)D.cap() * (size_t)D.f * 2);
@@ -285,16 +286,17 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const in
     uint8_t *xq = at<uint8_t>(ws, L.xq), *hq = at<uint8_t>(ws, L.hq);
     float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh);
     bf16_t *h = at<bf16_t>(ws, L.h);
+    // the tile-table kernel also zeroes h's row maxima (atomic max targets)
     hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
-                                       nullptr, 0, s);
+                                       at<int32_t>(ws, L.hmax), D.cap(), s);
     if (e == hipSuccess)
         e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, pstart, at<float>(ws, L.amax),
-                              xq, sx, s);
+                              false, xq, sx, s);
     if (e == hipSuccess)
         e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, (const uint8_t *)wq_gate, s_gate,
-                                   (const uint8_t *)wq_up, s_up, h, s);
+                                   (const uint8_t *)wq_up, s_up, h, at<uint32_t>(ws, L.hmax), s);
     if (e == hipSuccess)
-        e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.amax), hq, sh, s);
+        e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.hmax), true, hq, sh, s);
     if (e == hipSuccess)
         e = launch_gemm_down_f8(D, hq, sh, mt, nmt, (const uint8_t *)wq_down, s_down,
                                 (bf16_t *)y_perm, s);

@@ -200,17 +200,19 @@ hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *in
 
 // W8A8 (fp8.hip): per-row E4M3 quantisation, row-major or into the packed
 // layout at the segment starts pstart[] (rows of a row-major matrix with K
-// columns grouped by offsets[]), and the grouped E4M3 GEMMs: h rows [cap][f]
-// from packed x codes, y rows [cap][d] from packed h codes.
+// columns grouped by offsets[]; row maxima computed first into amax, or
+// given there when have_amax), and the grouped E4M3 GEMMs: h rows [cap][f]
+// (and their row maxima, atomically into the zeroed hmax) from packed x
+// codes, y rows [cap][d] from packed h codes.
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_t *q,
                              float *scale, hipStream_t s);
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
-                             const int32_t *pstart, float *amax, uint8_t *dst, float *scale,
-                             hipStream_t s);
+                             const int32_t *pstart, float *amax, bool have_amax, uint8_t *dst,
+                             float *scale, hipStream_t s);
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
                                   const uint8_t *wg, const float *sg, const uint8_t *wu,
-                                  const float *su, bf16_t *h, hipStream_t s);
+                                  const float *su, bf16_t *h, uint32_t *hmax, hipStream_t s);
 hipError_t launch_gemm_down_f8(const Dims &D, const uint8_t *hq, const float *sh,
                                const MTile *mtiles, const int32_t *n_mtiles, const uint8_t *wd,
                                const float *sd, bf16_t *y, hipStream_t s);
