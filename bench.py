@@ -127,13 +127,49 @@ def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
     }), flush=True)
 
 
+def layer_fp8_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
+    """Time moe_layer_fp8 (route, permute, W8A8 FFN, combine) on the workload;
+    the weights are quantised once beforehand."""
+    (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
+    ws = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
+                      device="cuda")
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    step = lambda: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
+                                   out_dtype=dt, topk_ids_out=ids, ws=ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    n_local = int(((ids_h >= cfg.e_lo) & (ids_h < cfg.E_hi)).sum())
+    flops = 6.0 * cfg.d * cfg.f * n_local
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    print(json.dumps({
+        "mode": "layer_fp8",
+        "metric": "MoE-layer tokens/s with the W8A8 (E4M3) expert FFN, 1 GPU",
+        "value": round(cfg.T * args.steps / elapsed, 1), "unit": "tokens/s",
+        "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup,
+        "layer_tflops": round(flops / (ms * 1e-3) / 1e12, 2), "dtype": "fp8_e4m3",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
+                   "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi]},
+    }), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--mode", default="layer", choices=["layer", "copy", "ffn_fp8", "ffn_bf16"])
+    ap.add_argument("--mode", default="layer",
+                    choices=["layer", "copy", "ffn_fp8", "ffn_bf16", "layer_fp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
@@ -166,6 +202,9 @@ def main() -> None:
     D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
     if args.mode in ("ffn_fp8", "ffn_bf16"):
         ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
+        return
+    if args.mode == "layer_fp8":
+        layer_fp8_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
         return
     M.moe_set_gather_dispatch(args.dispatch == "gather")
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")

@@ -173,6 +173,19 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const in
                               const float *s_up, const void *wq_down, const float *s_down,
                               void *y_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_layer_fp8: the whole forward pass with the W8A8 FFN, staged: route
+ * (as moe_route), row-major permute (as moe_permute), moe_expert_ffn_fp8,
+ * moe_combine -- one stream, one workspace, no host synchronisation.
+ * Arguments as moe_layer, with the E4M3 weights and scales of
+ * moe_expert_ffn_fp8 in place of the bf16 weights.  Requires f % 256 == 0. */
+size_t moe_layer_fp8_workspace_bytes(const moe_dims *dims);
+moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_router,
+                         const float *bias, const void *wq_gate, const float *s_gate,
+                         const void *wq_up, const float *s_up, const void *wq_down,
+                         const float *s_down, void *out, moe_dtype out_dtype,
+                         int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                         void *stream);
+
 /* ---- moe_combine: gate-weighted sum back to token order (Weave §2.1 stage 5).
  *   y_perm   bf16 [T*k, d]  expert outputs by row
  *   inv_perm i32  [T, k]    row of each (token, slot), -1 = skip

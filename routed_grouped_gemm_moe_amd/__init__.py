@@ -82,6 +82,8 @@ def load():
         "moe_quantize_fp8": ([vp, i64, i64, vp, vp, vp], i32),
         "moe_expert_ffn_fp8_workspace_bytes": ([dp], sz),
         "moe_expert_ffn_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_layer_fp8_workspace_bytes": ([dp], sz),
+        "moe_layer_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
         "moe_combine": ([dp, vp, vp, vp, vp, i32, vp], i32),
         "moe_layer_workspace_bytes": ([dp], sz),
         "moe_layer": ([dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
@@ -294,6 +296,40 @@ def moe_expert_ffn_fp8(dims, x_perm, offsets, wq_gate, s_gate, wq_up, s_up, wq_d
                                    ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "moe_expert_ffn_fp8")
     return y_perm
+
+
+def moe_layer_fp8_workspace_bytes(dims) -> int:
+    return int(load().moe_layer_fp8_workspace_bytes(C.byref(_dims(dims))))
+
+
+def moe_layer_fp8(dims, x, w_router, wq_gate, s_gate, wq_up, s_up, wq_down, s_down, bias=None,
+                  out=None, out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None,
+                  ws=None, stream=None):
+    """Forward pass with the W8A8 expert FFN (staged).  Returns out [T, d]."""
+    import torch
+    D = _dims(dims)
+    dev = x.device
+    EL = D.e_hi - D.e_lo
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(w_router, torch.bfloat16, (D.E, D.d), "w_router")
+    _require(wq_gate, torch.uint8, (EL, D.f, D.d), "wq_gate")
+    _require(wq_up, torch.uint8, (EL, D.f, D.d), "wq_up")
+    _require(wq_down, torch.uint8, (EL, D.d, D.f), "wq_down")
+    _require(s_gate, torch.float32, (EL, D.f), "s_gate")
+    _require(s_up, torch.float32, (EL, D.f), "s_up")
+    _require(s_down, torch.float32, (EL, D.d), "s_down")
+    if bias is not None:
+        _require(bias, torch.float32, (D.E,), "bias")
+    dt = torch.float32 if out_dtype == MOE_F32 else torch.bfloat16
+    out = torch.empty((D.T, D.d), dtype=dt, device=dev) if out is None else out
+    need = moe_layer_fp8_workspace_bytes(D)
+    ws = _workspace(need, dev) if ws is None else ws
+    rc = load().moe_layer_fp8(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(wq_gate),
+                              _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(wq_down), _ptr(s_down),
+                              _ptr(out), out_dtype, _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_layer_fp8")
+    return out
 
 
 def moe_combine(dims, y_perm, inv_perm, topk_w, out=None, out_dtype: int = MOE_BF16, stream=None):

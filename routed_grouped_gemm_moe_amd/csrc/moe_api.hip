@@ -257,6 +257,110 @@ moe_status check_dims_fp8(const moe_dims *dims, Dims *D) {
 }
 }  // namespace
 
+namespace {
+// The launches of the W8A8 FFN over a Layout8 workspace at ws.
+hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offsets,
+                       const uint8_t *wq_gate, const float *s_gate, const uint8_t *wq_up,
+                       const float *s_up, const uint8_t *wq_down, const float *s_down,
+                       bf16_t *y_perm, void *ws, hipStream_t s) {
+    const Layout8 L = make_layout8(D);
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    int32_t *pstart = at<int32_t>(ws, L.pstart);
+    uint8_t *xq = at<uint8_t>(ws, L.xq), *hq = at<uint8_t>(ws, L.hq);
+    float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh);
+    bf16_t *h = at<bf16_t>(ws, L.h);
+    // the tile-table kernel also zeroes h's row maxima (atomic max targets)
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
+                                       at<int32_t>(ws, L.hmax), D.cap(), s);
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.d, x_perm, offsets, pstart, at<float>(ws, L.amax), false, xq, sx,
+                              s);
+    if (e == hipSuccess)
+        e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, wq_gate, s_gate, wq_up, s_up, h,
+                                   at<uint32_t>(ws, L.hmax), s);
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.hmax), true, hq, sh, s);
+    if (e == hipSuccess) e = launch_gemm_down_f8(D, hq, sh, mt, nmt, wq_down, s_down, y_perm, s);
+    return e;
+}
+
+// Workspace of moe_layer_fp8: routing, the row-major permute, x_perm and y
+// rows, then the FFN's Layout8 region.
+struct LayoutL8 {
+    size_t route, ids, gates, blk_counts, blk_base, counts, offsets, perm_src, inv_perm, x_perm, y,
+        ffn, total;
+};
+LayoutL8 make_layout_l8(const Dims &D) {
+    LayoutL8 L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (off + bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    const size_t Tk = (size_t)(D.T * D.k), EL = (size_t)D.EL(), cap = (size_t)D.cap();
+    L.route = take(route_workspace_bytes(D));
+    L.ids = take(Tk * sizeof(int32_t));
+    L.gates = take(Tk * sizeof(float));
+    L.blk_counts = take((size_t)D.perm_blocks() * EL * sizeof(int32_t));
+    L.blk_base = take((size_t)D.perm_blocks() * EL * sizeof(int32_t));
+    L.counts = take(EL * sizeof(int32_t));
+    L.offsets = take((EL + 1) * sizeof(int32_t));
+    L.perm_src = take(cap * sizeof(int32_t));
+    L.inv_perm = take(Tk * sizeof(int32_t));
+    L.x_perm = take(cap * (size_t)D.d * 2);
+    L.y = take(cap * (size_t)D.d * 2);
+    L.ffn = take(make_layout8(D).total);
+    L.total = off;
+    return L;
+}
+}  // namespace
+
+size_t moe_layer_fp8_workspace_bytes(const moe_dims *dims) {
+    Dims D;
+    if (check_dims_fp8(dims, &D) != MOE_OK) return 0;
+    return make_layout_l8(D).total;
+}
+
+moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_router,
+                         const float *bias, const void *wq_gate, const float *s_gate,
+                         const void *wq_up, const float *s_up, const void *wq_down,
+                         const float *s_down, void *out, moe_dtype out_dtype,
+                         int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                         void *stream) {
+    Dims D;
+    moe_status st = check_dims_fp8(dims, &D);
+    if (st != MOE_OK) return st;
+    if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+    if (D.T == 0) return MOE_OK;
+    if (!x || !w_router || !wq_gate || !s_gate || !wq_up || !s_up || !wq_down || !s_down || !out)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(wq_gate) || !aligned16(wq_up) ||
+        !aligned16(wq_down) || !aligned16(out))
+        return MOE_ERR_INVALID_ARG;
+    const LayoutL8 L = make_layout_l8(D);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
+    int32_t *offsets = at<int32_t>(ws, L.offsets), *inv_perm = at<int32_t>(ws, L.inv_perm);
+    bf16_t *x_perm = at<bf16_t>(ws, L.x_perm), *y = at<bf16_t>(ws, L.y);
+    hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
+                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s);
+    if (e == hipSuccess)
+        e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
+                           at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
+                           at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), nullptr,
+                           nullptr, nullptr, nullptr, nullptr, 0, s);
+    if (e == hipSuccess)
+        e = run_ffn_fp8(D, x_perm, offsets, (const uint8_t *)wq_gate, s_gate,
+                        (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
+                        at<char>(ws, L.ffn), s);
+    if (e == hipSuccess) e = launch_combine(D, y, inv_perm, gates, out, out_dtype == MOE_F32, s);
+    return hip_status(e);
+}
+
 size_t moe_expert_ffn_fp8_workspace_bytes(const moe_dims *dims) {
     Dims D;
     if (check_dims_fp8(dims, &D) != MOE_OK) return 0;
@@ -279,28 +383,9 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const in
         return MOE_ERR_INVALID_ARG;
     const Layout8 L = make_layout8(D);
     if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-    MTile *mt = at<MTile>(ws, L.mtiles);
-    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
-    int32_t *pstart = at<int32_t>(ws, L.pstart);
-    uint8_t *xq = at<uint8_t>(ws, L.xq), *hq = at<uint8_t>(ws, L.hq);
-    float *sx = at<float>(ws, L.sx), *sh = at<float>(ws, L.sh);
-    bf16_t *h = at<bf16_t>(ws, L.h);
-    // the tile-table kernel also zeroes h's row maxima (atomic max targets)
-    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base), pstart,
-                                       at<int32_t>(ws, L.hmax), D.cap(), s);
-    if (e == hipSuccess)
-        e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, pstart, at<float>(ws, L.amax),
-                              false, xq, sx, s);
-    if (e == hipSuccess)
-        e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, (const uint8_t *)wq_gate, s_gate,
-                                   (const uint8_t *)wq_up, s_up, h, at<uint32_t>(ws, L.hmax), s);
-    if (e == hipSuccess)
-        e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.hmax), true, hq, sh, s);
-    if (e == hipSuccess)
-        e = launch_gemm_down_f8(D, hq, sh, mt, nmt, (const uint8_t *)wq_down, s_down,
-                                (bf16_t *)y_perm, s);
-    return hip_status(e);
+    return hip_status(run_ffn_fp8(D, (const bf16_t *)x_perm, offsets, (const uint8_t *)wq_gate,
+                                  s_gate, (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down,
+                                  s_down, (bf16_t *)y_perm, ws, (hipStream_t)stream));
 }
 
 moe_status moe_combine(const moe_dims *dims, const void *y_perm, const int32_t *inv_perm,

@@ -111,3 +111,56 @@ def test_fp8_ffn_matches_oracle(name):
     y2 = M.moe_expert_ffn_fp8(D, dev_bf16(xp), dev(ro.astype(np.int32)), gq, gs, uq, us, dq, ds)
     torch.cuda.synchronize()
     assert torch.equal(y[:N].view(torch.int16), y2[:N].view(torch.int16))
+
+
+LAYER_CASES = {k: FP8_CASES[k] for k in ("tiny", "ragged_T300", "local_subset_e16k4", "mixtral")}
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_fp8_layer_matches_oracle_and_staged_calls(name):
+    """moe_layer_fp8 against the oracle's route -> permute -> W8A8 FFN ->
+    combine on sampled tokens, and bit for bit against the staged C-ABI calls
+    (moe_route, moe_permute, moe_expert_ffn_fp8, moe_combine)."""
+    from gpu_util import TOL_GATE, sample_tokens
+    cfg = LAYER_CASES[name].scaled(name=name)
+    arrs = W.generate(cfg)
+    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    (gq, gs), (rgq, rgs) = _quant_both("w_gate", arrs["w_gate"])
+    (uq, us), (ruq, rus) = _quant_both("w_up", arrs["w_up"])
+    (dq, ds), (rdq, rds) = _quant_both("w_down", arrs["w_down"])
+    x, wr = dev_bf16(arrs["x"]), dev_bf16(arrs["w_router"])
+    bias = dev(arrs["bias"]) if arrs["bias"] is not None else None
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    say(f"moe_layer_fp8 {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    out = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
+                          topk_ids_out=ids, topk_w_out=gates)
+    torch.cuda.synchronize()
+    # staged calls, same kernels
+    say(f"staged fp8 calls {name}")
+    s_ids, s_gates, _ = M.moe_route(D, x, wr, bias)
+    _, offsets, _, inv, xp = M.moe_permute(D, x, s_ids)
+    y = M.moe_expert_ffn_fp8(D, xp, offsets, gq, gs, uq, us, dq, ds)
+    staged = M.moe_combine(D, y, inv, s_gates, out_dtype=dt)
+    torch.cuda.synchronize()
+    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
+    assert torch.equal(out.view(bits), staged.view(bits)), "moe_layer_fp8 != staged calls"
+    # oracle
+    r_ids, r_g = oracle.route(arrs["x"], arrs["w_router"], cfg.k, bias=arrs["bias"])
+    _, ro, rp, ri = oracle.permute(r_ids, cfg.E, cfg.e_lo, cfg.E_hi)
+    assert np.array_equal(ids.cpu().numpy(), r_ids)
+    assert np.abs(gates.cpu().numpy() - r_g).max() <= TOL_GATE
+    tokens = np.arange(cfg.T) if cfg.T <= 400 else sample_tokens(cfg.T, 24, seed=2)
+    need = np.unique(ri[tokens][ri[tokens] >= 0])
+    yref = np.zeros((max(int(ro[-1]), 1), cfg.d))
+    if need.size:
+        eor = (np.searchsorted(ro, need, side="right") - 1).astype(np.int32)
+        yref[need] = oracle.expert_rows_fp8(arrs["x"][rp[need]], eor, rgq, rgs, ruq, rus, rdq, rds)
+    ref = oracle.combine(yref, ri[tokens], gates.cpu().numpy()[tokens])
+    got = host_f32(out[torch.as_tensor(tokens, device="cuda")])
+    err = rel_err(got, ref)
+    rms = float(np.sqrt(np.mean((got - ref) ** 2) / max(np.mean(ref ** 2), 1e-300)))
+    say(f"  fp8 layer rel err {err:.3e}, rms err {rms:.3e} over {len(tokens)} tokens")
+    assert err <= TOL_FP8_TOKEN
+    assert rms <= TOL_FP8_RMS
