@@ -136,3 +136,21 @@ def test_fp8_entry_points_check_arguments_before_any_gpu_call():
     assert lib.moe_quantize_fp8(C.c_void_p(0x10002), 4, 32, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(None, 4, 32, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(None, 0, 32, None, None, None) == OK
+
+
+def test_fp8_layer_checks_arguments_before_any_gpu_call():
+    lib = M.load()
+    D = dims()
+    need = M.moe_layer_fp8_workspace_bytes(D)
+    assert need > M.moe_expert_ffn_fp8_workspace_bytes(D)
+    assert M.moe_layer_fp8_workspace_bytes(dims(f=384)) == 0
+    w = (FAKE,) * 9  # x, w_router, bias, wq_gate, s_gate, wq_up, s_up, wq_down, s_down
+    assert lib.moe_layer_fp8(C.byref(dims(f=384)), *w, FAKE, 0, None, None, FAKE_WS, 1 << 40,
+                             None) == UNSUPPORTED
+    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 5, None, None, FAKE_WS, 1 << 40, None) == INVALID
+    assert lib.moe_layer_fp8(C.byref(D), None, *w[1:], FAKE, 0, None, None, FAKE_WS, 1 << 40,
+                             None) == INVALID
+    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need - 1,
+                             None) == WORKSPACE
+    assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0,
+                             None) == OK
