@@ -73,6 +73,9 @@ FP8_CASES = {
                                                    e_hi=11, out_fp32=True, seed=4),
     "e128k8": W.CONFIGS["tiny"].scaled(T=160, d=256, f=256, E=128, k=8, seed=7),
     "multi_tile_rows": W.CONFIGS["tiny"].scaled(T=1000, d=256, f=256, E=4, k=2, seed=10),
+    "k_equals_E": W.CONFIGS["tiny"].scaled(T=64, d=256, f=256, E=4, k=4, seed=5),
+    "single_expert": W.CONFIGS["tiny"].scaled(T=77, d=256, f=256, E=1, k=1, seed=8),
+    "one_token": W.CONFIGS["tiny"].scaled(T=1, d=256, f=256, E=8, k=2, seed=9),
     "mixtral": W.CONFIGS["mixtral"],
 }
 
@@ -164,3 +167,21 @@ def test_fp8_layer_matches_oracle_and_staged_calls(name):
     say(f"  fp8 layer rel err {err:.3e}, rms err {rms:.3e} over {len(tokens)} tokens")
     assert err <= TOL_FP8_TOKEN
     assert rms <= TOL_FP8_RMS
+
+
+def test_fp8_layer_no_local_rows_gives_exact_zeros():
+    """Every token routed away from the local experts: no rows, zero output."""
+    cfg = W.CONFIGS["tiny"].scaled(T=96, d=256, f=256, E=8, k=2, e_lo=4, e_hi=8, out_fp32=True,
+                                   seed=12, name="fp8_no_local")
+    arrs = W.generate(cfg)
+    bias = np.zeros(cfg.E, np.float32)
+    bias[:2] = 1000.0  # experts 0 and 1 win every token; both are remote
+    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
+    (gq, gs), _ = _quant_both("w_gate", arrs["w_gate"])
+    (uq, us), _ = _quant_both("w_up", arrs["w_up"])
+    (dq, ds), _ = _quant_both("w_down", arrs["w_down"])
+    say("moe_layer_fp8 no local rows")
+    out = M.moe_layer_fp8(D, dev_bf16(arrs["x"]), dev_bf16(arrs["w_router"]), gq, gs, uq, us, dq,
+                          ds, bias=dev(bias), out_dtype=M.MOE_F32)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
