@@ -189,6 +189,12 @@ __global__ __launch_bounds__(RT_THREADS) void route_exact_kernel(
 // Chunk c of a staged row starts at c * (chunk bytes + 16): the 16-byte
 // stagger puts the 16 chunk lanes' reads of one step in distinct banks.
 __host__ __device__ __forceinline__ int64_t stag_pitch(int64_t d) { return 16 * (d / 16 * 2 + 16); }
+// LDS of one refine wave: staged x_t, then candidate ids and exact logits
+// (E of each), rounded up to 16 bytes so every wave's x_t stays 16-byte
+// aligned whatever E is.
+__host__ __device__ __forceinline__ int64_t refine_per_wave(int64_t d, int64_t E) {
+    return stag_pitch(d) + ((E * 8 + 15) & ~(int64_t)15);
+}
 
 template <int EP>
 __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
 
     const int64_t dc = d / 16, ppc = dc / 8;
     const int64_t cbs = dc * 2 + 16;
-    const int64_t per_wave = stag_pitch(d) + E * 8;
+    const int64_t per_wave = refine_per_wave(d, E);
     char *xs = smem + wave * per_wave;                          // staged x_t
     int32_t *cand = reinterpret_cast<int32_t *>(xs + stag_pitch(d));  // [E]
     float *exact = reinterpret_cast<float *>(cand + E);                // [E]
@@ -733,7 +739,7 @@ int route_splits(const Dims &D) {
 }
 
 bool route_uses_fast_path(const Dims &D) {
-    return D.E > 16 && (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8) <= 150 * 1024;
+    return D.E > 16 && (size_t)RF_WAVES * refine_per_wave(D.d, D.E) <= 150 * 1024;
 }
 
 static int tok_ep(const Dims &D) { return D.E <= 8 ? 8 : 16; }
@@ -811,7 +817,7 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
     hipLaunchKernelGGL(route_gemm_kernel, dim3((unsigned)tiles), dim3(GEMM_THREADS), GEMM_LDS_BYTES,
                        s, D.T, D.d, D.E, S, x, w_router, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds = (size_t)RF_WAVES * (stag_pitch(D.d) + D.E * 8);
+    const size_t lds = (size_t)RF_WAVES * refine_per_wave(D.d, D.E);
     auto refine = [&](auto rk) -> hipError_t {
         constexpr int R = decltype(rk)::value;
         hipError_t er = hipFuncSetAttribute((const void *)route_refine_kernel<R>,

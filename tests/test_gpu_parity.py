@@ -41,6 +41,8 @@ SMALL = {
     "e1024k64": W.CONFIGS["tiny"].scaled(T=40, d=256, f=128, E=1024, k=64, seed=14),
     "e256k8_local": W.CONFIGS["tiny"].scaled(T=700, d=1024, f=128, E=256, k=8, e_lo=32,
                                              e_hi=64, out_fp32=True, seed=15),
+    # odd E above 16: the refine kernel's per-wave LDS regions must stay aligned
+    "e17k3": W.CONFIGS["tiny"].scaled(T=150, d=256, f=128, E=17, k=3, seed=16),
 }
 
 
