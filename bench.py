@@ -172,6 +172,8 @@ def main() -> None:
                     choices=["layer", "copy", "ffn_fp8", "ffn_bf16", "layer_fp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w8a8", action="store_true",
+                    help="skip the extra W8A8 layer measurement of the default mode")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
                     help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
     args = ap.parse_args()
@@ -278,6 +280,26 @@ def main() -> None:
                      "kernel": "layer_kernel (persistent gate/up, down, combine tiles)",
                      "algorithmic_flops_per_launch": flops},
     }
+    if not args.no_w8a8 and cfg.f % 256 == 0:
+        # the same workload through moe_layer_fp8 (weights quantised once,
+        # outside the timed steps); reported beside the bf16 line, not as it
+        print("[bench] W8A8 layer", file=sys.stderr, flush=True)
+        (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
+        ws8 = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+        step8 = lambda: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
+                                        out_dtype=dt, ws=ws8)
+        for _ in range(args.warmup):
+            step8()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step8()
+        torch.cuda.synchronize()
+        el8 = time.perf_counter() - t0
+        rec["w8a8_layer"] = {"value": round(cfg.T * args.steps / el8, 1), "unit": "tokens/s",
+                             "ms_per_step": round(el8 / args.steps * 1e3, 4),
+                             "dtype": "fp8_e4m3", "entry_point": "moe_layer_fp8 (staged)"}
+        del ws8, gq, uq, dq
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_tokens} tokens)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, arrs, args.cpu_tokens)
