@@ -174,6 +174,8 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true",
                     help="skip the extra W8A8 layer measurement of the default mode")
+    ap.add_argument("--tile-order", type=int, default=0, choices=[0, 1],
+                    help="moe_layer persistent-kernel tile order: 0 by kind, 1 interleaved")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
                     help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
     args = ap.parse_args()
@@ -209,6 +211,7 @@ def main() -> None:
         layer_fp8_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
         return
     M.moe_set_gather_dispatch(args.dispatch == "gather")
+    M.moe_set_tile_order(args.tile_order)
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
@@ -267,7 +270,7 @@ def main() -> None:
         "data": "synthetic (seeded Gaussian activations and weights, Gaussian router)",
         "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi],
-                   "dispatch": args.dispatch,
+                   "dispatch": args.dispatch, "tile_order": args.tile_order,
                    "parallelism": "none (one GPU)"},
         "grouped_gemm_tflops": round(ffn_tflops, 2),
         "grouped_gemm_pct_mfma_peak": round(100 * ffn_tflops / PEAK_BF16_TFLOPS, 2),

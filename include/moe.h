@@ -258,6 +258,18 @@ void moe_set_wait_timeout_us(int64_t us);
  * thread-safe with concurrent moe_layer calls. */
 void moe_set_gather_dispatch(int on);
 
+/* Tile order of moe_layer's persistent kernel (process-wide; default 0).
+ *   0  by kind: every workgroup claims gate/up tiles until none are left,
+ *      then down tiles (waiting on their m-tile's gate/up tiles), then
+ *      combine tiles -- Weave §4's claiming in dependency order;
+ *   1  interleaved (X-Stage §4.3, ready-only form): before each gate/up
+ *      claim a workgroup takes the next down tile of its XCD's range when
+ *      every gate/up tile of that tile's m-tile is already published.
+ * Both orders run the same tiles with the same arithmetic: the output bits
+ * are identical.  Returns MOE_OK, or MOE_ERR_INVALID_ARG for another value.
+ * Not thread-safe with concurrent moe_layer calls. */
+int moe_set_tile_order(int policy);
+
 #ifdef __cplusplus
 }
 #endif

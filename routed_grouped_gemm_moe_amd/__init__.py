@@ -92,6 +92,7 @@ def load():
         "moe_timing_read": ([C.POINTER(C.c_float), i32], i32),
         "moe_set_wait_timeout_us": ([i64], None),
         "moe_set_gather_dispatch": ([i32], None),
+        "moe_set_tile_order": ([i32], i32),
         "moe_set_trace": ([vp, i64], None),
         "moe_wall_clock_hz": ([], i64),
     }
@@ -396,6 +397,12 @@ def moe_set_wait_timeout_us(us: int) -> None:
 def moe_set_gather_dispatch(on: bool = True) -> None:
     """moe_layer dispatch mode: gather rows of x on load (True) or packed x_perm (False)."""
     load().moe_set_gather_dispatch(1 if on else 0)
+
+
+def moe_set_tile_order(policy: int = 0) -> None:
+    """Persistent-kernel tile order of moe_layer: 0 by kind, 1 interleaved
+    (ready down tiles between gate/up tiles).  Same output bits."""
+    _check(load().moe_set_tile_order(int(policy)), "moe_set_tile_order")
 
 
 def moe_set_trace(buf=None, n_records: int = 0) -> None:

@@ -18,6 +18,11 @@
 // GEMM tiles are those of gemm_pa.h: x_perm and h are in its packed layout
 // (h written by the gate/up epilogue, read as the down tiles' A operand).
 //
+// Interleaved order (moe_set_tile_order(1)): before each gate/up claim a
+// workgroup takes the next down tile of its XCD's range if that tile's m-tile
+// has all its gate/up tiles published (compare-and-swap, so only a ready
+// tile is taken); such a tile never waits, so the argument below holds.
+//
 // Queues: gate/up and down tiles follow the blocked order of gemm_tile.h and
 // each kind is split into 8 contiguous ranges, one per XCD.  A workgroup reads
 // the XCD it runs on from the hardware (XCC_ID), drains that XCD's range
@@ -84,6 +89,33 @@ __device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd) {
         if (old < len) return lo + old;
     }
     return -1;
+}
+
+// Interleaved order (X-Stage §4.3, in its ready-only form): the next down
+// claim of this XCD's range, taken only if that tile's m-tile has every
+// gate/up tile published -- so the down tile never waits on gate/up work that
+// may not be claimed yet.  Compare-and-swap on the range's counter (lane 0
+// swaps cur -> cur + 1, the other lanes cur -> cur, which never changes it);
+// -1 if the range is drained, the tile is not ready, or another workgroup
+// claimed first.
+__device__ __forceinline__ int claim_ready_down(const LayerArgs &a, int32_t *q, int n, int n2,
+                                                int nsp, int S, int MT, int NT1, int NT2,
+                                                int xcd) {
+    const int per = (n + NUM_XCD - 1) / NUM_XCD;
+    const int lo = xcd * per;
+    const int len = min(n, lo + per) - lo;
+    if (len <= 0) return -1;
+    int32_t *c = q + xcd * QSTRIDE;
+    const int cur = uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (cur >= len) return -1;
+    int L, part, st, mt, nt;
+    dn_claim(lo + cur, n2, nsp, S, &L, &part, &st);
+    blocked_tile(L, MT, NT2, &mt, &nt);
+    if (uniform(__hip_atomic_load(a.gu_done + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+        NT1)
+        return -1;
+    const int old = uniform(atomicCAS(c, cur, lane_id() == 0 ? cur + 1 : cur));
+    return old == cur ? lo + cur : -1;
 }
 
 __device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim) {
@@ -160,6 +192,49 @@ __device__ __forceinline__ void trace_tile(const LayerArgs &a, int kind, int L, 
     }
 }
 
+// One down claim LS (a whole tile or a K part of a cut tile): wait until its
+// m-tile's gate/up tiles are published, GEMM1 into y, publish dn_flag.
+__device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, int nsp, int S,
+                                          int MT, int NT1, int NT2, int xcd, char *lds) {
+    const Dims &D = a.D;
+    const int64_t d = D.d, f = D.f;
+    const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+    int L, part, st;
+    dn_claim(LS, n2, nsp, S, &L, &part, &st);
+    int mt, nt;
+    blocked_tile(L, MT, NT2, &mt, &nt);
+    const MTile t = a.mtiles[mt];
+    if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
+    __syncthreads();
+    const int producers =
+        uniform(__hip_atomic_load(a.gu_xcd + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (producers & ~(1 << xcd))
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    else
+        invalidate_l1();
+    const int64_t prb = t.prow0 / 32;
+    // a cut tile computes K part `part`, starting at k = part * f / S
+    const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
+    const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
+    const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
+                      S};
+    const bool wrote = gemm_tile_pa<PA_BF16>(
+        a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
+        nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
+        part < 0 ? nullptr : &sc);
+    if (!wrote) {  // the last part to arrive writes the tile
+        trace_tile(a, 4, LS, xcd, t0);
+        return;
+    }
+    publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
+    // count published down tiles (after the release above, so a
+    // reader that sees the full count also sees every y row)
+    if (wave_id() == 0)
+        __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    trace_tile(a, part < 0 ? 2 : 4, LS, xcd, t0);
+}
+
 template <bool OUT_F32>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -171,12 +246,52 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
     const int NT2 = (int)D.nt_dn();
     const int64_t d = D.d, f = D.f, k = D.k;
 
-    // 1. gate/up tiles
+    // down claims: those of the last partial round (of gridDim.x workgroups)
+    // are cut into S K parts, claimed after the whole tiles
+    const int n2 = MT * NT2;
+    const int S = (int)D.dn_parts();
+    const int nsp = dn_split_tiles(S, n2, (int)gridDim.x);
+    const int n2c = n2 + (S - 1) * nsp;
+
+    // 1. gate/up tiles, then 2. down tiles, in one claim loop (so each tile
+    // body is instantiated once).  Phase 1 claims gate/up tiles -- with the
+    // interleaved order a ready down tile of this XCD's range first (kind bit
+    // 1 << 30) -- and phase 2, once every gate/up range is drained, the
+    // remaining down claims.
     const int n1 = MT * NT1;
-    if (n1 > 0)
+    constexpr int DOWN = 1 << 30;
+    int phase = n1 > 0 ? 1 : 2;
+    if (n1 > 0 || n2 > 0)
         for (;;) {
-            const int L = next_tile(a.queues, n1, xcd, &s_claim);
-            if (L < 0) break;
+            if (wave_id() == 0) {
+                int v;
+                if (phase == 1) {
+                    const int r = a.interleave && n2 > 0
+                                      ? claim_ready_down(a, a.queues + NUM_XCD * QSTRIDE, n2c, n2,
+                                                         nsp, S, MT, NT1, NT2, xcd)
+                                      : -1;
+                    v = r >= 0 ? (r | DOWN) : claim_tile(a.queues, n1, xcd);
+                    if (v < 0) v = -2;  // gate/up drained: move to phase 2
+                } else {
+                    const int r =
+                        n2 > 0 ? claim_tile(a.queues + NUM_XCD * QSTRIDE, n2c, xcd) : -1;
+                    v = r >= 0 ? (r | DOWN) : -1;
+                }
+                s_claim = v;  // every lane stores the same value
+            }
+            __syncthreads();
+            const int v = uniform(s_claim);
+            __syncthreads();
+            if (v == -2) {
+                phase = 2;
+                continue;
+            }
+            if (v < 0) break;
+            if (v & DOWN) {
+                down_tile(a, v & ~DOWN, n2, nsp, S, MT, NT1, NT2, xcd, lds);
+                continue;
+            }
+            const int L = v;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             int mt, nt;
             blocked_tile(L, MT, NT1, &mt, &nt);
@@ -194,53 +309,6 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                                              lds);
             publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
             trace_tile(a, 1, L, xcd, t0);
-        }
-
-    // 2. down tiles; those of the last partial round (of gridDim.x
-    // workgroups) are cut into S K parts, claimed after the whole tiles
-    const int n2 = MT * NT2;
-    const int S = (int)D.dn_parts();
-    const int nsp = dn_split_tiles(S, n2, (int)gridDim.x);
-    if (n2 > 0)
-        for (;;) {
-            const int LS =
-                next_tile(a.queues + NUM_XCD * QSTRIDE, n2 + (S - 1) * nsp, xcd, &s_claim);
-            if (LS < 0) break;
-            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
-            int L, part, st;
-            dn_claim(LS, n2, nsp, S, &L, &part, &st);
-            int mt, nt;
-            blocked_tile(L, MT, NT2, &mt, &nt);
-            const MTile t = a.mtiles[mt];
-            if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
-            __syncthreads();
-            const int producers =
-                uniform(__hip_atomic_load(a.gu_xcd + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            if (producers & ~(1 << xcd))
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            else
-                invalidate_l1();
-            const int64_t prb = t.prow0 / 32;
-            // a cut tile computes K part `part`, starting at k = part * f / S
-            const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
-            const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
-            const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
-                              S};
-            const bool wrote = gemm_tile_pa<PA_BF16>(
-                a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
-                nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
-                part < 0 ? nullptr : &sc);
-            if (!wrote) {  // the last part to arrive writes the tile
-                trace_tile(a, 4, LS, xcd, t0);
-                continue;
-            }
-            publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
-            // count published down tiles (after the release above, so a
-            // reader that sees the full count also sees every y row)
-            if (wave_id() == 0)
-                __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            trace_tile(a, part < 0 ? 2 : 4, LS, xcd, t0);
         }
 
     // 3. combine tiles

@@ -69,6 +69,7 @@ int64_t *g_trace = nullptr;   // per-tile trace buffer of moe_layer (device), or
 int64_t g_trace_cap = 0;
 bool g_timing = false;
 bool g_gather = false;  // gather-on-load dispatch in moe_layer
+int g_tile_order = 0;   // persistent-kernel tile order of moe_layer
 struct CallEvents {
     hipEvent_t ev[4];
 };
@@ -429,6 +430,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
     int64_t wait_us;
     CallEvents ce{};
     bool timing, gather;
+    int tile_order;
     int64_t *trace;
     int64_t trace_cap;
     {
@@ -437,6 +439,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         timing = g_timing;
         // 32-bit buffer offsets address x in gather mode
         gather = g_gather && D.T * D.d * 2 < ((int64_t)1 << 31);
+        tile_order = g_tile_order;
         trace = g_trace;
         trace_cap = g_trace_cap;
         if (timing)
@@ -474,6 +477,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.D = D;
         a.x_perm = x_perm;
         a.gather = gather ? 1 : 0;
+        a.interleave = tile_order;
         a.x = (const bf16_t *)x;
         a.perm_src = at<int32_t>(ws, L.perm_src);
         a.w_gate = (const bf16_t *)w_gate;
@@ -568,6 +572,13 @@ void moe_set_trace(void *buf, int64_t n_records) {
 }
 
 int64_t moe_wall_clock_hz(void) { return wall_clock_hz(); }
+
+int moe_set_tile_order(int policy) {
+    if (policy != 0 && policy != 1) return MOE_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_tile_order = policy;
+    return MOE_OK;
+}
 
 void moe_set_gather_dispatch(int on) {
     std::lock_guard<std::mutex> lk(g_mu);

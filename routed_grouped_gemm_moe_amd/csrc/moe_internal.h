@@ -223,6 +223,9 @@ struct LayerArgs {
     // gather-on-load dispatch: gate/up tiles read their rows of x through
     // perm_src (x_perm is not written); 0 = packed x_perm from the permute
     int gather;
+    // tile order: 0 = by kind (gate/up, then down), 1 = ready down tiles of
+    // the own XCD's range taken between gate/up tiles
+    int interleave;
     const bf16_t *x;
     const int32_t *perm_src;
     bf16_t *h, *y;

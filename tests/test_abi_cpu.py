@@ -154,3 +154,11 @@ def test_fp8_layer_checks_arguments_before_any_gpu_call():
                              None) == WORKSPACE
     assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0,
                              None) == OK
+
+
+def test_tile_order_values():
+    lib = M.load()
+    assert lib.moe_set_tile_order(2) == INVALID
+    assert lib.moe_set_tile_order(-1) == INVALID
+    assert lib.moe_set_tile_order(1) == OK
+    assert lib.moe_set_tile_order(0) == OK

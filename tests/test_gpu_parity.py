@@ -362,3 +362,31 @@ def test_gather_on_load_dispatch(name):
     assert err <= TOL_LAYER
     del t
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["tiny", "local_subset_e16k4", "e128k8", "mixtral"])
+def test_interleaved_tile_order_same_bits(name):
+    """moe_set_tile_order(1) takes ready down tiles between gate/up tiles; the
+    tiles and their arithmetic are unchanged, so the output bits are too."""
+    cfg = (SMALL[name] if name in SMALL else W.CONFIGS[name]).scaled(name=name)
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    D = _dims(cfg)
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    say(f"moe_layer tile order 0 {name}")
+    ref = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
+                      out_dtype=dt, ws=ws)
+    torch.cuda.synchronize()
+    try:
+        M.moe_set_tile_order(1)
+        ws.fill_(0xFF)
+        say(f"moe_layer tile order 1 {name}")
+        out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
+                          t["bias"], out_dtype=dt, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        M.moe_set_tile_order(0)
+    assert M.moe_device_status(D, ws) == 0
+    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
+    assert torch.equal(out.view(bits), ref.view(bits))
