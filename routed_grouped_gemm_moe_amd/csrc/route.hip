@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
     float acc[RT_EG];
 #pragma unroll
     for (int e = 0; e < RT_EG; ++e) acc[e] = 0.0f;
-    constexpr int PG = 16;  // activation vectors per prefetch group
+    constexpr int PG = 4;  // activation vectors per prefetch group (4 measured best of 2..16)
     u32x4_t xa[PG], xb[PG];
     auto load = [&](u32x4_t (&r)[PG], int b) {
 #pragma unroll
