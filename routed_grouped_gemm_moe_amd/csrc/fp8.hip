@@ -167,8 +167,9 @@ __device__ __forceinline__ int xcd_tile_f8(int n) {
 // [cap][d].
 template <bool GATE_UP>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
-    int64_t d, int64_t f, const uint8_t *__restrict__ A, const float *__restrict__ sa,
+    int64_t d, int64_t f, int64_t EL, const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
+    const int32_t *__restrict__ mtile_base,
     const uint8_t *__restrict__ W0, const float *__restrict__ s0, const uint8_t *__restrict__ W1,
     const float *__restrict__ s1, bf16_t *__restrict__ out, uint32_t *__restrict__ rowmax) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
     const int L = xcd_tile_f8(MT * NT);
     if (L < 0) return;
     int mt, nt;
-    blocked_tile(L, MT, NT, &mt, &nt);
+    expert_tile(L, MT, NT, (int)EL, mtiles, mtile_base, &mt, &nt);
     const MTile t = mtiles[mt];
     const int64_t prb = t.prow0 / 32;
     if (GATE_UP) {
@@ -196,7 +197,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
 
 template <bool GATE_UP>
 hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, const MTile *mtiles,
-                          const int32_t *n_mtiles, const uint8_t *W0, const float *s0,
+                          const int32_t *n_mtiles, const int32_t *mtile_base, const uint8_t *W0,
+                          const float *s0,
                           const uint8_t *W1, const float *s1, bf16_t *out, uint32_t *rowmax,
                           hipStream_t s) {
     const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
@@ -207,7 +209,8 @@ hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, cons
                                        hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_f8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       PA_LDS_BYTES, s, D.d, D.f, A, sa, mtiles, n_mtiles, W0, s0, W1, s1, out,
+                       PA_LDS_BYTES, s, D.d, D.f, D.EL(), A, sa, mtiles, n_mtiles, mtile_base, W0,
+                       s0, W1, s1, out,
                        rowmax);
     return hipGetLastError();
 }
@@ -242,16 +245,19 @@ hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const 
 
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
-                                  const uint8_t *wg, const float *sg, const uint8_t *wu,
-                                  const float *su, bf16_t *h, uint32_t *hmax, hipStream_t s) {
-    return launch_gemm_f8<true>(D, xq, sx, mtiles, n_mtiles, wg, sg, wu, su, h, hmax, s);
+                                  const int32_t *mtile_base, const uint8_t *wg, const float *sg,
+                                  const uint8_t *wu, const float *su, bf16_t *h, uint32_t *hmax,
+                                  hipStream_t s) {
+    return launch_gemm_f8<true>(D, xq, sx, mtiles, n_mtiles, mtile_base, wg, sg, wu, su, h, hmax,
+                                s);
 }
 
 hipError_t launch_gemm_down_f8(const Dims &D, const uint8_t *hq, const float *sh,
-                               const MTile *mtiles, const int32_t *n_mtiles, const uint8_t *wd,
-                               const float *sd, bf16_t *y, hipStream_t s) {
-    return launch_gemm_f8<false>(D, hq, sh, mtiles, n_mtiles, wd, sd, nullptr, nullptr, y, nullptr,
-                                 s);
+                               const MTile *mtiles, const int32_t *n_mtiles,
+                               const int32_t *mtile_base, const uint8_t *wd, const float *sd,
+                               bf16_t *y, hipStream_t s) {
+    return launch_gemm_f8<false>(D, hq, sh, mtiles, n_mtiles, mtile_base, wd, sd, nullptr, nullptr,
+                                 y, nullptr, s);
 }
 
 }  // namespace moe

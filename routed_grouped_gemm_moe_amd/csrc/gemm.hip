@@ -6,9 +6,11 @@
 // result reaches the kernel as a parameter).
 //
 // Launch shape: one workgroup per (m-tile, n-tile), grid sized for the worst
-// case and surplus workgroups exit at once.  Tiles follow the blocked order
-// of gemm_tile.h (groups of 4 m-tiles swept n-tile-major, so the tiles in
-// flight share weight and activation tiles) and each of the 8 XCDs takes one
+// case and surplus workgroups exit at once.  Tiles follow the expert-aligned
+// blocked order of gemm_tile.h (groups of up to 8 m-tiles of one expert swept
+// n-tile-major, so the tiles in flight share weight and activation tiles --
+// the same order as the persistent kernel, which fixes which down tiles are
+// cut) and each of the 8 XCDs takes one
 // contiguous eighth of that order: workgroup b runs on XCD b % 8 (round-robin
 // dispatch), so the workgroups sharing a tile meet in one XCD's L2.
 #include <algorithm>
@@ -86,8 +88,9 @@ struct DownSplit {
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
-    int64_t d, int64_t f, const bf16_t *__restrict__ A, const MTile *__restrict__ mtiles,
-    const int32_t *__restrict__ n_mtiles, const bf16_t *__restrict__ W0,
+    int64_t d, int64_t f, int64_t EL, const bf16_t *__restrict__ A,
+    const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
+    const int32_t *__restrict__ mtile_base, const bf16_t *__restrict__ W0,
     const bf16_t *__restrict__ W1, bf16_t *__restrict__ out, DownSplit ds) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int MT = *n_mtiles;
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     int L, part, st;
     dn_claim(LS, MT * NT, nsp, S, &L, &part, &st);
     int mt, nt;
-    blocked_tile(L, MT, NT, &mt, &nt);
+    expert_tile(L, MT, NT, (int)EL, mtiles, mtile_base, &mt, &nt);
     const MTile t = mtiles[mt];
     const int64_t prb = t.prow0 / 32;  // first packed row block
     if (GATE_UP) {
@@ -120,8 +123,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
 
 template <bool GATE_UP>
 hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, const int32_t *n_mtiles,
-                       const bf16_t *W0, const bf16_t *W1, bf16_t *out, const DownSplit &ds,
-                       hipStream_t s) {
+                       const int32_t *mtile_base, const bf16_t *W0, const bf16_t *W1, bf16_t *out,
+                       const DownSplit &ds, hipStream_t s) {
     const int64_t NT = GATE_UP ? D.nt_gu() : D.nt_dn();
     int64_t grid = D.max_mtiles() * NT;
     if (!GATE_UP && D.dn_parts() > 1)  // extra claims of the cut tiles' parts
@@ -132,7 +135,8 @@ hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, cons
                                        hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       GEMM_LDS_BYTES, s, D.d, D.f, A, mtiles, n_mtiles, W0, W1, out, ds);
+                       GEMM_LDS_BYTES, s, D.d, D.f, D.EL(), A, mtiles, n_mtiles, mtile_base, W0, W1,
+                       out, ds);
     return hipGetLastError();
 }
 
@@ -148,15 +152,16 @@ hipError_t launch_build_mtiles(const Dims &D, const int32_t *offsets, MTile *mti
 }
 
 hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
-                               const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
-                               bf16_t *h, hipStream_t s) {
-    return launch_gemm<true>(D, xp, mtiles, n_mtiles, w_gate, w_up, h, DownSplit{}, s);
+                               const int32_t *n_mtiles, const int32_t *mtile_base,
+                               const bf16_t *w_gate, const bf16_t *w_up, bf16_t *h, hipStream_t s) {
+    return launch_gemm<true>(D, xp, mtiles, n_mtiles, mtile_base, w_gate, w_up, h, DownSplit{}, s);
 }
 
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
-                            const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
-                            int32_t *dn_cnt, float *dn_part, int grid, hipStream_t s) {
-    return launch_gemm<false>(D, h, mtiles, n_mtiles, w_down, nullptr, y,
+                            const int32_t *n_mtiles, const int32_t *mtile_base,
+                            const bf16_t *w_down, bf16_t *y, int32_t *dn_cnt, float *dn_part,
+                            int grid, hipStream_t s) {
+    return launch_gemm<false>(D, h, mtiles, n_mtiles, mtile_base, w_down, nullptr, y,
                               DownSplit{dn_cnt, dn_part, grid}, s);
 }
 

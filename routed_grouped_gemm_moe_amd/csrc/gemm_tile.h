@@ -93,6 +93,30 @@ __host__ __device__ __forceinline__ void blocked_tile(int L, int MT, int NT, int
     *mt = g * GM_GROUP + (r - *nt * s);
 }
 
+// Expert-aligned blocked order of the expert GEMMs: the m-tiles of one
+// expert form groups of at most GM_MAX, each group swept n-tile-major, so
+// the m-tiles that read the same weight tile are claimed one after another
+// (and run side by side in one XCD's L2); groups never mix experts, whose
+// weights differ.  L in [0, MT*NT) -> (m-tile, n-tile).  mtiles[m].e is the
+// local expert of m-tile m, mtile_base[e] the first m-tile of expert e (EL
+// local experts, MT m-tiles in all).  A group covers m-tiles [g0, g0 + s)
+// and claims [g0*NT, (g0 + s)*NT), so L / NT names an m-tile of its group.
+constexpr int GM_MAX = 8;
+__host__ __device__ __forceinline__ void expert_tile(int L, int MT, int NT, int EL,
+                                                     const MTile *mtiles,
+                                                     const int32_t *mtile_base, int *mt,
+                                                     int *nt) {
+    const int m0 = L / NT;
+    const int e = mtiles[m0].e;
+    const int base = mtile_base[e];
+    const int end = e + 1 < EL ? mtile_base[e + 1] : MT;
+    const int g0 = base + (m0 - base) / GM_MAX * GM_MAX;
+    const int s = min(GM_MAX, end - g0);
+    const int r = L - g0 * NT;
+    *nt = r / s;
+    *mt = g0 + (r - *nt * s);
+}
+
 // Epilogues: h = silu(g) * u as bf16 (gate/up, dual B) in rows or in the
 // packed fragment layout of gemm_pa.h, y as bf16 (down), or the raw float32
 // accumulators (router logit partials; columns >= out_cols are not stored).

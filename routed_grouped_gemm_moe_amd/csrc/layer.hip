@@ -110,7 +110,7 @@ __device__ __forceinline__ int claim_ready_down(const LayerArgs &a, int32_t *q, 
     if (cur >= len) return -1;
     int L, part, st, mt, nt;
     dn_claim(lo + cur, n2, nsp, S, &L, &part, &st);
-    blocked_tile(L, MT, NT2, &mt, &nt);
+    expert_tile(L, MT, NT2, (int)a.D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
     if (uniform(__hip_atomic_load(a.gu_done + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
         NT1)
         return -1;
@@ -202,7 +202,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
     int L, part, st;
     dn_claim(LS, n2, nsp, S, &L, &part, &st);
     int mt, nt;
-    blocked_tile(L, MT, NT2, &mt, &nt);
+    expert_tile(L, MT, NT2, (int)a.D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
     const MTile t = a.mtiles[mt];
     if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
     __syncthreads();
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             const int L = v;
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             int mt, nt;
-            blocked_tile(L, MT, NT1, &mt, &nt);
+            expert_tile(L, MT, NT1, (int)D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
             const MTile t = a.mtiles[mt];
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
             const int64_t prb = t.prow0 / 32;  // first packed row block

@@ -204,9 +204,11 @@ moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_
                                        at<int32_t>(ws, L.status), clear_ints, s);
     if (e == hipSuccess) e = launch_pack_rows(D, (const bf16_t *)x_perm, offsets, pstart, xp, s);
     if (e == hipSuccess)
-        e = launch_gemm_gate_up(D, xp, mt, nmt, (const bf16_t *)w_gate, (const bf16_t *)w_up, h, s);
+        e = launch_gemm_gate_up(D, xp, mt, nmt, at<int32_t>(ws, L.mtile_base),
+                                (const bf16_t *)w_gate, (const bf16_t *)w_up, h, s);
     if (e == hipSuccess)
-        e = launch_gemm_down(D, h, mt, nmt, (const bf16_t *)w_down, (bf16_t *)y_perm,
+        e = launch_gemm_down(D, h, mt, nmt, at<int32_t>(ws, L.mtile_base),
+                             (const bf16_t *)w_down, (bf16_t *)y_perm,
                              at<int32_t>(ws, L.dn_cnt), at<float>(ws, L.dn_part), layer_grid_size(),
                              s);
     return hip_status(e);
@@ -278,11 +280,14 @@ hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offse
         e = launch_quant_pack(D, D.d, x_perm, offsets, pstart, at<float>(ws, L.amax), false, xq, sx,
                               s);
     if (e == hipSuccess)
-        e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, wq_gate, s_gate, wq_up, s_up, h,
+        e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, at<int32_t>(ws, L.mtile_base), wq_gate,
+                                   s_gate, wq_up, s_up, h,
                                    at<uint32_t>(ws, L.hmax), s);
     if (e == hipSuccess)
         e = launch_quant_pack(D, D.f, h, offsets, pstart, at<float>(ws, L.hmax), true, hq, sh, s);
-    if (e == hipSuccess) e = launch_gemm_down_f8(D, hq, sh, mt, nmt, wq_down, s_down, y_perm, s);
+    if (e == hipSuccess)
+        e = launch_gemm_down_f8(D, hq, sh, mt, nmt, at<int32_t>(ws, L.mtile_base), wq_down, s_down,
+                                y_perm, s);
     return e;
 }
 

@@ -186,14 +186,15 @@ hipError_t launch_pack_rows(const Dims &D, const bf16_t *x_perm, const int32_t *
 // Grouped GEMMs over packed activations: h (packed) from xp; y (row-major at
 // the m-tiles' row0) from h.
 hipError_t launch_gemm_gate_up(const Dims &D, const bf16_t *xp, const MTile *mtiles,
-                               const int32_t *n_mtiles, const bf16_t *w_gate, const bf16_t *w_up,
-                               bf16_t *h, hipStream_t s);
+                               const int32_t *n_mtiles, const int32_t *mtile_base,
+                               const bf16_t *w_gate, const bf16_t *w_up, bf16_t *h, hipStream_t s);
 // Cut down tiles (dn_split_tiles with G = grid) meet through dn_cnt
 // (cleared, one int per cut tile) and the float32 partials dn_part
 // (CUT_MAX x 256 KiB per cut tile).
 hipError_t launch_gemm_down(const Dims &D, const bf16_t *h, const MTile *mtiles,
-                            const int32_t *n_mtiles, const bf16_t *w_down, bf16_t *y,
-                            int32_t *dn_cnt, float *dn_part, int grid, hipStream_t s);
+                            const int32_t *n_mtiles, const int32_t *mtile_base,
+                            const bf16_t *w_down, bf16_t *y, int32_t *dn_cnt, float *dn_part,
+                            int grid, hipStream_t s);
 
 hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *inv_perm,
                           const float *gates, void *out, bool out_f32, hipStream_t s);
@@ -211,10 +212,12 @@ hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const 
                              float *scale, hipStream_t s);
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
+                                  const int32_t *mtile_base,
                                   const uint8_t *wg, const float *sg, const uint8_t *wu,
                                   const float *su, bf16_t *h, uint32_t *hmax, hipStream_t s);
 hipError_t launch_gemm_down_f8(const Dims &D, const uint8_t *hq, const float *sh,
-                               const MTile *mtiles, const int32_t *n_mtiles, const uint8_t *wd,
+                               const MTile *mtiles, const int32_t *n_mtiles,
+                               const int32_t *mtile_base, const uint8_t *wd,
                                const float *sd, bf16_t *y, hipStream_t s);
 
 struct LayerArgs {

@@ -21,3 +21,15 @@ def test_down_claim_map_is_a_bijection(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "0 violations" in out.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_expert_aligned_tile_order_is_a_bijection(tmp_path):
+    exe = tmp_path / "expert_tile_check"
+    src = os.path.join(HERE, "host", "expert_tile_check.cpp")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-O2", "-std=c++17", src, "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert " 0 violations" in out.stdout
