@@ -7,7 +7,7 @@
 //
 // Launch shape: one workgroup per (m-tile, n-tile), grid sized for the worst
 // case and surplus workgroups exit at once.  Tiles follow the expert-aligned
-// blocked order of gemm_tile.h (groups of up to 8 m-tiles of one expert swept
+// blocked order of gemm_tile.h (groups of up to 16 m-tiles of one expert swept
 // n-tile-major, so the tiles in flight share weight and activation tiles --
 // the same order as the persistent kernel, which fixes which down tiles are
 // cut) and each of the 8 XCDs takes one

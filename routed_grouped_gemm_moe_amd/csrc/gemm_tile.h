@@ -94,14 +94,14 @@ __host__ __device__ __forceinline__ void blocked_tile(int L, int MT, int NT, int
 }
 
 // Expert-aligned blocked order of the expert GEMMs: the m-tiles of one
-// expert form groups of at most GM_MAX, each group swept n-tile-major, so
+// expert form groups of at most GM_MAX (16), each group swept n-tile-major, so
 // the m-tiles that read the same weight tile are claimed one after another
 // (and run side by side in one XCD's L2); groups never mix experts, whose
 // weights differ.  L in [0, MT*NT) -> (m-tile, n-tile).  mtiles[m].e is the
 // local expert of m-tile m, mtile_base[e] the first m-tile of expert e (EL
 // local experts, MT m-tiles in all).  A group covers m-tiles [g0, g0 + s)
 // and claims [g0*NT, (g0 + s)*NT), so L / NT names an m-tile of its group.
-constexpr int GM_MAX = 8;
+constexpr int GM_MAX = 16;
 __host__ __device__ __forceinline__ void expert_tile(int L, int MT, int NT, int EL,
                                                      const MTile *mtiles,
                                                      const int32_t *mtile_base, int *mt,
