@@ -177,6 +177,24 @@ def test_degenerate_one_expert_takes_everything(hot, k):
     _check_layer(cfg, t, arrs, staged_out=staged)
 
 
+def test_expert_with_more_m_tiles_than_one_group():
+    # One expert takes all 4600 tokens: 18 m-tiles, so the expert-aligned
+    # tile order splits it into groups of 16 and 2 m-tiles.  Fused must equal
+    # staged bit for bit, and both must match the oracle.
+    cfg = W.CONFIGS["tiny"].scaled(name="hot18", T=4600, d=256, f=256, E=8, k=1, seed=19)
+    arrs = W.generate(cfg, bias_override=_bias_all_to_one(8, 2))
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    assert np.all(r_ids[:, 0] == 2)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    assert (N + 255) // 256 == 18
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=40, replace=False)]))
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N, rows=rows)
+    staged = _staged(cfg, t, y, inv, gates)
+    _check_layer(cfg, t, arrs, staged_out=staged, tokens=sample_tokens(cfg.T, 40, seed=6))
+
+
 def test_no_local_rows_gives_zero_output():
     # every token routes only to experts outside the local range
     cfg = W.CONFIGS["tiny"].scaled(name="nolocal", T=50, d=256, f=128, E=8, k=1, e_lo=0, e_hi=2,
