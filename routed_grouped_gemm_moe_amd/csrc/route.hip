@@ -770,7 +770,6 @@ static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, 
     hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3(nblk * 4 * (EP / RT_EG)), dim3(256), 0,
                        s, D.T, D.d, D.E, x, wf, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
                        part, bias, ids, gates);
     return hipGetLastError();
