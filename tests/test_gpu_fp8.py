@@ -8,10 +8,15 @@ v_mfma_f32_32x32x64_f8f6f4 is off by up to 2.8e-4 of the sum of the
 products' magnitudes (about 12-bit alignment).  That error moves a few h
 values across an E4M3 rounding boundary (about 0.2% of h codes differ from
 the oracle's), and each such code moves y by one E4M3 step of that h element
-times its weights.  Bounds: 6e-2 per token (the rel_err metric of the bf16
-path; 2.9e-2 measured at f = 1024, where one code weighs most) and 6e-3 for
-the root-mean-square error over all checked outputs (a wrong operand, scale
-or k-step gives errors of 1e-1 and more).
+times its weights.  A step is at most 2^-3 of the element; against a row of
+y, whose rms grows as sqrt(f) times the rms of h and of the weights, one
+moved code weighs about 2^-3 * (|h_j| / rms h) * (|w_ij| / rms w) / sqrt(f),
+and the two magnitude ratios together reach about 16 in the tails of these
+Gaussian inputs.  Bounds: max(6e-2, 2 / sqrt(f)) per token (the rel_err
+metric of the bf16 path; 2.9e-2 measured at f = 1024, 7.2e-2 at f = 512
+with k = 1, where no second expert's share dilutes it) and 6e-3 for the
+root-mean-square error over all checked outputs (a wrong operand, scale or
+k-step gives errors of 1e-1 and more).
 Inputs: the seeded workloads; the permutation is the oracle's own.
 """
 import numpy as np
@@ -21,8 +26,12 @@ import moe_workloads as W
 import oracle
 from gpu_util import dev, dev_bf16, host_f32, rel_err, say
 
-TOL_FP8_TOKEN = 6e-2
 TOL_FP8_RMS = 6e-3
+
+
+def tol_fp8_token(f):
+    return max(6e-2, 2.0 / np.sqrt(f))
+
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -108,7 +117,7 @@ def test_fp8_ffn_matches_oracle(name):
     err = rel_err(got, ref)
     rms = float(np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2)))
     say(f"  fp8 ffn rel err {err:.3e}, rms err {rms:.3e} over {len(rows)} rows")
-    assert err <= TOL_FP8_TOKEN
+    assert err <= tol_fp8_token(cfg.f)
     assert rms <= TOL_FP8_RMS
     # repeatable: a second call gives the same bits
     y2 = M.moe_expert_ffn_fp8(D, dev_bf16(xp), dev(ro.astype(np.int32)), gq, gs, uq, us, dq, ds)
@@ -117,6 +126,23 @@ def test_fp8_ffn_matches_oracle(name):
 
 
 LAYER_CASES = {k: FP8_CASES[k] for k in ("tiny", "ragged_T300", "local_subset_e16k4", "mixtral")}
+
+
+def _random_fp8_case(seed):
+    """A seeded shape across the W8A8 path's range (f a multiple of 256):
+    ragged T, E across both router paths, a random local expert range."""
+    g = np.random.default_rng(3000 + seed)
+    E = int(g.choice([1, 4, 8, 16, 17, 40]))
+    k = int(g.integers(1, min(E, 4) + 1))
+    e_lo = int(g.integers(0, E))
+    e_hi = int(g.integers(e_lo + 1, E + 1))
+    return W.CONFIGS["tiny"].scaled(
+        T=int(g.integers(1, 500)), d=int(g.choice([256, 512, 768])),
+        f=int(g.choice([256, 512, 768, 1280])), E=E, k=k, e_lo=e_lo, e_hi=e_hi,
+        out_fp32=bool(g.integers(0, 2)), seed=400 + seed)
+
+
+LAYER_CASES.update({f"rand{i}": _random_fp8_case(i) for i in range(6)})
 
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
@@ -165,7 +191,7 @@ def test_fp8_layer_matches_oracle_and_staged_calls(name):
     err = rel_err(got, ref)
     rms = float(np.sqrt(np.mean((got - ref) ** 2) / max(np.mean(ref ** 2), 1e-300)))
     say(f"  fp8 layer rel err {err:.3e}, rms err {rms:.3e} over {len(tokens)} tokens")
-    assert err <= TOL_FP8_TOKEN
+    assert err <= tol_fp8_token(cfg.f)
     assert rms <= TOL_FP8_RMS
 
 

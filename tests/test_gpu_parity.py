@@ -163,6 +163,33 @@ def test_small_case_all_stages(name):
     _check_layer(cfg, t, arrs, staged_out=staged)
 
 
+def _random_case(seed):
+    """A seeded shape drawn across the supported ranges: ragged T, d and f of
+    several tiles, E across both router paths, k up to 6, a random local
+    expert range and output dtype."""
+    g = np.random.default_rng(1000 + seed)
+    E = int(g.choice([1, 2, 3, 5, 8, 12, 16, 17, 24, 33, 64]))
+    k = int(g.integers(1, min(E, 6) + 1))
+    e_lo = int(g.integers(0, E))
+    e_hi = int(g.integers(e_lo + 1, E + 1))
+    return W.CONFIGS["tiny"].scaled(
+        name=f"rand{seed}", T=int(g.integers(1, 600)), d=int(g.choice([256, 512, 768, 1280])),
+        f=int(g.choice([128, 256, 384, 640, 896])), E=E, k=k, e_lo=e_lo, e_hi=e_hi,
+        out_fp32=bool(g.integers(0, 2)), seed=200 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_all_stages(seed):
+    cfg = _random_case(seed)
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N)
+    staged = _staged(cfg, t, y, inv, gates)
+    _check_layer(cfg, t, arrs, staged_out=staged)
+
+
 @pytest.mark.parametrize("hot,k", [(5, 1), (2, 2)])
 def test_degenerate_one_expert_takes_everything(hot, k):
     cfg = W.CONFIGS["tiny"].scaled(name=f"hot{hot}k{k}", T=260, d=256, f=256, E=8, k=k, seed=11)
