@@ -371,13 +371,20 @@ def test_cut_down_tiles(f, parts):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_T300", "local_subset_e16k4", "e128k8", "mixtral"])
+def _named_case(name):
+    if name.startswith("rand"):
+        return _random_case(int(name[4:]))
+    return (SMALL[name] if name in SMALL else W.CONFIGS[name]).scaled(name=name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_T300", "local_subset_e16k4", "e128k8", "mixtral",
+                                  "rand1", "rand2", "rand6", "rand9"])
 def test_gather_on_load_dispatch(name):
     # Gather-on-load dispatch: gate/up tiles fetch their rows of x through
     # perm_src (x_perm never written).  Same tile k-order as the packed path,
     # so the layer output must equal the packed-dispatch output bit for bit,
     # and match the oracle.
-    cfg = SMALL[name] if name in SMALL else W.CONFIGS[name]
+    cfg = _named_case(name)
     D = _dims(cfg)
     arrs = W.generate(cfg)
     t = upload(cfg, arrs)
@@ -409,11 +416,12 @@ def test_gather_on_load_dispatch(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["tiny", "local_subset_e16k4", "e128k8", "mixtral"])
+@pytest.mark.parametrize("name", ["tiny", "local_subset_e16k4", "e128k8", "mixtral",
+                                  "rand1", "rand2", "rand6", "rand9"])
 def test_interleaved_tile_order_same_bits(name):
     """moe_set_tile_order(1) takes ready down tiles between gate/up tiles; the
     tiles and their arithmetic are unchanged, so the output bits are too."""
-    cfg = (SMALL[name] if name in SMALL else W.CONFIGS[name]).scaled(name=name)
+    cfg = _named_case(name)
     arrs = W.generate(cfg)
     t = upload(cfg, arrs)
     D = _dims(cfg)
