@@ -326,8 +326,19 @@ __global__ __launch_bounds__(256) void route_tok_wprep_kernel(int64_t n, int64_t
 
 // Each wave takes EG of the EP experts (two or more waves per SIMD, so one
 // wave's scalar-load waits overlap another's FMAs); grid = token blocks x 4
-// chunk quads x EP/EG expert groups.
+// chunk quads x EP/EG expert groups.  Workgroups are dealt to the 8 XCDs in
+// turn, so the EP/EG expert groups of one (token block, chunk quad) unit are
+// placed 8 workgroups apart: they run on one XCD at about the same time and
+// all but the first read that unit's activations from the XCD's L2.  The
+// grid is padded to whole sets of 8 units; padding workgroups exit at once.
 constexpr int RT_EG = 4;
+
+__host__ __device__ constexpr int64_t route_tok_units(int64_t T) {
+    return 4 * ((T + RTOK - 1) / RTOK);
+}
+__host__ __device__ constexpr int64_t route_tok_grid(int64_t T, int ng) {
+    return (route_tok_units(T) + 7) / 8 * 8 * ng;
+}
 
 template <int EP>
 __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_t d, int64_t E,
@@ -338,10 +349,12 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
     constexpr int NG = EP / RT_EG;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t blk = blockIdx.x / (4 * NG);
-    const int rem = (int)(blockIdx.x % (4 * NG));
-    const int e0 = (rem / 4) * RT_EG;           // first expert of this wave
-    const int c = (rem % 4) * 4 + wave;         // chunk, wave-uniform
+    const int64_t rest = blockIdx.x / 8;
+    const int64_t unit = (rest / NG) * 8 + blockIdx.x % 8;
+    if (unit >= route_tok_units(T)) return;
+    const int64_t blk = unit / 4;
+    const int e0 = (int)(rest % NG) * RT_EG;    // first expert of this wave
+    const int c = (int)(unit % 4) * 4 + wave;   // chunk, wave-uniform
     const int64_t t = blk * RTOK + lane;
     const int64_t dc = d / 16;
     const int nvec = (int)(dc / 8);  // 16-byte activation vectors per chunk
@@ -767,7 +780,8 @@ static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, 
                        0, s, n, n_pad, w, wf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3(nblk * 4 * (EP / RT_EG)), dim3(256), 0,
+    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)),
+                       dim3(256), 0,
                        s, D.T, D.d, D.E, x, wf, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
