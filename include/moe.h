@@ -89,9 +89,10 @@ int moe_version(void);
  *   ws, ws_bytes               workspace of moe_route_workspace_bytes(dims)
  *                              bytes (256-byte aligned), or NULL
  * A workspace enables the fast paths.  E <= 16: one lane per token and one
- * wave per chunk of the hidden dimension, with the router weights (widened to
- * float32 in the workspace) as wave-uniform scalar operands, chunk sums kept
- * in the workspace and folded by a second kernel.  E > 16: MFMA logits with a
+ * wave per chunk of the hidden dimension, with the router weights as
+ * wave-uniform scalar operands (read as bf16 and widened exactly on the
+ * scalar unit), chunk sums kept in the workspace and folded by a second
+ * kernel.  E > 16: MFMA logits with a
  * rigorous rounding-error bound pick the candidate experts, whose logits are
  * then evaluated in the defined order.  Either way ids and gates are the same
  * as when every logit is evaluated in that order, which is what happens with

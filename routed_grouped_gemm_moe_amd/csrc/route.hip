@@ -301,7 +301,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
 // every expert come from scalar loads and enter the FMAs as scalar operands;
 // each lane keeps EP accumulators.  Only the activations use the vector
 // memory path (each token row read once).
-//  route_tok_wprep_kernel: W_r widened to float32 (exact), wf[e][i];
 //  route_tok_chunks_kernel: workgroup = 64 tokens x 4 chunks x 4 experts;
 //    writes the chunk sums part[blk][c][e][lane];
 //  route_tok_finish_kernel: workgroup = 64 tokens; folds the 16 chunk sums by
@@ -309,20 +308,6 @@ __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
 //    desc, id asc) and forms the gates with the same float32 operations, in
 //    the same order, as wave_topk_gates.
 constexpr int RTOK = 64;  // tokens per block (one per lane)
-
-// Rows E..EP-1 of wf are zero, so the chunk kernel runs all EP experts
-// without branches (their sums are never stored).
-__global__ __launch_bounds__(256) void route_tok_wprep_kernel(int64_t n, int64_t n_pad,
-                                                              const bf16_t *__restrict__ w,
-                                                              float *__restrict__ wf) {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8 elements each
-    if (p * 8 >= n_pad) return;
-    const u32x4_t v = p * 8 < n ? reinterpret_cast<const u32x4_t *>(w)[p] : u32x4_t{0u, 0u, 0u, 0u};
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
-    f32x4v *o = reinterpret_cast<f32x4v *>(wf) + 2 * p;
-    o[0] = f32x4v{bf16x8_elem(v, 0), bf16x8_elem(v, 1), bf16x8_elem(v, 2), bf16x8_elem(v, 3)};
-    o[1] = f32x4v{bf16x8_elem(v, 4), bf16x8_elem(v, 5), bf16x8_elem(v, 6), bf16x8_elem(v, 7)};
-}
 
 // Each wave takes EG of the EP experts (two or more waves per SIMD, so one
 // wave's scalar-load waits overlap another's FMAs); grid = token blocks x 4
@@ -343,9 +328,8 @@ __host__ __device__ constexpr int64_t route_tok_grid(int64_t T, int ng) {
 template <int EP>
 __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_t d, int64_t E,
                                                                const bf16_t *__restrict__ x,
-                                                               const float *__restrict__ wf,
+                                                               const bf16_t *__restrict__ w,
                                                                float *__restrict__ part) {
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
     constexpr int NG = EP / RT_EG;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -359,8 +343,13 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
     const int64_t dc = d / 16;
     const int nvec = (int)(dc / 8);  // 16-byte activation vectors per chunk
     const u32x4_t *xp = reinterpret_cast<const u32x4_t *>(x + (t < T ? t : T - 1) * d + c * dc);
-    const int64_t wstride = d / 4;  // float4s between experts
-    const f32x4v *wp = reinterpret_cast<const f32x4v *>(wf + c * dc) + e0 * wstride;
+    // W_r rows of this wave's experts (bf16, read by scalar loads and widened
+    // exactly by a 16-bit shift); experts E..EP-1 repeat row E-1, and their
+    // sums are never stored
+    const u32x4_t *wp[RT_EG];
+#pragma unroll
+    for (int e = 0; e < RT_EG; ++e)
+        wp[e] = reinterpret_cast<const u32x4_t *>(w + (e0 + e < E ? e0 + e : E - 1) * d + c * dc);
 
     float acc[RT_EG];
 #pragma unroll
@@ -372,35 +361,29 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
         for (int u = 0; u < PG; ++u) r[u] = (b + u < nvec) ? xp[b + u] : u32x4_t{0u, 0u, 0u, 0u};
     };
     // the weights of vector v + 1 are loaded (scalar) while vector v computes
-    f32x4v wc0[RT_EG], wc1[RT_EG], wn0[RT_EG], wn1[RT_EG];
-    auto loadw = [&](f32x4v (&w0)[RT_EG], f32x4v (&w1)[RT_EG], int v) {
+    u32x4_t wc[RT_EG], wn[RT_EG];
+    auto loadw = [&](u32x4_t (&wv)[RT_EG], int v) {
         const int vv = v < nvec ? v : nvec - 1;
 #pragma unroll
-        for (int e = 0; e < RT_EG; ++e) {
-            w0[e] = wp[e * wstride + 2 * vv];
-            w1[e] = wp[e * wstride + 2 * vv + 1];
-        }
+        for (int e = 0; e < RT_EG; ++e) wv[e] = wp[e][vv];
     };
     auto compute = [&](const u32x4_t (&r)[PG], int b) {
 #pragma unroll
         for (int u = 0; u < PG; ++u) {
             if (b + u >= nvec) break;
-            loadw(wn0, wn1, b + u + 1);
+            loadw(wn, b + u + 1);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const float xf = bf16x8_elem(r[u], q);
 #pragma unroll
                 for (int e = 0; e < RT_EG; ++e)
-                    acc[e] = __builtin_fmaf(xf, q < 4 ? wc0[e][q] : wc1[e][q - 4], acc[e]);
+                    acc[e] = __builtin_fmaf(xf, bf16x8_elem(wc[e], q), acc[e]);
             }
 #pragma unroll
-            for (int e = 0; e < RT_EG; ++e) {
-                wc0[e] = wn0[e];
-                wc1[e] = wn1[e];
-            }
+            for (int e = 0; e < RT_EG; ++e) wc[e] = wn[e];
         }
     };
-    loadw(wc0, wc1, 0);
+    loadw(wc, 0);
     load(xa, 0);
     for (int b = 0; b < nvec; b += 2 * PG) {
         if (b + PG < nvec) load(xb, b + PG);
@@ -759,9 +742,8 @@ static int tok_ep(const Dims &D) { return D.E <= 8 ? 8 : 16; }
 
 size_t route_workspace_bytes(const Dims &D) {
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    if (D.E <= 16)  // token-lane chunk sums, then W_r in float32
-        return al((size_t)((D.T + RTOK - 1) / RTOK) * 16 * tok_ep(D) * RTOK * sizeof(float)) +
-               al((size_t)tok_ep(D) * D.d * sizeof(float));
+    if (D.E <= 16)  // token-lane chunk sums
+        return al((size_t)((D.T + RTOK - 1) / RTOK) * 16 * tok_ep(D) * RTOK * sizeof(float));
     if (!route_uses_fast_path(D)) return 0;
     return al((size_t)route_splits(D) * D.T * D.E * 4) + al((size_t)D.E * D.d * 2) +
            al((size_t)D.E * 4);
@@ -772,18 +754,10 @@ static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, 
                                int32_t *ids, float *gates, void *ws, hipStream_t s) {
     const unsigned nblk = (unsigned)((D.T + RTOK - 1) / RTOK);
     float *part = reinterpret_cast<float *>(ws);
-    float *wf = reinterpret_cast<float *>(
-        reinterpret_cast<char *>(ws) +
-        (((size_t)nblk * 16 * EP * RTOK * sizeof(float) + 255) & ~(size_t)255));
-    const int64_t n = D.E * D.d, n_pad = EP * D.d;
-    hipLaunchKernelGGL(route_tok_wprep_kernel, dim3((unsigned)((n_pad / 8 + 255) / 256)), dim3(256),
-                       0, s, n, n_pad, w, wf);
+    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)),
+                       dim3(256), 0, s, D.T, D.d, D.E, x, w, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)),
-                       dim3(256), 0,
-                       s, D.T, D.d, D.E, x, wf, part);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
                        part, bias, ids, gates);
     return hipGetLastError();
