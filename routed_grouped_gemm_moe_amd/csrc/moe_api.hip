@@ -352,13 +352,15 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
     float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
     int32_t *offsets = at<int32_t>(ws, L.offsets), *inv_perm = at<int32_t>(ws, L.inv_perm);
     bf16_t *x_perm = at<bf16_t>(ws, L.x_perm), *y = at<bf16_t>(ws, L.y);
+    bool hist_done = false;  // the router may also count the permute's histogram
     hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
-                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s);
+                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s,
+                                at<int32_t>(ws, L.blk_counts), &hist_done);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
                            at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
                            at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), nullptr,
-                           nullptr, nullptr, nullptr, nullptr, 0, s);
+                           nullptr, nullptr, nullptr, nullptr, 0, s, hist_done);
     if (e == hipSuccess)
         e = run_ffn_fp8(D, x_perm, offsets, (const uint8_t *)wq_gate, s_gate,
                         (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
@@ -467,15 +469,17 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
                     : (int64_t)((L.dn_flag - L.status) / 4) + D.max_mtiles() * D.nt_dn();
 
     mark(0);
+    bool hist_done = false;  // the router may also count the permute's histogram
     hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
-                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s);
+                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s,
+                                at<int32_t>(ws, L.blk_counts), &hist_done);
     mark(1);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
                            at<int32_t>(ws, L.perm_src), inv_perm, gather ? nullptr : x_perm,
                            at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
                            at<int32_t>(ws, L.pstart), mt, nmt, mtile_base,
-                           at<int32_t>(ws, L.status), sched_ints, s);
+                           at<int32_t>(ws, L.status), sched_ints, s, hist_done);
     mark(2);
     if (e == hipSuccess) {
         LayerArgs a;

@@ -155,24 +155,29 @@ __host__ __device__ inline T *at(void *ws, size_t off) {
 // Router.  With logits != NULL, or without a large enough workspace when the
 // fast path applies, every logit is evaluated in the defined order; otherwise
 // E <= 16 uses the LDS-staged exact kernel and E > 16 the MFMA + exact-refine
-// fast path (same ids and gates).
+// fast path (same ids and gates).  With hist_done != NULL and the E <= 16
+// token-lane path taken, the router also writes the permute's histogram
+// (blk_counts, per token block of PERM_TB tokens and local expert) and sets
+// *hist_done; otherwise *hist_done is false and blk_counts is untouched.
 size_t route_workspace_bytes(const Dims &D);
 bool route_uses_fast_path(const Dims &D);
 int route_splits(const Dims &D);
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
-                        hipStream_t s);
+                        hipStream_t s, int32_t *blk_counts = nullptr, bool *hist_done = nullptr);
 
 // Permute.  With pstart != NULL (the fused layer) x_perm is written in the
 // packed fragment layout of gemm_pa.h at the 32-aligned segment starts
 // pstart[] (not at all when x_perm is NULL: gather-on-load dispatch), and the
 // GEMM m-tile table is built and the scheduler state of the persistent kernel
-// cleared; otherwise x_perm is row-major at offsets[].
+// cleared; otherwise x_perm is row-major at offsets[].  hist_done: blk_counts
+// already holds the histogram (written by the router), so it is not recounted.
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
                           int32_t *blk_counts, int32_t *blk_base, int32_t *pstart,
                           MTile *mtiles, int32_t *n_mtiles, int32_t *mtile_base,
-                          int32_t *sched_state, int64_t sched_state_ints, hipStream_t s);
+                          int32_t *sched_state, int64_t sched_state_ints, hipStream_t s,
+                          bool hist_done = false);
 
 // Staged FFN: m-tile table and pstart[] from offsets[], then the row-major
 // x_perm repacked into xp (packed, pcap rows).

@@ -234,10 +234,10 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
                           int32_t *blk_counts, int32_t *blk_base, int32_t *pstart, MTile *mtiles,
                           int32_t *n_mtiles, int32_t *mtile_base, int32_t *sched_state,
-                          int64_t sched_state_ints, hipStream_t s) {
+                          int64_t sched_state_ints, hipStream_t s, bool hist_done) {
     const int64_t EL = D.EL(), nblk = D.perm_blocks();
     hipError_t e;
-    if (nblk > 0) {
+    if (nblk > 0 && !hist_done) {
         hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblk), dim3(PERM_TB), EL * sizeof(int32_t),
                            s, D.T, D.k, D.e_lo, EL, ids, blk_counts);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -329,10 +329,15 @@ template <int EP>
 __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_t d, int64_t E,
                                                                const bf16_t *__restrict__ x,
                                                                const bf16_t *__restrict__ w,
-                                                               float *__restrict__ part) {
+                                                               float *__restrict__ part,
+                                                               int32_t *__restrict__ hist,
+                                                               int64_t hist_n) {
     constexpr int NG = EP / RT_EG;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the permute's histogram, filled by the finish kernel, starts at zero
+    if (hist && blockIdx.x == 0)
+        for (int64_t i = threadIdx.x; i < hist_n; i += 256) hist[i] = 0;
     const int64_t rest = blockIdx.x / 8;
     const int64_t unit = (rest / NG) * 8 + blockIdx.x % 8;
     if (unit >= route_tok_units(T)) return;
@@ -402,7 +407,9 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
                                                                const float *__restrict__ part,
                                                                const float *__restrict__ bias,
                                                                int32_t *__restrict__ ids,
-                                                               float *__restrict__ gates) {
+                                                               float *__restrict__ gates,
+                                                               int64_t e_lo, int64_t EL,
+                                                               int32_t *__restrict__ hist) {
     __shared__ float s_l[EP][RTOK];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -423,7 +430,8 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
     }
     __syncthreads();
     const int64_t t = blk * RTOK + lane;
-    if (wave != 0 || t >= T) return;
+    if (wave != 0) return;
+    const bool valid = t < T;  // lanes past T select on clamped rows, store nothing
     float l[EP];
 #pragma unroll
     for (int e = 0; e < EP; ++e) l[e] = e < E ? s_l[e][lane] : -__builtin_inff();
@@ -459,10 +467,28 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
     }
 #pragma unroll
     for (int j = 0; j < EP; ++j)
-        if (j < k) {
+        if (valid && j < k) {
             ids[t * k + j] = sid[j];
             gates[t * k + j] = ej[j] / denom;
         }
+    if (!hist) return;
+    // The permute's count of (token block, local expert) assignments: this
+    // wave's 64 tokens lie in one token block of PERM_TB, so they are counted
+    // in LDS (s_l is free again) and added with one global atomic per expert.
+    int32_t *s_h = reinterpret_cast<int32_t *>(&s_l[0][0]);
+    if (lane < EL) s_h[lane] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < EP; ++j) {
+        const int64_t el = sid[j] - e_lo;
+        if (valid && j < k && el >= 0 && el < EL) atomicAdd(&s_h[el], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < EL && s_h[lane]) atomicAdd(&hist[(blk * RTOK / PERM_TB) * EL + lane], s_h[lane]);
 }
 
 // ------------------------------------------------------------ fast path
@@ -751,21 +777,23 @@ size_t route_workspace_bytes(const Dims &D) {
 
 template <int EP>
 static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
-                               int32_t *ids, float *gates, void *ws, hipStream_t s) {
+                               int32_t *ids, float *gates, void *ws, int32_t *hist, hipStream_t s) {
     const unsigned nblk = (unsigned)((D.T + RTOK - 1) / RTOK);
     float *part = reinterpret_cast<float *>(ws);
     hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)),
-                       dim3(256), 0, s, D.T, D.d, D.E, x, w, part);
+                       dim3(256), 0, s, D.T, D.d, D.E, x, w, part, hist,
+                       D.perm_blocks() * D.EL());
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
-                       part, bias, ids, gates);
+                       part, bias, ids, gates, D.e_lo, D.EL(), hist);
     return hipGetLastError();
 }
 
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t *blk_counts, bool *hist_done) {
+    if (hist_done) *hist_done = false;
     if (D.T == 0) return hipSuccess;
     if (logits || (route_uses_fast_path(D) && (!ws || ws_bytes < route_workspace_bytes(D)))) {
         // every logit in the defined order
@@ -774,8 +802,10 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
         return launch_exact_t<4, 8>(D, x, w_router, bias, ids, gates, logits, s);
     }
     if (D.E <= 16 && ws && ws_bytes >= route_workspace_bytes(D)) {
-        if (D.E <= 8) return launch_tok_t<8>(D, x, w_router, bias, ids, gates, ws, s);
-        return launch_tok_t<16>(D, x, w_router, bias, ids, gates, ws, s);
+        int32_t *hist = hist_done ? blk_counts : nullptr;
+        if (hist) *hist_done = true;
+        if (D.E <= 8) return launch_tok_t<8>(D, x, w_router, bias, ids, gates, ws, hist, s);
+        return launch_tok_t<16>(D, x, w_router, bias, ids, gates, ws, hist, s);
     }
     if (!route_uses_fast_path(D)) {
         const size_t lds = (size_t)(D.E * stag_pitch(D.d) + RT_TOK * D.E * sizeof(float));
