@@ -82,10 +82,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int64_t c
 __global__ __launch_bounds__(256) void row_amax_kernel(int64_t K, int64_t EL,
                                                        const bf16_t *__restrict__ src,
                                                        const int32_t *__restrict__ offsets,
-                                                       float *__restrict__ amax) {
+                                                       int64_t n_rows, float *__restrict__ amax) {
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (r >= offsets[EL]) return;
+    if (r >= (offsets ? (int64_t)offsets[EL] : n_rows)) return;  // rows: routed, or n_rows
     const u32x4_t *row = reinterpret_cast<const u32x4_t *>(src + r * K);
     float m = 0.0f;
     for (int64_t c = lane; c < K / 8; c += 64) m = amax8(row[c], m);
@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
                                                          const float *__restrict__ amax,
                                                          const int32_t *__restrict__ offsets,
                                                          const int32_t *__restrict__ pstart,
+                                                         const int32_t *__restrict__ row_map,
                                                          uint8_t *__restrict__ dst,
                                                          float *__restrict__ scale) {
     __shared__ int32_t s_row[32];
@@ -124,7 +125,9 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
         }
         const int64_t local = prow0 + tid - pstart[lo];
         const int64_t cnt = offsets[lo + 1] - offsets[lo];
-        const int32_t sr = local < cnt ? (int32_t)(offsets[lo] + local) : -1;
+        const int32_t rr = local < cnt ? (int32_t)(offsets[lo] + local) : -1;
+        // with row_map, routed row rr is row row_map[rr] of src (and of amax)
+        const int32_t sr = (rr >= 0 && row_map) ? row_map[rr] : rr;
         const int e = row_scale_exp(sr >= 0 ? amax[sr] : 0.0f);
         s_row[tid] = sr;
         s_inv[tid] = __uint_as_float((uint32_t)(127 - e) << 23);
@@ -227,19 +230,21 @@ hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_
 
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
                              const int32_t *pstart, float *amax, bool have_amax, uint8_t *dst,
-                             float *scale, hipStream_t s) {
-    const int64_t nrb = D.pcap() / 32, rows = D.cap();
+                             float *scale, hipStream_t s, const int32_t *row_map,
+                             int64_t map_rows) {
+    const int64_t nrb = D.pcap() / 32, rows = row_map ? map_rows : D.cap();
     if (nrb == 0 || D.EL() == 0) return hipSuccess;
     hipError_t e;
-    if (!have_amax) {
-        // row maxima of the routed rows (grid sized for every row a segment may hold)
+    if (!have_amax && rows > 0) {
+        // row maxima of src's rows: the routed rows (grid sized for every row a
+        // segment may hold), or with row_map all map_rows rows, each once
         hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, K,
-                           D.EL(), src, offsets, amax);
+                           D.EL(), src, row_map ? nullptr : offsets, rows, amax);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const unsigned ny = (unsigned)((K / 32 + PACK_FR - 1) / PACK_FR);
     hipLaunchKernelGGL(quant_pack_kernel, dim3((unsigned)nrb, ny), dim3(256), 0, s, K, D.EL(), src,
-                       amax, offsets, pstart, dst, scale);
+                       amax, offsets, pstart, row_map, dst, scale);
     return hipGetLastError();
 }
 

@@ -262,10 +262,13 @@ moe_status check_dims_fp8(const moe_dims *dims, Dims *D) {
 
 namespace {
 // The launches of the W8A8 FFN over a Layout8 workspace at ws.
+// x_perm: the routed rows, row-major; or, with perm_src, x_perm is the tokens'
+// x and routed row r is token perm_src[r] (each token quantised once).
 hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offsets,
                        const uint8_t *wq_gate, const float *s_gate, const uint8_t *wq_up,
                        const float *s_up, const uint8_t *wq_down, const float *s_down,
-                       bf16_t *y_perm, void *ws, hipStream_t s) {
+                       bf16_t *y_perm, void *ws, hipStream_t s,
+                       const int32_t *perm_src = nullptr) {
     const Layout8 L = make_layout8(D);
     MTile *mt = at<MTile>(ws, L.mtiles);
     int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
@@ -278,7 +281,7 @@ hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offse
                                        at<int32_t>(ws, L.hmax), D.cap(), s);
     if (e == hipSuccess)
         e = launch_quant_pack(D, D.d, x_perm, offsets, pstart, at<float>(ws, L.amax), false, xq, sx,
-                              s);
+                              s, perm_src, perm_src ? D.T : 0);
     if (e == hipSuccess)
         e = launch_gemm_gate_up_f8(D, xq, sx, mt, nmt, at<int32_t>(ws, L.mtile_base), wq_gate,
                                    s_gate, wq_up, s_up, h,
@@ -351,20 +354,23 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
     int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
     float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
     int32_t *offsets = at<int32_t>(ws, L.offsets), *inv_perm = at<int32_t>(ws, L.inv_perm);
-    bf16_t *x_perm = at<bf16_t>(ws, L.x_perm), *y = at<bf16_t>(ws, L.y);
+    bf16_t *y = at<bf16_t>(ws, L.y);
+    int32_t *perm_src = at<int32_t>(ws, L.perm_src);
     bool hist_done = false;  // the router may also count the permute's histogram
     hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
                                 nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s,
                                 at<int32_t>(ws, L.blk_counts), &hist_done);
+    // No x_perm: the FFN quantises each token's row of x once and places its
+    // codes at every routed row of that token through perm_src.
     if (e == hipSuccess)
-        e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
-                           at<int32_t>(ws, L.perm_src), inv_perm, x_perm,
-                           at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), nullptr,
-                           nullptr, nullptr, nullptr, nullptr, 0, s, hist_done);
+        e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets, perm_src,
+                           inv_perm, nullptr, at<int32_t>(ws, L.blk_counts),
+                           at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr, nullptr,
+                           nullptr, 0, s, hist_done);
     if (e == hipSuccess)
-        e = run_ffn_fp8(D, x_perm, offsets, (const uint8_t *)wq_gate, s_gate,
+        e = run_ffn_fp8(D, (const bf16_t *)x, offsets, (const uint8_t *)wq_gate, s_gate,
                         (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
-                        at<char>(ws, L.ffn), s);
+                        at<char>(ws, L.ffn), s, perm_src);
     if (e == hipSuccess) e = launch_combine(D, y, inv_perm, gates, out, out_dtype == MOE_F32, s);
     return hip_status(e);
 }

@@ -170,7 +170,8 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
 // packed fragment layout of gemm_pa.h at the 32-aligned segment starts
 // pstart[] (not at all when x_perm is NULL: gather-on-load dispatch), and the
 // GEMM m-tile table is built and the scheduler state of the persistent kernel
-// cleared; otherwise x_perm is row-major at offsets[].  hist_done: blk_counts
+// cleared; otherwise x_perm is row-major at offsets[] (not written when
+// NULL: only the indices are produced).  hist_done: blk_counts
 // already holds the histogram (written by the router), so it is not recounted.
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
@@ -212,9 +213,13 @@ hipError_t launch_combine(const Dims &D, const bf16_t *y_perm, const int32_t *in
 // codes, y rows [cap][d] from packed h codes.
 hipError_t launch_quant_rows(int64_t rows, int64_t cols, const bf16_t *x, uint8_t *q,
                              float *scale, hipStream_t s);
+// With row_map (the permute's perm_src), src holds map_rows unpermuted rows
+// (the tokens' x) and routed row r is read from src row row_map[r]: each row
+// is quantised once, however many slots use it, with the same codes.
 hipError_t launch_quant_pack(const Dims &D, int64_t K, const bf16_t *src, const int32_t *offsets,
                              const int32_t *pstart, float *amax, bool have_amax, uint8_t *dst,
-                             float *scale, hipStream_t s);
+                             float *scale, hipStream_t s, const int32_t *row_map = nullptr,
+                             int64_t map_rows = 0);
 hipError_t launch_gemm_gate_up_f8(const Dims &D, const uint8_t *xq, const float *sx,
                                   const MTile *mtiles, const int32_t *n_mtiles,
                                   const int32_t *mtile_base,

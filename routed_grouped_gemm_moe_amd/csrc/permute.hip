@@ -253,7 +253,7 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (pstart) {
             if (x_perm) e = launch_pack(D, x, perm_src, offsets, pstart, x_perm, s);
-        } else {
+        } else if (x_perm) {
             const unsigned g = (unsigned)((D.T + GATHER_TOK - 1) / GATHER_TOK);
             hipLaunchKernelGGL(gather_kernel, dim3(g), dim3(GATHER_THREADS), 0, s, D.T, D.d, D.k, x,
                                inv_perm, x_perm);
