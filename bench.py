@@ -5,26 +5,38 @@
 A step is one moe_layer call (route, permute, persistent expert-FFN + combine)
 over the seeded synthetic Mixtral-shape batch (T=4096, d=4096, f=14336, E=8,
 top-2), inputs resident in HBM.  W untimed steps, then K timed steps between
-two device synchronisations.  Prints one JSON line with the layer throughput
-(tokens/s), the grouped-GEMM TFLOP/s of the persistent kernel, its roofline
-entry and the CPU oracle timed on a bounded sample of the same workload.
+two device synchronisations.  Each timed step also passes four HIP events to
+the library (moe_layer_opts.events), which records them around its launches;
+their medians over the K steps give the per-stage times (X-Stage, §5.1,
+reports medians).  Prints one JSON line with the layer throughput (tokens/s),
+the grouped-GEMM TFLOP/s of the persistent kernel, its roofline entry, the
+route / permute / combine bandwidth against HBM, and the CPU oracle timed on
+bounded samples of every workload.
 
---mode copy runs a plain device-to-device copy of known size (used to scale
-the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
+Memory-bound stage probes (route, permute, combine as standalone C-ABI calls)
+rotate through copies of their inputs totalling more than the 256 MB
+Infinity Cache, so their bytes come from HBM.
 
---mode ffn_fp8 / ffn_bf16 time the staged expert FFN alone (moe_expert_ffn_fp8
-on E4M3 weights quantised once beforehand, or moe_expert_ffn in bf16) on the
-same workload's routed rows, and print one JSON line in TFLOP/s of 6*d*f per
-routed row against the MFMA peak of that precision.
+Other modes:
+  --mode copy        a plain device copy of known size (scales the FETCH_SIZE
+                     and WRITE_SIZE counters of rocprofv3 to bytes)
+  --mode ffn_fp8 / ffn_bf16 / layer_fp8
+                     the staged W8A8 or bf16 expert FFN alone, or the W8A8 layer
+  --summarize-trace DIR
+                     per-kernel medians of the timed dispatches in the
+                     rocprofv3 kernel trace (csv) under DIR, skipping the
+                     warm-up dispatches (give the run's --warmup / --steps)
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import glob
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -34,7 +46,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_kernel_mixtral_traffic.txt")
+INFINITY_CACHE_BYTES = 256 << 20
+METRIC = "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA bf16 peak), 1 GPU"
 
 
 def kernel_source_hash() -> str:
@@ -46,18 +59,59 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(workload: str):
     """HBM bytes per launch of the persistent kernel from the committed counter
-    summary, or None if absent or taken from different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    summary of this workload, or None if absent or taken from other sources."""
+    path = os.path.join(ROOT, "profiles", f"layer_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
 
+
+def median(v):
+    return float(statistics.median(v)) if v else 0.0
+
+
+# ------------------------------------------------------------ trace summary
+
+def short_name(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("moe::", "")
+    n = re.sub(r"^void\s+", "", n)
+    n = re.sub(r"\(.*$", "", n)              # drop the argument list
+    return n.strip()
+
+
+def summarize_trace(args) -> None:
+    rows = []
+    for p in sorted(glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_trace.csv"),
+                              recursive=True)):
+        with open(p) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                             short_name(r["Kernel_Name"])))
+    rows.sort()
+    by = {}
+    for t0, t1, n in rows:
+        by.setdefault(n, []).append((t1 - t0) / 1000.0)
+    calls = args.warmup + args.steps
+    print(f"kernel trace: {len(rows)} dispatches; warm-up dispatches dropped: the first "
+          f"warmup/(warmup+steps) = {args.warmup}/{calls} of each kernel's calls")
+    total = sum(sum(v) for v in by.values())
+    for n, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        per = len(v) // calls if len(v) % calls == 0 and len(v) >= calls else 0
+        timed = v[per * args.warmup:] if per else v
+        print(f"  {n:48s} calls={len(v):4d} timed={len(timed):4d} "
+              f"median_us={median(timed):10.2f} mean_us={sum(timed) / len(timed):10.2f} "
+              f"min_us={min(timed):10.2f} max_us={max(timed):10.2f} "
+              f"pct_all={100 * sum(v) / total:6.2f}" + ("" if per else "  (not per-step)"))
+
+
+# ------------------------------------------------------------ modes
 
 def copy_mode(args) -> None:
     import torch
@@ -73,19 +127,123 @@ def copy_mode(args) -> None:
                       "copies": args.steps}), flush=True)
 
 
-def cpu_baseline(cfg, arrs, n_tokens: int):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_sample(cfg, arrs, n_tokens: int):
+    """Time the oracle on n_tokens evenly spaced tokens of the workload."""
     import numpy as np
     import oracle
-    toks = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    toks = np.unique(np.linspace(0, cfg.T - 1, min(n_tokens, cfg.T)).astype(np.int64))
     t0 = time.perf_counter()
-    oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"], arrs["w_up"],
-                        arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi, bias=arrs["bias"])
+    _, ids, _ = oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"],
+                                    arrs["w_up"], arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi,
+                                    bias=arrs["bias"])
     dt = time.perf_counter() - t0
-    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n_tokens} evenly spaced tokens of the same {cfg.name} batch, each routed "
-                      f"and run through its {cfg.k} selected experts' float64 SwiGLU and combine "
-                      f"({dt:.1f} s)"}
+    pairs = int(((ids >= cfg.e_lo) & (ids < cfg.E_hi)).sum())
+    return {"tokens": int(len(toks)), "seconds": round(dt, 3),
+            "tokens_per_s": round(len(toks) / dt, 2),
+            "gflops": round(6.0 * cfg.d * cfg.f * pairs / dt / 1e9, 2),
+            "full_layer_s_est": round(cfg.T * dt / len(toks), 1)}
+
+
+def cpu_baseline(cfg, arrs, n_tokens: int, per_config: bool):
+    """The oracle as it stands, on this host's cores: the headline sample of
+    the benchmarked workload, bounded samples of every workload, and the tiny
+    workload once more on one thread, with the host's CPU model."""
+    import moe_workloads as W
+    import oracle
+    threads = oracle.num_threads()
+    head = oracle_sample(cfg, arrs, n_tokens)
+    rec = {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{head['tokens']} evenly spaced tokens of the same {cfg.name} batch, each "
+                     f"routed and run through its selected experts' float64 SwiGLU and combine "
+                     f"({head['seconds']} s; {head['gflops']} GFLOP/s)"}
+    if per_config:
+        sizes = {"tiny": 256, "mixtral": 128, "fine": 1024, "skewed": 128, "dsv3_share": 1024}
+        pc = {}
+        for name, n in sizes.items():
+            c = W.CONFIGS[name]
+            a = arrs if name == cfg.name else W.generate(c)
+            pc[name] = oracle_sample(c, a, n)
+            del a
+        oracle.set_num_threads(1)
+        try:
+            one = oracle_sample(W.CONFIGS["tiny"], W.generate(W.CONFIGS["tiny"]), 256)
+        finally:
+            oracle.set_num_threads(threads)
+        rec["per_config"] = pc
+        rec["tiny_one_thread"] = one
+    return rec
+
+
+def stage_probes(args, cfg, M, torch, D, x, wr, bias, n_rows, t_local):
+    """Route, permute and combine as standalone C-ABI calls, inputs rotated
+    through copies totalling more than the Infinity Cache; median of
+    args.steps calls each, against the algorithmic bytes of each stage."""
+    def copies(t):
+        n = max(2, -(-int(1.25 * INFINITY_CACHE_BYTES) // (t.numel() * t.element_size())))
+        return [t.clone() for _ in range(n)]
+
+    def timed(fn, n_in):
+        for i in range(args.warmup):
+            fn(i % n_in)
+        torch.cuda.synchronize()
+        ms = []
+        for i in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn((args.warmup + i) % n_in)
+            e1.record()
+            ms.append((e0, e1))
+        torch.cuda.synchronize()
+        return median([a.elapsed_time(b) for a, b in ms])
+
+    T, d, k, E = cfg.T, cfg.d, cfg.k, cfg.E
+    xs = copies(x)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(M.moe_route_workspace_bytes(D), 256), dtype=torch.uint8, device="cuda")
+    route_ms = timed(lambda i: M.moe_route(D, xs[i], wr, bias, topk_ids=ids, topk_w=gates, ws=rws),
+                     len(xs))
+    route_bytes = T * d * 2 + E * d * 2 + T * k * 8
+    cap = max(T * k, 1)
+    counts = torch.empty(D.e_hi - D.e_lo, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(D.e_hi - D.e_lo + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(cap, dtype=torch.int32, device="cuda")
+    inv = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    xp = torch.empty((cap, d), dtype=torch.bfloat16, device="cuda")
+    pws = torch.empty(M.moe_permute_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    perm_ms = timed(lambda i: M.moe_permute(D, xs[i], ids, counts, offsets, perm, inv, xp, ws=pws),
+                    len(xs))
+    # read every token row with a local slot once, write the routed rows and indices
+    perm_bytes = t_local * d * 2 + n_rows * d * 2 + T * k * 8 + n_rows * 4
+    del xs
+    ys = copies(xp)
+    out_f32 = bool(cfg.out_fp32)
+    out = torch.empty((T, d), dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    dt = M.MOE_F32 if out_f32 else M.MOE_BF16
+    comb_ms = timed(lambda i: M.moe_combine(D, ys[i], inv, gates, out=out, out_dtype=dt), len(ys))
+    comb_bytes = n_rows * d * 2 + T * k * 8 + T * d * (4 if out_f32 else 2)
+    del ys
+
+    def entry(ms, nbytes, what):
+        gbs = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        return {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes), "GBps": round(gbs, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "call": what}
+    return {"route": entry(route_ms, route_bytes, "moe_route"),
+            "permute": entry(perm_ms, perm_bytes, "moe_permute (row-major x_perm)"),
+            "combine": entry(comb_ms, comb_bytes, "moe_combine"),
+            "rotation": "inputs rotated through copies > 1.25 x 256 MB; median of "
+                        f"{args.steps} calls after {args.warmup} warm-up"}
 
 
 def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
@@ -106,19 +264,21 @@ def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
+    evs = []
     for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         step()
-    ev1.record()
+        e1.record()
+        evs.append((e0, e1))
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = median([a.elapsed_time(b) for a, b in evs])
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     print(json.dumps({
         "mode": args.mode,
         "metric": "staged expert-FFN TFLOP/s (" + ("W8A8 E4M3" if fp8 else "bf16") + "), 1 GPU",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 4),
+        "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_call_median": round(ms, 4),
         "steps": args.steps, "warmup": args.warmup, "peak": peak, "frac": round(tflops / peak, 4),
         "dtype": "fp8_e4m3" if fp8 else "bf16", "routed_rows": n_rows,
         "flops_per_call": flops,
@@ -127,39 +287,27 @@ def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
     }), flush=True)
 
 
-def layer_fp8_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
-    """Time moe_layer_fp8 (route, permute, W8A8 FFN, combine) on the workload;
-    the weights are quantised once beforehand."""
+def w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt):
+    """The same workload through moe_layer_fp8 (weights quantised once,
+    outside the timed steps)."""
     (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
-    ws = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
-    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
-    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
-                      device="cuda")
-    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
-    step = lambda: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
-                                   out_dtype=dt, topk_ids_out=ids, ws=ws)
+    ws8 = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    step8 = lambda o=None: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
+                                           out_dtype=dt, ws=ws8, opts=o)
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ids_h = ids.cpu().numpy()
-    n_local = int(((ids_h >= cfg.e_lo) & (ids_h < cfg.E_hi)).sum())
-    flops = 6.0 * cfg.d * cfg.f * n_local
+        step8()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    opts = [M.layer_opts(events=e) for e in evs]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for o in opts:
+        step8(o)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed / args.steps * 1e3
-    print(json.dumps({
-        "mode": "layer_fp8",
-        "metric": "MoE-layer tokens/s with the W8A8 (E4M3) expert FFN, 1 GPU",
-        "value": round(cfg.T * args.steps / elapsed, 1), "unit": "tokens/s",
-        "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup,
-        "layer_tflops": round(flops / (ms * 1e-3) / 1e12, 2), "dtype": "fp8_e4m3",
-        "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
-                   "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi]},
-    }), flush=True)
+    el = time.perf_counter() - t0
+    return {"value": round(cfg.T * args.steps / el, 1), "unit": "tokens/s",
+            "ms_per_step": round(el / args.steps * 1e3, 4),
+            "ms_per_step_median": round(median([e[0].elapsed_time(e[3]) for e in evs]), 4),
+            "dtype": "fp8_e4m3", "entry_point": "moe_layer_fp8 (staged)"}
 
 
 def main() -> None:
@@ -172,14 +320,23 @@ def main() -> None:
                     choices=["layer", "copy", "ffn_fp8", "ffn_bf16", "layer_fp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-per-config", action="store_true",
+                    help="oracle baseline on the benchmarked workload only")
     ap.add_argument("--no-w8a8", action="store_true",
                     help="skip the extra W8A8 layer measurement of the default mode")
-    ap.add_argument("--tile-order", type=int, default=0, choices=[0, 1],
-                    help="moe_layer persistent-kernel tile order: 0 by kind, 1 interleaved")
+    ap.add_argument("--no-stage-probe", action="store_true",
+                    help="skip the standalone route / permute / combine measurements")
+    ap.add_argument("--tile-order", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="moe_layer tile order (moe_tile_order)")
+    ap.add_argument("--lead", type=int, default=0, help="dependency lead of tile order 2")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
                     help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
+    ap.add_argument("--summarize-trace", default=None, metavar="DIR")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -207,62 +364,84 @@ def main() -> None:
     if args.mode in ("ffn_fp8", "ffn_bf16"):
         ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
         return
-    if args.mode == "layer_fp8":
-        layer_fp8_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias)
-        return
-    M.moe_set_gather_dispatch(args.dispatch == "gather")
-    M.moe_set_tile_order(args.tile_order)
-    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
                       device="cuda")
+    if args.mode == "layer_fp8":
+        rec = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt)
+        rec.update({"mode": "layer_fp8",
+                    "metric": "MoE-layer tokens/s with the W8A8 (E4M3) expert FFN, 1 GPU",
+                    "steps": args.steps, "warmup": args.warmup,
+                    "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d,
+                               "f": cfg.f, "E": cfg.E, "k": cfg.k,
+                               "local_experts": [cfg.e_lo, cfg.E_hi]}})
+        print(json.dumps(rec), flush=True)
+        return
+
+    base = dict(dispatch=M.MOE_DISPATCH_GATHER if args.dispatch == "gather" else
+                M.MOE_DISPATCH_PACKED, tile_order=args.tile_order, lead=args.lead)
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
 
-    def step():
+    def step(opts):
         M.moe_layer(D, x, wr, wg, wu, wd, bias=bias, out=out, out_dtype=dt, topk_ids_out=ids,
-                    topk_w_out=gates, ws=ws)
+                    topk_w_out=gates, ws=ws, opts=opts)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    warm_opts = M.layer_opts(**base)
     for _ in range(args.warmup):
-        step()
+        step(warm_opts)
     torch.cuda.synchronize()
     if M.moe_device_status(D, ws) != 0:
         raise RuntimeError("device status not OK after warmup")
 
     # local rows (all T*k for a full-local config)
     ids_h = ids.cpu().numpy()
-    n_local = int(((ids_h >= cfg.e_lo) & (ids_h < cfg.E_hi)).sum())
+    local = (ids_h >= cfg.e_lo) & (ids_h < cfg.E_hi)
+    n_local = int(local.sum())
+    t_local = int(local.any(axis=1).sum())
     flops = 6.0 * cfg.d * cfg.f * n_local   # Weave §3.1: 6*H*I per token-expert pair
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    M.moe_timing_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    opts = [M.layer_opts(**base, events=e) for e in evs]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for o in opts:
+        step(o)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    n_ev, (route_ms, perm_ms, ffn_ms) = M.moe_timing_read()
-    M.moe_timing_enable(False)
     if M.moe_device_status(D, ws) != 0:
         raise RuntimeError("device status not OK after timed steps")
+    route_ms = median([e[0].elapsed_time(e[1]) for e in evs])
+    perm_ms = median([e[1].elapsed_time(e[2]) for e in evs])
+    ffn_ms = median([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = median([e[0].elapsed_time(e[3]) for e in evs])
 
     elapsed = t1 - t0
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = cfg.T * args.steps / elapsed
     ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12 if ffn_ms > 0 else 0.0
     layer_tflops = flops / (ms_per_step * 1e-3) / 1e12
-    traffic = read_traffic()
+    # algorithmic bytes of the fused layer's route and permute stages
+    route_bytes = cfg.T * cfg.d * 2 + cfg.E * cfg.d * 2 + cfg.T * cfg.k * 8
+    perm_bytes = t_local * cfg.d * 2 + n_local * cfg.d * 2 + cfg.T * cfg.k * 8 + n_local * 4
+
+    def gb(nbytes, ms):
+        g = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        return {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes), "GBps": round(g, 1),
+                "frac_hbm": round(g / PEAK_HBM_GBS, 4)}
 
     rec = {
-        "metric": "MoE-layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA bf16 peak), 1 GPU",
+        "metric": METRIC,
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -275,37 +454,31 @@ def main() -> None:
         "grouped_gemm_tflops": round(ffn_tflops, 2),
         "grouped_gemm_pct_mfma_peak": round(100 * ffn_tflops / PEAK_BF16_TFLOPS, 2),
         "layer_tflops": round(layer_tflops, 2),
-        "stages_ms": {"route": round(route_ms, 4), "permute": round(perm_ms, 4),
-                      "expert_ffn_combine_persistent": round(ffn_ms, 4), "events": n_ev},
+        "stages_median": {"route": gb(route_bytes, route_ms), "permute": gb(perm_bytes, perm_ms),
+                          "expert_ffn_combine_persistent_us": round(ffn_ms * 1e3, 2),
+                          "source": "HIP events of moe_layer_opts.events, median of the "
+                                    f"{args.steps} timed steps"},
         "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ffn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
+                     "traffic": read_traffic(cfg.name),
                      "kernel": "layer_kernel (persistent gate/up, down, combine tiles)",
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": flops,
+                     "duration": "median over the timed steps of the launch's HIP events"},
     }
+    if not args.no_stage_probe:
+        print("[bench] stage probes", file=sys.stderr, flush=True)
+        rec["memory_bound_stages"] = stage_probes(args, cfg, M, torch, D, x, wr, bias, n_local,
+                                                  t_local)
     if not args.no_w8a8 and cfg.f % 256 == 0:
-        # the same workload through moe_layer_fp8 (weights quantised once,
-        # outside the timed steps); reported beside the bf16 line, not as it
         print("[bench] W8A8 layer", file=sys.stderr, flush=True)
-        (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
-        ws8 = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
-        step8 = lambda: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
-                                        out_dtype=dt, ws=ws8)
-        for _ in range(args.warmup):
-            step8()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step8()
-        torch.cuda.synchronize()
-        el8 = time.perf_counter() - t0
-        rec["w8a8_layer"] = {"value": round(cfg.T * args.steps / el8, 1), "unit": "tokens/s",
-                             "ms_per_step": round(el8 / args.steps * 1e3, 4),
-                             "dtype": "fp8_e4m3", "entry_point": "moe_layer_fp8 (staged)"}
-        del ws8, gq, uq, dq
+        rec["w8a8_layer"] = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt)
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline ({args.cpu_tokens} tokens)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, arrs, args.cpu_tokens)
+        del x, wr, wg, wu, wd, ws
+        torch.cuda.empty_cache()
+        print(f"[bench] cpu baseline ({args.cpu_tokens} tokens + per-workload samples)",
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, arrs, args.cpu_tokens,
+                                           not args.no_cpu_per_config)
     print(json.dumps(rec), flush=True)
 
 

@@ -72,6 +72,79 @@ typedef struct {
     int64_t T, d, f, E, k, e_lo, e_hi;
 } moe_dims;
 
+/* ---- Per-call options of moe_layer and moe_layer_fp8.  A NULL pointer, or
+ * a zero-initialised struct, selects every default.  The options travel with
+ * the call: nothing is kept between calls, so calls on distinct workspaces
+ * (and streams) are independent whatever options each passes. */
+typedef enum {
+    MOE_DISPATCH_PACKED = 0,  /* the permute writes x_perm in the packed
+                                 MFMA-fragment layout; gate/up tiles load it
+                                 straight into registers (default) */
+    MOE_DISPATCH_GATHER = 1   /* gather-on-load: x_perm is never written; each
+                                 gate/up tile fetches its rows of x through
+                                 perm_src into LDS (Weave §4 overlaps dispatch
+                                 with the first GEMM; on one GPU the dispatch is
+                                 this gather).  Inputs of 2 GiB or more
+                                 (T*d*2 bytes) use the packed mode. */
+} moe_dispatch;
+
+/* Tile order of moe_layer's persistent kernel.  Every order runs the same
+ * tiles with the same arithmetic, so the output bits do not depend on it. */
+typedef enum {
+    MOE_ORDER_BY_KIND = 0,    /* every workgroup claims gate/up tiles until none
+                                 are left, then down tiles (each waiting on its
+                                 m-tile's gate/up tiles), then combine tiles:
+                                 Weave §4's claiming in dependency order */
+    MOE_ORDER_READY_DOWN = 1, /* X-Stage §4.3, ready-only form: before each
+                                 gate/up claim a workgroup takes the next down
+                                 tile of its XCD's range if every gate/up tile
+                                 of that tile's m-tile is already published */
+    MOE_ORDER_LEAD = 2,       /* X-Stage §4.3 with a dependency lead: gate/up
+                                 and down tiles form one stream in which a down
+                                 tile follows the last gate/up tile it reads by
+                                 at least `lead` gate/up tiles (down first
+                                 whenever it is eligible) */
+    MOE_ORDER_COMBINE_FIRST = 3 /* tile-level signaling, consumers first: down
+                                 tiles are claimed column group by column group
+                                 (the columns one combine tile covers), and
+                                 before each down claim a workgroup takes a
+                                 combine tile whose column group is complete */
+} moe_tile_order;
+
+typedef struct {
+    int32_t dispatch;        /* moe_dispatch (moe_layer only) */
+    int32_t tile_order;      /* moe_tile_order (moe_layer only) */
+    int32_t lead;            /* MOE_ORDER_LEAD: the lead in gate/up tiles; 0 =
+                                one round of the persistent grid */
+    uint32_t perturb_seed;   /* moe_layer only; 0 = off.  A test aid for the
+                                flag protocol: every producer tile waits a
+                                seeded pseudo-random delay (0 to about 100 us)
+                                between writing its output and publishing it,
+                                and (orders 0, 1, 3) the tiles of each kind are
+                                claimed in reverse order.  The result bits are
+                                unchanged; only the timing is adversarial. */
+    int64_t wait_timeout_us; /* moe_layer only: bound of each device-side flag
+                                wait; 0 = 2 s.  A wait that times out records
+                                MOE_ERR_DEVICE_TIMEOUT in the workspace and
+                                makes every other wait of that launch return at
+                                once, so the launch still drains. */
+    int64_t *trace;          /* moe_layer only: per-tile trace (measurement aid,
+                                after X-Stage §5.1's per-tile clock traces), or
+                                NULL.  Device memory, int64 [1 + 4*trace_records]:
+                                [0] = records written (the caller zeroes it; it
+                                may exceed trace_records, the excess is
+                                dropped), then per tile of the persistent kernel
+                                {kind << 32 | tile index, workgroup << 8 | XCD,
+                                start tick, end tick}: kind 1 gate/up, 2 down,
+                                4 a K part of a cut down tile, 3 combine; ticks
+                                of moe_wall_clock_hz(). */
+    int64_t trace_records;
+    void *events[4];         /* hipEvent_t handles or NULL: recorded on `stream`
+                                before the route, after the route, after the
+                                permute, and after the last launch (measurement
+                                aid: stage times per call) */
+} moe_layer_opts;
+
 /* Human-readable name of a status code (static string). */
 const char *moe_status_string(moe_status s);
 
@@ -103,6 +176,20 @@ size_t moe_route_workspace_bytes(const moe_dims *dims);
 moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
                      int32_t *topk_ids, float *topk_w, float *logits, void *ws, size_t ws_bytes,
                      void *stream);
+
+/* moe_route_bounds: the quantities the E > 16 fast path of moe_route selects
+ * with, written out so that a caller can check the premise its ids rest on
+ * (verification aid).
+ *   approx f32 [T, E] out  the sum of the split-K matrix-core partials of
+ *                          x . w_e, plus the bias
+ *   eps    f32 [T, E] out  the bound the router assumes: |approx - logit| <=
+ *                          eps, logit being the defined-order value
+ * Arguments otherwise as moe_route; ws (moe_route_workspace_bytes) is
+ * required.  MOE_ERR_UNSUPPORTED when the fast path does not apply
+ * (E <= 16, or d too large for its LDS staging). */
+moe_status moe_route_bounds(const moe_dims *dims, const void *x, const void *w_router,
+                            const float *bias, float *approx, float *eps, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /* ---- moe_permute: dispatch into expert-contiguous rows (Weave §2.1 stage
  * 1, Figure 3; on one GPU the "send" is a gather; each source row is read
@@ -174,18 +261,35 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const void *x_perm, const in
                               const float *s_up, const void *wq_down, const float *s_down,
                               void *y_perm, void *ws, size_t ws_bytes, void *stream);
 
+/* The two halves of moe_expert_ffn_fp8 as separate calls (verification aid;
+ * the same kernels, so down(gate_up(x)) equals moe_expert_ffn_fp8 bit for
+ * bit).  ws: moe_expert_ffn_fp8_workspace_bytes(dims) bytes.
+ * moe_gate_up_fp8: GEMM0 + SiLU-mul (Weave §2.1 stages 2-3) on E4M3 codes of
+ *   the rows of x_perm, quantised per row inside:
+ *   h bf16 [T*k, f] out (first offsets[E_loc] rows valid)
+ * moe_down_fp8: GEMM1 (Weave §2.1 stage 4) of bf16 rows h [T*k, f],
+ *   quantised per row inside:  y_perm bf16 [T*k, d] out. */
+moe_status moe_gate_up_fp8(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                           const void *wq_gate, const float *s_gate, const void *wq_up,
+                           const float *s_up, void *h, void *ws, size_t ws_bytes, void *stream);
+moe_status moe_down_fp8(const moe_dims *dims, const void *h, const int32_t *offsets,
+                        const void *wq_down, const float *s_down, void *y_perm, void *ws,
+                        size_t ws_bytes, void *stream);
+
 /* moe_layer_fp8: the whole forward pass with the W8A8 FFN, staged: route
  * (as moe_route), row-major permute (as moe_permute), moe_expert_ffn_fp8,
  * moe_combine -- one stream, one workspace, no host synchronisation.
  * Arguments as moe_layer, with the E4M3 weights and scales of
- * moe_expert_ffn_fp8 in place of the bf16 weights.  Requires f % 256 == 0. */
+ * moe_expert_ffn_fp8 in place of the bf16 weights.  Requires f % 256 == 0.
+ * Of opts only events[] applies (the stages are separate launches); its
+ * other fields must be zero (MOE_ERR_INVALID_ARG otherwise). */
 size_t moe_layer_fp8_workspace_bytes(const moe_dims *dims);
 moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_router,
                          const float *bias, const void *wq_gate, const float *s_gate,
                          const void *wq_up, const float *s_up, const void *wq_down,
                          const float *s_down, void *out, moe_dtype out_dtype,
                          int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                         void *stream);
+                         const moe_layer_opts *opts, void *stream);
 
 /* ---- moe_combine: gate-weighted sum back to token order (Weave §2.1 stage 5).
  *   y_perm   bf16 [T*k, d]  expert outputs by row
@@ -207,69 +311,37 @@ moe_status moe_combine(const moe_dims *dims, const void *y_perm, const int32_t *
  * releases a flag that the combine tiles reading it acquire.
  *   out          [T, d] bf16 or f32 (f32 for an expert-parallel partial)
  *   topk_ids_out i32 [T,k], topk_w_out f32 [T,k]: optional copies of routing
+ *   opts         per-call options (moe_layer_opts) or NULL for the defaults;
+ *                MOE_ERR_INVALID_ARG for a value outside its range
  */
 size_t moe_layer_workspace_bytes(const moe_dims *dims);
 moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
                      const void *w_gate, const void *w_up, const void *w_down, void *out,
                      moe_dtype out_dtype, int32_t *topk_ids_out, float *topk_w_out, void *ws,
-                     size_t ws_bytes, void *stream);
+                     size_t ws_bytes, const moe_layer_opts *opts, void *stream);
+
+/* ---- Matrix-core probe (measurement aid).  Runs, for each of n cases, a
+ * chain of `steps` matrix-core instructions and returns the float32 results,
+ * so that their rounding can be compared with exact sums: the fast router's
+ * error bound and the W8A8 tolerance rest on it.
+ *   kind 0: v_mfma_f32_32x32x16_bf16, K = 16, a and b bf16;
+ *   kind 1: v_mfma_f32_32x32x64_f8f6f4 on E4M3 codes, K = 64, a and b bytes.
+ *   a, b  [n][steps][32][K]  rows of A and of B^T for each step
+ *   c     f32 [n][32][32]    accumulator before the first step
+ *   d     f32 [n][32][32] out  c + sum over steps (in order) of a_s . b_s^T
+ * Device pointers, 16-byte aligned; 1 <= steps <= 4096; n < 2^31.
+ * MOE_ERR_INVALID_ARG otherwise. */
+moe_status moe_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
+                          const float *c, float *d, void *stream);
 
 /* Synchronises `stream`, then reads the device status word at offset 0 of a
  * workspace last used by moe_layer or moe_expert_ffn (MOE_OK, or
  * MOE_ERR_DEVICE_TIMEOUT if a flag wait gave up).  ws_bytes must be >= 256. */
 moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_bytes, void *stream);
 
-/* ---- Stage timing (measurement aid).  When enabled, moe_layer records HIP
- * events on its stream around each of its launches; moe_timing_read
- * synchronises and returns the average milliseconds per call of each stage
- * since the last enable: [0] route, [1] permute (all its kernels), [2] the
- * persistent expert-FFN + combine kernel.  Returns the number of calls
- * averaged.  Not thread-safe; for benchmarking only. */
-void moe_timing_enable(int on);
-int moe_timing_read(float *stage_ms, int n_stages);
-
-/* ---- Per-tile trace (measurement aid, after the per-tile clock traces that
- * X-Stage, §5.1, takes of its fused kernel).  With a buffer set, every
- * moe_layer launch appends one record per tile of its persistent kernel:
- *   int64 buf[1 + 4*n_records], buf[0] = records written (the caller zeroes it;
- *   it can exceed n_records, extra records are dropped), then per record
- *   {kind << 32 | tile index, workgroup << 8 | XCD, start tick, end tick},
- *   kind 1 = gate/up, 2 = down, 4 = a K part of a cut down tile, 3 = combine;
- *   ticks of the device's constant
- *   wall clock, moe_wall_clock_hz() per second.
- * buf is device memory owned by the caller; NULL (or n_records < 1) turns the
- * trace off.  Not thread-safe; for profiling only. */
-void moe_set_trace(void *buf, int64_t n_records);
+/* Frequency of the device's constant wall clock (ticks per second), the
+ * time base of the per-tile trace. */
 int64_t moe_wall_clock_hz(void);
-
-/* Timeout of each device-side flag wait of moe_layer, in microseconds
- * (default 2 s; values < 1 restore the default).  A wait that times out
- * records MOE_ERR_DEVICE_TIMEOUT and makes every other wait of that launch
- * return at once, so the launch still drains.  Used by tests to exercise the
- * timeout path. */
-void moe_set_wait_timeout_us(int64_t us);
-
-/* Dispatch mode of moe_layer (process-wide; default off).  Off: the permute
- * writes x_perm in the packed MFMA-fragment layout and the gate/up tiles load
- * it straight into registers.  On: gather-on-load dispatch -- x_perm is never
- * written; each gate/up tile fetches its rows of x through perm_src into LDS
- * (Weave §4 overlaps dispatch with the first GEMM; on one GPU the dispatch is
- * this gather).  Both modes give the same bits: the tiles share one k-order.
- * Inputs of 2 GiB or more (T*d*2 bytes) always use the packed mode.  Not
- * thread-safe with concurrent moe_layer calls. */
-void moe_set_gather_dispatch(int on);
-
-/* Tile order of moe_layer's persistent kernel (process-wide; default 0).
- *   0  by kind: every workgroup claims gate/up tiles until none are left,
- *      then down tiles (waiting on their m-tile's gate/up tiles), then
- *      combine tiles -- Weave §4's claiming in dependency order;
- *   1  interleaved (X-Stage §4.3, ready-only form): before each gate/up
- *      claim a workgroup takes the next down tile of its XCD's range when
- *      every gate/up tile of that tile's m-tile is already published.
- * Both orders run the same tiles with the same arithmetic: the output bits
- * are identical.  Returns MOE_OK, or MOE_ERR_INVALID_ARG for another value.
- * Not thread-safe with concurrent moe_layer calls. */
-int moe_set_tile_order(int policy);
 
 #ifdef __cplusplus
 }

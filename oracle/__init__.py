@@ -32,6 +32,12 @@ Parity status of each function (what pins it, in tests/test_oracle_*.py):
                   dense SwiGLU of the decoded operands (numpy matmuls) up to
                   the bf16/E4M3 rounding of h; per-row and per-channel scales
                   land on their own axes (non-uniform scales).
+  gate_up_rows_fp8  pinned: equals numpy float64 products of the decoded
+                  codes with the row and channel scales, then silu(g)*u; its
+                  bf16 rounding equals expert_rows_fp8's h.
+  down_rows_fp8   pinned: equals a numpy float64 dense product of decoded
+                  codes and scales; fed the oracle's own quantised h it gives
+                  expert_rows_fp8's y.
   layer_tokens    pinned: k=1 one-hot reduces to one expert's FFN; identical
                   experts reduce to the dense FFN (gates sum to 1); sum of
                   expert-parallel shard partials equals the unsharded layer.
@@ -88,7 +94,13 @@ def _load():
         lib.oracle_expert_rows_fp8.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                vp, vp]
         lib.oracle_expert_rows_fp8.restype = C.c_int
+        lib.oracle_gate_up_rows_fp8.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_gate_up_rows_fp8.restype = C.c_int
+        lib.oracle_down_rows_fp8.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        lib.oracle_down_rows_fp8.restype = C.c_int
         lib.oracle_num_threads.restype = C.c_int
+        lib.oracle_set_num_threads.argtypes = [C.c_int]
+        lib.oracle_set_num_threads.restype = None
         for name in ("oracle_router_logits", "oracle_router_logits_f64", "oracle_topk_gates",
                      "oracle_route", "oracle_permute", "oracle_expert_rows", "oracle_combine",
                      "oracle_layer_tokens"):
@@ -100,6 +112,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle runs with."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP thread count of later oracle calls."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _p(a: Optional[np.ndarray]):
@@ -279,3 +296,34 @@ def expert_rows_fp8(x_rows, expert_of_row, wq_gate, s_gate, wq_up, s_up, wq_down
                                           _p(su), _p(wd), _p(sd), _p(y), _p(h)),
            "expert_rows_fp8")
     return (y, h) if want_h else y
+
+
+def gate_up_rows_fp8(x_rows, expert_of_row, wq_gate, s_gate, wq_up, s_up) -> np.ndarray:
+    """GEMM0 + SiLU-mul of the W8A8 FFN: h [n, f] float64, not rounded."""
+    x_rows = _u16(x_rows)
+    e = np.ascontiguousarray(expert_of_row, dtype=np.int32)
+    u8 = lambda a: np.ascontiguousarray(a, dtype=np.uint8)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    wg, wu, sg, su = u8(wq_gate), u8(wq_up), f32(s_gate), f32(s_up)
+    n, d = x_rows.shape
+    EL, f, _ = wg.shape
+    h = np.empty((n, f), dtype=np.float64)
+    _check(_load().oracle_gate_up_rows_fp8(n, d, f, EL, _p(x_rows), _p(e), _p(wg), _p(sg),
+                                           _p(wu), _p(su), _p(h)), "gate_up_rows_fp8")
+    return h
+
+
+def down_rows_fp8(hq, sh, expert_of_row, wq_down, s_down) -> np.ndarray:
+    """GEMM1 of the W8A8 FFN from given E4M3 codes hq [n, f] and row scales
+    sh [n] of h: y [n, d] float64."""
+    hq = np.ascontiguousarray(hq, dtype=np.uint8)
+    sh = np.ascontiguousarray(sh, dtype=np.float32)
+    e = np.ascontiguousarray(expert_of_row, dtype=np.int32)
+    wd = np.ascontiguousarray(wq_down, dtype=np.uint8)
+    sd = np.ascontiguousarray(s_down, dtype=np.float32)
+    n, f = hq.shape
+    EL, d, _ = wd.shape
+    y = np.empty((n, d), dtype=np.float64)
+    _check(_load().oracle_down_rows_fp8(n, d, f, EL, _p(hq), _p(sh), _p(e), _p(wd), _p(sd),
+                                        _p(y)), "down_rows_fp8")
+    return y

@@ -57,8 +57,10 @@ int oracle_version(void) { return 1; }
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
 
 /* ---------------------------------------------------------------- routing */
@@ -476,4 +478,75 @@ int oracle_expert_rows_fp8(int64_t n, int64_t d, int64_t f, int64_t E_loc,
         free(xr); free(hb); free(xq); free(hq);
     }
     return rc;
+}
+
+/* The two GEMMs of the W8A8 FFN on their own (same recipe as above), so that
+ * each can be checked separately against a GPU that rounds differently.
+ *
+ * oracle_gate_up_rows_fp8: h[r,c] = silu(g) * u, in double and NOT rounded,
+ * with g = sx * sg[c] * sum_i dec(xq_i) dec(wgq[c,i]) (u likewise), xq and sx
+ * the row's own E4M3 codes and scale.  h [n,f] double. */
+int oracle_gate_up_rows_fp8(int64_t n, int64_t d, int64_t f, int64_t E_loc,
+                            const uint16_t *x_rows, const int32_t *expert_of_row,
+                            const uint8_t *wq_gate, const float *s_gate, const uint8_t *wq_up,
+                            const float *s_up, double *h) {
+    if (n < 0 || d <= 0 || f <= 0 || E_loc <= 0 || !x_rows || !expert_of_row || !wq_gate ||
+        !s_gate || !wq_up || !s_up || !h)
+        return ORACLE_EINVAL;
+    for (int64_t r = 0; r < n; ++r)
+        if (expert_of_row[r] < 0 || expert_of_row[r] >= E_loc) return ORACLE_EINVAL;
+    double lut[256];
+    for (int c = 0; c < 256; ++c) lut[c] = oracle_e4m3_value(c);
+    int rc = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t e = expert_of_row[r];
+        float *xr = (float *)malloc(sizeof(float) * (size_t)d);
+        uint8_t *xq = (uint8_t *)malloc((size_t)d);
+        if (!xr || !xq) {
+            rc = ORACLE_EINVAL;
+        } else {
+            float sx;
+            for (int64_t i = 0; i < d; ++i) xr[i] = bf(x_rows[r * d + i]);
+            quant_row(d, xr, xq, &sx);
+            for (int64_t c = 0; c < f; ++c) {
+                const uint8_t *rg = wq_gate + (e * f + c) * d, *ru = wq_up + (e * f + c) * d;
+                double g = 0.0, u = 0.0;
+                for (int64_t i = 0; i < d; ++i) {
+                    g += lut[xq[i]] * lut[rg[i]];
+                    u += lut[xq[i]] * lut[ru[i]];
+                }
+                g *= (double)sx * (double)s_gate[e * f + c];
+                u *= (double)sx * (double)s_up[e * f + c];
+                h[r * f + c] = g / (1.0 + exp(-g)) * u;
+            }
+        }
+        free(xr); free(xq);
+    }
+    return rc;
+}
+
+/* oracle_down_rows_fp8: y[r,o] = sh[r] * sd[o] * sum_c dec(hq[r,c]) dec(wdq[o,c])
+ * in double, from given codes hq [n,f] and row scales sh [n] of h. */
+int oracle_down_rows_fp8(int64_t n, int64_t d, int64_t f, int64_t E_loc, const uint8_t *hq,
+                         const float *sh, const int32_t *expert_of_row, const uint8_t *wq_down,
+                         const float *s_down, double *y) {
+    if (n < 0 || d <= 0 || f <= 0 || E_loc <= 0 || !hq || !sh || !expert_of_row || !wq_down ||
+        !s_down || !y)
+        return ORACLE_EINVAL;
+    for (int64_t r = 0; r < n; ++r)
+        if (expert_of_row[r] < 0 || expert_of_row[r] >= E_loc) return ORACLE_EINVAL;
+    double lut[256];
+    for (int c = 0; c < 256; ++c) lut[c] = oracle_e4m3_value(c);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        const int64_t e = expert_of_row[r];
+        for (int64_t o = 0; o < d; ++o) {
+            const uint8_t *rd = wq_down + (e * d + o) * f;
+            double s = 0.0;
+            for (int64_t c = 0; c < f; ++c) s += lut[hq[r * f + c]] * lut[rd[c]];
+            y[r * d + o] = s * (double)sh[r] * (double)s_down[e * d + o];
+        }
+    }
+    return ORACLE_OK;
 }

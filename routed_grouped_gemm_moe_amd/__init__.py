@@ -19,13 +19,14 @@ from typing import Optional, Tuple
 
 __all__ = [
     "MoEDims", "lib_path", "load", "exported_abi_names", "header_abi_names",
-    "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+    "moe_route", "moe_route_bounds", "moe_probe_mfma", "moe_gate_up_fp8", "moe_down_fp8",
+    "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
     "moe_route_workspace_bytes",
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
-    "moe_timing_enable", "moe_timing_read", "moe_set_wait_timeout_us", "moe_set_trace",
-    "moe_set_gather_dispatch",
-    "moe_wall_clock_hz", "MoEError",
+    "MoELayerOpts", "layer_opts", "moe_wall_clock_hz", "MoEError",
+    "MOE_DISPATCH_PACKED", "MOE_DISPATCH_GATHER", "MOE_ORDER_BY_KIND", "MOE_ORDER_READY_DOWN",
+    "MOE_ORDER_LEAD", "MOE_ORDER_COMBINE_FIRST",
     "MOE_BF16", "MOE_F32",
 ]
 
@@ -34,6 +35,8 @@ _LIB = os.path.join(_HERE, "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 
 MOE_BF16, MOE_F32 = 0, 1
+MOE_DISPATCH_PACKED, MOE_DISPATCH_GATHER = 0, 1
+MOE_ORDER_BY_KIND, MOE_ORDER_READY_DOWN, MOE_ORDER_LEAD, MOE_ORDER_COMBINE_FIRST = 0, 1, 2, 3
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_TIMEOUT"}
 
@@ -51,6 +54,40 @@ class MoEDims(C.Structure):
     def make(cls, T, d, f, E, k, e_lo=0, e_hi=None) -> "MoEDims":
         return cls(int(T), int(d), int(f), int(E), int(k), int(e_lo),
                    int(E if e_hi is None else e_hi))
+
+
+class MoELayerOpts(C.Structure):
+    """Per-call options of moe_layer / moe_layer_fp8 (include/moe.h)."""
+    _fields_ = [("dispatch", C.c_int32), ("tile_order", C.c_int32), ("lead", C.c_int32),
+                ("perturb_seed", C.c_uint32), ("wait_timeout_us", C.c_int64),
+                ("trace", C.c_void_p), ("trace_records", C.c_int64),
+                ("events", C.c_void_p * 4)]
+
+
+def _event_handle(ev) -> Optional[int]:
+    """hipEvent_t of a torch.cuda.Event (created on first record)."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return int(ev.cuda_event)
+
+
+def layer_opts(dispatch: int = MOE_DISPATCH_PACKED, tile_order: int = MOE_ORDER_BY_KIND,
+               lead: int = 0, perturb_seed: int = 0, wait_timeout_us: int = 0, trace=None,
+               trace_records: int = 0, events=None) -> MoELayerOpts:
+    """Build a MoELayerOpts.  trace: int64 device tensor of 1 + 4*trace_records
+    elements (element 0 zeroed by the caller); events: up to 4 torch.cuda.Event
+    (or None) recorded before the route, after the route, after the permute
+    and after the last launch."""
+    o = MoELayerOpts()
+    o.dispatch, o.tile_order, o.lead = int(dispatch), int(tile_order), int(lead)
+    o.perturb_seed, o.wait_timeout_us = int(perturb_seed), int(wait_timeout_us)
+    if trace is not None:
+        o.trace, o.trace_records = trace.data_ptr(), int(trace_records)
+    for i, ev in enumerate(list(events or [])[:4]):
+        o.events[i] = _event_handle(ev)
+    return o
 
 
 def lib_path() -> str:
@@ -75,6 +112,10 @@ def load():
         "moe_version": ([], i32),
         "moe_route_workspace_bytes": ([dp], sz),
         "moe_route": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_route_bounds": ([dp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_probe_mfma": ([i32, i64, i32, vp, vp, vp, vp, vp], i32),
+        "moe_gate_up_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_down_fp8": ([dp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_permute_workspace_bytes": ([dp], sz),
         "moe_permute": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_expert_ffn_workspace_bytes": ([dp], sz),
@@ -83,17 +124,13 @@ def load():
         "moe_expert_ffn_fp8_workspace_bytes": ([dp], sz),
         "moe_expert_ffn_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_layer_fp8_workspace_bytes": ([dp], sz),
-        "moe_layer_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
+        "moe_layer_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz,
+                           C.POINTER(MoELayerOpts), vp], i32),
         "moe_combine": ([dp, vp, vp, vp, vp, i32, vp], i32),
         "moe_layer_workspace_bytes": ([dp], sz),
-        "moe_layer": ([dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
+        "moe_layer": ([dp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, C.POINTER(MoELayerOpts),
+                       vp], i32),
         "moe_device_status": ([dp, vp, sz, vp], i32),
-        "moe_timing_enable": ([i32], None),
-        "moe_timing_read": ([C.POINTER(C.c_float), i32], i32),
-        "moe_set_wait_timeout_us": ([i64], None),
-        "moe_set_gather_dispatch": ([i32], None),
-        "moe_set_tile_order": ([i32], i32),
-        "moe_set_trace": ([vp, i64], None),
         "moe_wall_clock_hz": ([], i64),
     }
     for name, (args, res) in sig.items():
@@ -148,9 +185,16 @@ def _require(t, dtype, shape, name):
                          f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
 
 
-def _workspace(nbytes: int, device):
+def _workspace(nbytes: int, device, stream=None):
+    """A workspace allocated here for one call.  Allocated on torch's current
+    stream; if the call runs on another stream, that use is recorded so the
+    caching allocator does not hand the block out before the call's kernels
+    are done with it."""
     import torch
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
 
 
 # ------------------------------------------------------------------ ABI calls
@@ -197,12 +241,49 @@ def moe_route(dims, x, w_router, bias=None, topk_ids=None, topk_w=None, logits=N
         logits = torch.empty((D.T, D.E), dtype=torch.float32, device=dev)
     if ws is None and use_workspace:
         nb = moe_route_workspace_bytes(D)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb > 0 else None
+        ws = _workspace(nb, dev, stream) if nb > 0 else None
     rc = load().moe_route(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(topk_ids),
                           _ptr(topk_w), _ptr(logits), _ptr(ws),
                           ws.numel() if ws is not None else 0, _stream(stream))
     _check(rc, "moe_route")
     return topk_ids, topk_w, logits
+
+
+def moe_route_bounds(dims, x, w_router, bias=None, approx=None, eps=None, ws=None, stream=None):
+    """The fast router's approximate logits and their error bounds (E > 16).
+    Returns (approx f32 [T,E], eps f32 [T,E])."""
+    import torch
+    D = _dims(dims)
+    dev = x.device
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(w_router, torch.bfloat16, (D.E, D.d), "w_router")
+    if bias is not None:
+        _require(bias, torch.float32, (D.E,), "bias")
+    approx = torch.empty((D.T, D.E), dtype=torch.float32, device=dev) if approx is None else approx
+    eps = torch.empty((D.T, D.E), dtype=torch.float32, device=dev) if eps is None else eps
+    ws = _workspace(moe_route_workspace_bytes(D), dev, stream) if ws is None else ws
+    rc = load().moe_route_bounds(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(approx),
+                                 _ptr(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(rc, "moe_route_bounds")
+    return approx, eps
+
+
+def moe_probe_mfma(kind: int, a, b, c, d=None, stream=None):
+    """Matrix-core probe: kind 0 bf16 (a, b bf16 [n, steps, 32, 16]), kind 1
+    E4M3 (a, b uint8 [n, steps, 32, 64]); c f32 [n, 32, 32].  Returns d =
+    c + sum over steps of a_s . b_s^T as computed by the matrix cores."""
+    import torch
+    want = (torch.bfloat16, 16) if kind == 0 else (torch.uint8, 64)
+    if a.dtype != want[0] or b.dtype != want[0] or a.dim() != 4 or tuple(a.shape) != tuple(b.shape) \
+            or tuple(a.shape[2:]) != (32, want[1]) or not a.is_contiguous() or not b.is_contiguous():
+        raise ValueError("a, b: contiguous [n, steps, 32, K] operands of the probe's kind")
+    n, steps = int(a.shape[0]), int(a.shape[1])
+    _require(c, torch.float32, (n, 32, 32), "c")
+    d = torch.empty_like(c) if d is None else d
+    _check(load().moe_probe_mfma(int(kind), n, steps, _ptr(a), _ptr(b), _ptr(c), _ptr(d),
+                                 _stream(stream)), "moe_probe_mfma")
+    return d
 
 
 def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv_perm=None,
@@ -221,7 +302,7 @@ def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv
     inv_perm = torch.empty((D.T, D.k), dtype=torch.int32, device=dev) if inv_perm is None else inv_perm
     x_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if x_perm is None else x_perm
     need = moe_permute_workspace_bytes(D)
-    ws = _workspace(need, dev) if ws is None else ws
+    ws = _workspace(need, dev, stream) if ws is None else ws
     rc = load().moe_permute(C.byref(D), _ptr(x), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
                             _ptr(perm_src), _ptr(inv_perm), _ptr(x_perm), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream))
@@ -230,8 +311,9 @@ def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv
 
 
 def moe_expert_ffn(dims, x_perm, offsets, w_gate, w_up, w_down, y_perm=None, ws=None,
-                   stream=None):
-    """Grouped SwiGLU FFN over expert-contiguous rows.  Returns y_perm bf16 [T*k, d]."""
+                   check_status: bool = False, stream=None):
+    """Grouped SwiGLU FFN over expert-contiguous rows.  Returns y_perm bf16 [T*k, d].
+    check_status: synchronise and raise MoEError on a nonzero device status."""
     import torch
     D = _dims(dims)
     dev = x_perm.device
@@ -244,11 +326,13 @@ def moe_expert_ffn(dims, x_perm, offsets, w_gate, w_up, w_down, y_perm=None, ws=
         raise ValueError("x_perm must have at least T*k rows of d")
     y_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if y_perm is None else y_perm
     need = moe_expert_ffn_workspace_bytes(D)
-    ws = _workspace(need, dev) if ws is None else ws
+    ws = _workspace(need, dev, stream) if ws is None else ws
     rc = load().moe_expert_ffn(C.byref(D), _ptr(x_perm), _ptr(offsets), _ptr(w_gate), _ptr(w_up),
                                _ptr(w_down), _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(),
                                _stream(stream))
     _check(rc, "moe_expert_ffn")
+    if check_status:
+        _check(moe_device_status(D, ws, stream), "moe_expert_ffn (device status)")
     return y_perm
 
 
@@ -290,12 +374,55 @@ def moe_expert_ffn_fp8(dims, x_perm, offsets, wq_gate, s_gate, wq_up, s_up, wq_d
         raise ValueError("x_perm must be bf16 with at least T*k rows of d")
     y_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if y_perm is None else y_perm
     need = moe_expert_ffn_fp8_workspace_bytes(D)
-    ws = _workspace(need, dev) if ws is None else ws
+    ws = _workspace(need, dev, stream) if ws is None else ws
     rc = load().moe_expert_ffn_fp8(C.byref(D), _ptr(x_perm), _ptr(offsets), _ptr(wq_gate),
                                    _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(wq_down),
                                    _ptr(s_down), _ptr(y_perm), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "moe_expert_ffn_fp8")
+    return y_perm
+
+
+def moe_gate_up_fp8(dims, x_perm, offsets, wq_gate, s_gate, wq_up, s_up, h=None, ws=None,
+                    stream=None):
+    """GEMM0 + SiLU-mul of the W8A8 FFN.  Returns h bf16 [T*k, f]."""
+    import torch
+    D = _dims(dims)
+    dev = x_perm.device
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(wq_gate, torch.uint8, (EL, D.f, D.d), "wq_gate")
+    _require(wq_up, torch.uint8, (EL, D.f, D.d), "wq_up")
+    _require(s_gate, torch.float32, (EL, D.f), "s_gate")
+    _require(s_up, torch.float32, (EL, D.f), "s_up")
+    _require(offsets, torch.int32, (EL + 1,), "offsets")
+    if x_perm.dtype != torch.bfloat16 or x_perm.shape[0] < cap or x_perm.shape[1] != D.d:
+        raise ValueError("x_perm must be bf16 with at least T*k rows of d")
+    h = torch.empty((max(cap, 1), D.f), dtype=torch.bfloat16, device=dev) if h is None else h
+    ws = _workspace(moe_expert_ffn_fp8_workspace_bytes(D), dev, stream) if ws is None else ws
+    rc = load().moe_gate_up_fp8(C.byref(D), _ptr(x_perm), _ptr(offsets), _ptr(wq_gate),
+                                _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(h), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "moe_gate_up_fp8")
+    return h
+
+
+def moe_down_fp8(dims, h, offsets, wq_down, s_down, y_perm=None, ws=None, stream=None):
+    """GEMM1 of the W8A8 FFN on bf16 rows h [T*k, f].  Returns y_perm bf16 [T*k, d]."""
+    import torch
+    D = _dims(dims)
+    dev = h.device
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(wq_down, torch.uint8, (EL, D.d, D.f), "wq_down")
+    _require(s_down, torch.float32, (EL, D.d), "s_down")
+    _require(offsets, torch.int32, (EL + 1,), "offsets")
+    if h.dtype != torch.bfloat16 or h.shape[0] < cap or h.shape[1] != D.f:
+        raise ValueError("h must be bf16 with at least T*k rows of f")
+    y_perm = torch.empty((max(cap, 1), D.d), dtype=torch.bfloat16, device=dev) if y_perm is None else y_perm
+    ws = _workspace(moe_expert_ffn_fp8_workspace_bytes(D), dev, stream) if ws is None else ws
+    rc = load().moe_down_fp8(C.byref(D), _ptr(h), _ptr(offsets), _ptr(wq_down), _ptr(s_down),
+                             _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream(stream))
+    _check(rc, "moe_down_fp8")
     return y_perm
 
 
@@ -305,7 +432,7 @@ def moe_layer_fp8_workspace_bytes(dims) -> int:
 
 def moe_layer_fp8(dims, x, w_router, wq_gate, s_gate, wq_up, s_up, wq_down, s_down, bias=None,
                   out=None, out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None,
-                  ws=None, stream=None):
+                  ws=None, opts: Optional[MoELayerOpts] = None, stream=None):
     """Forward pass with the W8A8 expert FFN (staged).  Returns out [T, d]."""
     import torch
     D = _dims(dims)
@@ -324,11 +451,12 @@ def moe_layer_fp8(dims, x, w_router, wq_gate, s_gate, wq_up, s_up, wq_down, s_do
     dt = torch.float32 if out_dtype == MOE_F32 else torch.bfloat16
     out = torch.empty((D.T, D.d), dtype=dt, device=dev) if out is None else out
     need = moe_layer_fp8_workspace_bytes(D)
-    ws = _workspace(need, dev) if ws is None else ws
+    ws = _workspace(need, dev, stream) if ws is None else ws
     rc = load().moe_layer_fp8(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(wq_gate),
                               _ptr(s_gate), _ptr(wq_up), _ptr(s_up), _ptr(wq_down), _ptr(s_down),
                               _ptr(out), out_dtype, _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream))
+                              ws.numel() * ws.element_size(),
+                              C.byref(opts) if opts is not None else None, _stream(stream))
     _check(rc, "moe_layer_fp8")
     return out
 
@@ -350,8 +478,10 @@ def moe_combine(dims, y_perm, inv_perm, topk_w, out=None, out_dtype: int = MOE_B
 
 def moe_layer(dims, x, w_router, w_gate, w_up, w_down, bias=None, out=None,
               out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None, ws=None,
-              stream=None):
-    """Whole layer forward.  Returns out [T, d]."""
+              opts: Optional[MoELayerOpts] = None, check_status: bool = False, stream=None):
+    """Whole layer forward.  Returns out [T, d].  opts: a MoELayerOpts (see
+    layer_opts) or None for the defaults.  check_status: synchronise and raise
+    MoEError if a device-side wait timed out (the workspace's status word)."""
     import torch
     D = _dims(dims)
     dev = x.device
@@ -366,49 +496,20 @@ def moe_layer(dims, x, w_router, w_gate, w_up, w_down, bias=None, out=None,
     dt = torch.float32 if out_dtype == MOE_F32 else torch.bfloat16
     out = torch.empty((D.T, D.d), dtype=dt, device=dev) if out is None else out
     need = moe_layer_workspace_bytes(D)
-    ws = _workspace(need, dev) if ws is None else ws
+    ws = _workspace(need, dev, stream) if ws is None else ws
     rc = load().moe_layer(C.byref(D), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate),
                           _ptr(w_up), _ptr(w_down), _ptr(out), int(out_dtype), _ptr(topk_ids_out),
                           _ptr(topk_w_out), _ptr(ws), ws.numel() * ws.element_size(),
-                          _stream(stream))
+                          C.byref(opts) if opts is not None else None, _stream(stream))
     _check(rc, "moe_layer")
+    if check_status:
+        _check(moe_device_status(D, ws, stream), "moe_layer (device status)")
     return out
 
 
 def moe_device_status(dims, ws, stream=None) -> int:
     return int(load().moe_device_status(C.byref(_dims(dims)), _ptr(ws),
                                         ws.numel() * ws.element_size(), _stream(stream)))
-
-
-def moe_timing_enable(on: bool = True) -> None:
-    load().moe_timing_enable(1 if on else 0)
-
-
-def moe_timing_read() -> Tuple[int, Tuple[float, float, float]]:
-    arr = (C.c_float * 3)()
-    n = load().moe_timing_read(arr, 3)
-    return int(n), (arr[0], arr[1], arr[2])
-
-
-def moe_set_wait_timeout_us(us: int) -> None:
-    load().moe_set_wait_timeout_us(int(us))
-
-
-def moe_set_gather_dispatch(on: bool = True) -> None:
-    """moe_layer dispatch mode: gather rows of x on load (True) or packed x_perm (False)."""
-    load().moe_set_gather_dispatch(1 if on else 0)
-
-
-def moe_set_tile_order(policy: int = 0) -> None:
-    """Persistent-kernel tile order of moe_layer: 0 by kind, 1 interleaved
-    (ready down tiles between gate/up tiles).  Same output bits."""
-    _check(load().moe_set_tile_order(int(policy)), "moe_set_tile_order")
-
-
-def moe_set_trace(buf=None, n_records: int = 0) -> None:
-    """Per-tile trace of moe_layer into an int64 device tensor of 1 + 4*n_records
-    elements (element 0 = record count, zero it first); None turns it off."""
-    load().moe_set_trace(_ptr(buf), int(n_records) if buf is not None else 0)
 
 
 def moe_wall_clock_hz() -> int:

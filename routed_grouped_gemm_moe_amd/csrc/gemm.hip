@@ -114,7 +114,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
         // a cut tile computes K part `part`, starting at k = part * f / S
         const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
         const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
-        const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (CUT_MAX * BM * BN_DN), part, S};
+        const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (CUT_MAX * BM * BN_DN), part, S, 0};
         gemm_tile_pa<PA_BF16>(A + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, wd,
                               nullptr, f, out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
                               part < 0 ? nullptr : &sc);

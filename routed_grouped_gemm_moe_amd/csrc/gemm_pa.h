@@ -196,6 +196,7 @@ struct SplitCtl {
     float *part;  // nparts x (256 x 256) floats, each in accumulator-register order
     int self;     // which part this call computes (0 .. nparts-1)
     int nparts;   // 2 or 4
+    int sleeps;   // schedule perturbation: s_sleep(127) count before arriving
 };
 
 // Float offset of accumulator vector (wave, i, j, v/4 = g) of lane `lane`:
@@ -232,6 +233,7 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
     __syncthreads();
     int *s_x = reinterpret_cast<int *>(lds);
     if (wave == 0) {
+        for (int i = 0; i < sp.sleeps; ++i) __builtin_amdgcn_s_sleep(127);
         // lane 0 adds 1, the others 0: lane 0's pre-op value is the arrival
         const int old = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
             sp.cnt, lane == 0 ? 1 : 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));

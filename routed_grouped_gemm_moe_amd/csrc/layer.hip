@@ -18,7 +18,7 @@
 // GEMM tiles are those of gemm_pa.h: x_perm and h are in its packed layout
 // (h written by the gate/up epilogue, read as the down tiles' A operand).
 //
-// Interleaved order (moe_set_tile_order(1)): before each gate/up claim a
+// Interleaved order (MOE_ORDER_READY_DOWN): before each gate/up claim a
 // workgroup takes the next down tile of its XCD's range if that tile's m-tile
 // has all its gate/up tiles published (compare-and-swap, so only a ready
 // tile is taken); such a tile never waits, so the argument below holds.
@@ -71,9 +71,35 @@ __device__ __forceinline__ int hw_xcd() {
     return id & (NUM_XCD - 1);
 }
 
+// Schedule perturbation (a test aid for the flag protocol, off when the seed
+// is 0): a pseudo-random delay, from the seed, the tile kind and the tile
+// index, that a producer waits between writing its output and publishing it
+// -- a quarter of the tiles wait 0 to 24 sleeps of 8128 clocks (about 100 us
+// at most), far below the wait bound -- and claims taken from the far end of
+// each range.  Consumers that did not wait correctly would then read
+// unwritten rows.  Results are unchanged.
+__device__ __forceinline__ uint32_t perturb_hash(uint32_t seed, uint32_t kind, uint32_t tile) {
+    uint32_t h = seed ^ (kind * 0x9E3779B9u) ^ (tile * 0x85EBCA6Bu);
+    h ^= h >> 16;
+    h *= 0x7FEB352Du;
+    h ^= h >> 15;
+    h *= 0x846CA68Bu;
+    h ^= h >> 16;
+    return h;
+}
+__device__ __forceinline__ int perturb_sleeps(uint32_t seed, uint32_t kind, uint32_t tile) {
+    if (!seed) return 0;
+    const uint32_t h = perturb_hash(seed, kind, tile);
+    return (h & 3u) == 0 ? (int)((h >> 2) % 25u) : 0;
+}
+__device__ __forceinline__ void sleep_units(int n) {  // n wave-uniform
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
 // Claim one tile of [0, n) for the calling wave.  Queue y covers
-// [y*per, y*per + per); the own XCD's queue first, then the others.
-__device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd) {
+// [y*per, y*per + per); the own XCD's queue first, then the others.  With
+// rev, each range is handed out from its far end.
+__device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd, bool rev = false) {
     const int per = (n + NUM_XCD - 1) / NUM_XCD;
     for (int r = 0; r < NUM_XCD; ++r) {
         const int y = (xcd + r) & (NUM_XCD - 1);
@@ -86,7 +112,7 @@ __device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd) {
         // lane 0 adds 1, the others 0: lane 0's pre-op value is the claim
         const int old = uniform(__hip_atomic_fetch_add(c, lane_id() == 0 ? 1 : 0,
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (old < len) return lo + old;
+        if (old < len) return lo + (rev ? len - 1 - old : old);
     }
     return -1;
 }
@@ -108,18 +134,19 @@ __device__ __forceinline__ int claim_ready_down(const LayerArgs &a, int32_t *q, 
     int32_t *c = q + xcd * QSTRIDE;
     const int cur = uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (cur >= len) return -1;
+    const int idx = lo + (a.perturb ? len - 1 - cur : cur);
     int L, part, st, mt, nt;
-    dn_claim(lo + cur, n2, nsp, S, &L, &part, &st);
+    dn_claim(idx, n2, nsp, S, &L, &part, &st);
     expert_tile(L, MT, NT2, (int)a.D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
     if (uniform(__hip_atomic_load(a.gu_done + mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
         NT1)
         return -1;
     const int old = uniform(atomicCAS(c, cur, lane_id() == 0 ? cur + 1 : cur));
-    return old == cur ? lo + cur : -1;
+    return old == cur ? idx : -1;
 }
 
-__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim) {
-    if (wave_id() == 0) *s_claim = claim_tile(q, n, xcd);  // all lanes store the same value
+__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim, bool rev) {
+    if (wave_id() == 0) *s_claim = claim_tile(q, n, xcd, rev);  // all lanes store the same value
     __syncthreads();
     const int L = uniform(*s_claim);
     __syncthreads();
@@ -150,13 +177,15 @@ __device__ __forceinline__ void wave_wait_geq(const int32_t *p, int32_t target, 
 }
 
 // Publish a finished tile: every wave's stores have completed (reached L2)
-// before the barrier; then wave 0 optionally records its XCD in *xmask and
-// bumps (add) or sets (store 1) the counter with one agent-scope release,
-// which writes this XCD's L2 back first.
-__device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, int xcd) {
+// before the barrier; then wave 0 (after the perturbation delay, if any)
+// optionally records its XCD in *xmask and bumps (add) or sets (store 1) the
+// counter with one agent-scope release, which writes this XCD's L2 back first.
+__device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, int xcd,
+                                        int sleeps) {
     wait_vmcnt<0>();
     __syncthreads();
     if (wave_id() == 0) {
+        sleep_units(sleeps);
         const bool l0 = lane_id() == 0;
         if (xmask)
             __hip_atomic_fetch_or(xmask, l0 ? (1 << xcd) : 0, __ATOMIC_RELAXED,
@@ -217,7 +246,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
     const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
     const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
     const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
-                      S};
+                      S, perturb_sleeps(a.perturb, 4, (uint32_t)LS)};
     const bool wrote = gemm_tile_pa<PA_BF16>(
         a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
         nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
@@ -226,13 +255,82 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
         trace_tile(a, 4, LS, xcd, t0);
         return;
     }
-    publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd);
+    publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
+            perturb_sleeps(a.perturb, 2, (uint32_t)LS));
     // count published down tiles (after the release above, so a
     // reader that sees the full count also sees every y row)
-    if (wave_id() == 0)
+    if (wave_id() == 0) {
         __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.dn_cg + nt / COMB_CB, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
     trace_tile(a, part < 0 ? 2 : 4, LS, xcd, t0);
+}
+
+// Combine-first order: the next combine tile of the first range whose next
+// tile's column group has every down tile published (the group's count in
+// dn_cg), claimed with a compare-and-swap as in claim_ready_down; -1 if none
+// is ready.  Such a tile's flag waits pass at once, so it never blocks.
+__device__ __forceinline__ int claim_ready_combine(const LayerArgs &a, int32_t *q, int n3,
+                                                   int NTB, int NT2, int MT, bool rev) {
+    const int per = (n3 + NUM_XCD - 1) / NUM_XCD;
+    for (int y = 0; y < NUM_XCD; ++y) {
+        const int lo = y * per;
+        const int len = min(n3, lo + per) - lo;
+        if (len <= 0) break;
+        int32_t *c = q + y * QSTRIDE;
+        const int cur = uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (cur >= len) continue;
+        const int idx = lo + (rev ? len - 1 - cur : cur);
+        const int cg = idx / NTB;
+        const int ncb = min(COMB_CB, NT2 - cg * COMB_CB);
+        if (uniform(__hip_atomic_load(a.dn_cg + cg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+            MT * ncb)
+            continue;
+        const int old = uniform(atomicCAS(c, cur, lane_id() == 0 ? cur + 1 : cur));
+        return old == cur ? idx : -1;
+    }
+    return -1;
+}
+
+// One combine tile L (COMB_TOK tokens x up to COMB_CB column blocks of
+// BN_DN): every (token, slot) waits for the down tile holding its row --
+// unless every down tile has already been published -- then the gated sum.
+template <bool OUT_F32>
+__device__ __forceinline__ void combine_tile(const LayerArgs &a, int L, int NTB, int NT2, int n2,
+                                             int xcd, bool &all_done, char *lds) {
+    const Dims &D = a.D;
+    const int64_t d = D.d, k = D.k;
+    const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+    const int cg = L / NTB, tb = L % NTB;
+    const int nt0 = cg * COMB_CB, ncb = min(COMB_CB, NT2 - nt0);
+    if (!all_done)  // stays true once seen
+        all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) >= n2;
+    for (int base = 0; !all_done && base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
+        const int i = base + (int)threadIdx.x;
+        const int64_t t = (int64_t)tb * COMB_TOK + i / k;
+        const int64_t j = i % k;
+        bool need = false;
+        int32_t mt = 0;
+        if (i < COMB_TOK * k && t < D.T) {
+            const int32_t p = a.inv_perm[t * k + j];
+            if (p >= 0) {
+                const int32_t e = a.ids[t * k + j] - (int32_t)D.e_lo;
+                mt = a.mtile_base[e] + (p - a.offsets[e]) / BM;
+                need = true;
+            }
+        }
+        for (int c = 0; c < ncb; ++c)
+            wave_wait_geq(a.dn_flag + (int64_t)mt * NT2 + nt0 + c, 1, need, a.wait_ticks,
+                          a.status);
+    }
+    __syncthreads();
+    combine_tile_staged<OUT_F32, COMB_TOK, BN_DN / 8, GEMM_THREADS>(
+        (int64_t)tb * COMB_TOK, D.T, (int64_t)nt0 * (BN_DN / 8), ncb, d, k, a.y, a.inv_perm,
+        a.gates, a.out, lds);
+    trace_tile(a, 3, L, xcd, t0);
 }
 
 template <bool OUT_F32>
@@ -244,7 +342,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
     const int MT = *a.n_mtiles;
     const int NT1 = (int)D.nt_gu();
     const int NT2 = (int)D.nt_dn();
-    const int64_t d = D.d, f = D.f, k = D.k;
+    const int64_t d = D.d, f = D.f;
+    const bool rev = a.perturb != 0;  // claims from the far end of each range
 
     // down claims: those of the last partial round (of gridDim.x workgroups)
     // are cut into S K parts, claimed after the whole tiles
@@ -253,40 +352,75 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
     const int nsp = dn_split_tiles(S, n2, (int)gridDim.x);
     const int n2c = n2 + (S - 1) * nsp;
 
-    // 1. gate/up tiles, then 2. down tiles, in one claim loop (so each tile
-    // body is instantiated once).  Phase 1 claims gate/up tiles -- with the
-    // interleaved order a ready down tile of this XCD's range first (kind bit
-    // 1 << 30) -- and phase 2, once every gate/up range is drained, the
-    // remaining down claims.
+    // combine tiles: COMB_TOK tokens x up to COMB_CB column blocks, column
+    // group major (tile L covers column group L / NTB)
+    const int NTB = (int)D.comb_blocks();
+    const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
+    const int n3 = NTB * NCG;
+    int32_t *const q1 = a.queues, *const q2 = a.queues + NUM_XCD * QSTRIDE,
+                   *const q3 = a.queues + 2 * NUM_XCD * QSTRIDE;
+    bool all_done = false;
+
+    // 1. gate/up tiles, 2. down tiles, 3. combine tiles, in one claim loop
+    // (so each tile body is instantiated once).  Phase 1 claims gate/up tiles
+    // -- with the ready-down order a ready down tile of this XCD's range first
+    // (kind bit DOWN) -- phase 2, once every gate/up range is drained, the
+    // down claims: with the combine-first order through the column-group-
+    // sorted table, each preceded by a try for a combine tile whose column
+    // group is complete (kind bit COMB) -- and phase 3 the remaining combine
+    // tiles.  The dependency-lead order replaces phases 1 and 2 by phase 0:
+    // the merged stream of its table, in the gate/up queues.
     const int n1 = MT * NT1;
-    constexpr int DOWN = 1 << 30;
-    int phase = n1 > 0 ? 1 : 2;
-    if (n1 > 0 || n2 > 0)
+    constexpr int DOWN = 1 << 30, COMB = 1 << 29;
+    const int nM = a.order == 2 ? n1 + n2c : 0;
+    int phase = a.order == 2 ? 0 : n1 > 0 ? 1 : 2;
+    if (n1 > 0 || n2 > 0 || n3 > 0)
         for (;;) {
             if (wave_id() == 0) {
                 int v;
-                if (phase == 1) {
-                    const int r = a.interleave && n2 > 0
-                                      ? claim_ready_down(a, a.queues + NUM_XCD * QSTRIDE, n2c, n2,
-                                                         nsp, S, MT, NT1, NT2, xcd)
+                if (phase == 0) {
+                    const int p = claim_tile(q1, nM, xcd);  // never reversed: see launch_build_order
+                    v = p >= 0 ? uniform(a.order_tab[p]) : -1;
+                } else if (phase == 1) {
+                    const int r = a.order == 1 && n2 > 0
+                                      ? claim_ready_down(a, q2, n2c, n2, nsp, S, MT, NT1, NT2, xcd)
                                       : -1;
-                    v = r >= 0 ? (r | DOWN) : claim_tile(a.queues, n1, xcd);
+                    v = r >= 0 ? (r | DOWN) : claim_tile(q1, n1, xcd, rev);
                     if (v < 0) v = -2;  // gate/up drained: move to phase 2
+                } else if (phase == 2) {
+                    const int c = a.order == 3 && n3 > 0
+                                      ? claim_ready_combine(a, q3, n3, NTB, NT2, MT, rev)
+                                      : -1;
+                    if (c >= 0) {
+                        v = c | COMB;
+                    } else {
+                        const int r = n2 > 0 ? claim_tile(q2, n2c, xcd, rev) : -1;
+                        v = r < 0 ? -3 : (a.order == 3 ? uniform(a.order_tab[r]) : r) | DOWN;
+                    }
                 } else {
-                    const int r =
-                        n2 > 0 ? claim_tile(a.queues + NUM_XCD * QSTRIDE, n2c, xcd) : -1;
-                    v = r >= 0 ? (r | DOWN) : -1;
+                    const int c = n3 > 0 ? claim_tile(q3, n3, xcd, rev) : -1;
+                    v = c < 0 ? -1 : c | COMB;
                 }
                 s_claim = v;  // every lane stores the same value
             }
             __syncthreads();
             const int v = uniform(s_claim);
             __syncthreads();
-            if (v == -2) {
-                phase = 2;
+            if (v == -2 || v == -3) {  // a kind drained: the next phase
+                phase = v == -2 ? 2 : 3;
                 continue;
             }
-            if (v < 0) break;
+            if (v < 0) {
+                if (phase == 0) {  // the merged stream is drained: combine tiles
+                    phase = 3;
+                    continue;
+                }
+                break;
+            }
+            if (v & COMB) {
+                combine_tile<OUT_F32>(a, v & ~COMB, NTB, NT2, n2, xcd, all_done, lds);
+                continue;
+            }
             if (v & DOWN) {
                 down_tile(a, v & ~DOWN, n2, nsp, S, MT, NT1, NT2, xcd, lds);
                 continue;
@@ -307,55 +441,149 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 gemm_tile_pa<PA_SILU_PACKED>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
                                              (int)d, a.w_gate + wo, a.w_up + wo, d, ho, f / 16,
                                              lds);
-            publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd);
+            publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
+                    perturb_sleeps(a.perturb, 1, (uint32_t)L));
             trace_tile(a, 1, L, xcd, t0);
         }
 
-    // 3. combine tiles
-    // tile = COMB_TOK tokens x up to COMB_CB column blocks of BN_DN
-    const int NTB = (int)D.comb_blocks();
-    const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
-    const int n3 = NTB * NCG;
-    bool all_done = false;
-    if (n3 > 0)
-        for (;;) {
-            const int L = next_tile(a.queues + 2 * NUM_XCD * QSTRIDE, n3, xcd, &s_claim);
-            if (L < 0) break;
-            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
-            const int cg = L / NTB, tb = L % NTB;
-            const int nt0 = cg * COMB_CB, ncb = min(COMB_CB, NT2 - nt0);
-            // every (token, slot) of the tile waits for the down tile holding its
-            // row -- unless every down tile has already been published
-            if (!all_done)  // stays true once seen
-                all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)) >= n2;
-            for (int base = 0; !all_done && base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
-                const int i = base + (int)threadIdx.x;
-                const int64_t t = (int64_t)tb * COMB_TOK + i / k;
-                const int64_t j = i % k;
-                bool need = false;
-                int32_t mt = 0;
-                if (i < COMB_TOK * k && t < D.T) {
-                    const int32_t p = a.inv_perm[t * k + j];
-                    if (p >= 0) {
-                        const int32_t e = a.ids[t * k + j] - (int32_t)D.e_lo;
-                        mt = a.mtile_base[e] + (p - a.offsets[e]) / BM;
-                        need = true;
-                    }
-                }
-                for (int c = 0; c < ncb; ++c)
-                    wave_wait_geq(a.dn_flag + (int64_t)mt * NT2 + nt0 + c, 1, need, a.wait_ticks,
-                                  a.status);
-            }
-            __syncthreads();
-            combine_tile_staged<OUT_F32, COMB_TOK, BN_DN / 8, GEMM_THREADS>(
-                (int64_t)tb * COMB_TOK, D.T, (int64_t)nt0 * (BN_DN / 8), ncb, d, k, a.y,
-                a.inv_perm, a.gates, a.out, lds);
-            trace_tile(a, 3, L, xcd, t0);
+}
+
+// Position, in the gate/up blocked order (expert_tile), of the last gate/up
+// tile of m-tile mt: group [g0, g0 + s) is swept n-tile-major, so m-tile mt's
+// tiles sit at g0 * NT1 + nt * s + (mt - g0).
+__device__ __forceinline__ int gu_last_pos(int mt, int MT, int NT1, int EL, const MTile *mtiles,
+                                           const int32_t *mtile_base) {
+    const int e = mtiles[mt].e;
+    const int base = mtile_base[e];
+    const int end = e + 1 < EL ? mtile_base[e + 1] : MT;
+    const int g0 = base + (mt - base) / GM_MAX * GM_MAX;
+    const int s = min(GM_MAX, end - g0);
+    return g0 * NT1 + (NT1 - 1) * s + (mt - g0);
+}
+
+// Claim tables of the tile orders that are not plain queues; one workgroup.
+//
+// Order 2 (dependency lead, X-Stage §4.3): gate/up tiles i (blocked order) and
+// down claims LS (dn_claim order) merge into one stream, each kind keeping its
+// own order, with a down claim placed as soon as at least `lead` gate/up tiles
+// follow the last gate/up tile it reads: need(LS) = last(m-tile) + 1 + lead
+// gate/up tiles before it (at most n1), P(LS) = the running maximum of need
+// (down claims keep their order), so down claim LS lands at P(LS) + LS and
+// gate/up tile i at i + #{LS : P(LS) <= i}.  Every claim's producers sit at
+// earlier positions of the stream, which the persistent kernel hands out as
+// contiguous per-XCD ranges, own range first; the earliest unfinished claim
+// is therefore always runnable, so the stream cannot deadlock.  (That
+// argument needs claims in increasing order within a range, which is why the
+// schedule perturbation does not reverse this order.)
+//
+// Order 3 (combine first): the down claims of every per-XCD range, stably
+// sorted by the combine column group of their tile (n-tile / COMB_CB), so
+// each XCD finishes its share of column group 0 first.  128 threads per
+// range count their run of claims per group (LDS), exclusive scans give every
+// thread its slots, and a second pass places the claims.
+__global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
+    const Dims &D = a.D;
+    const int MT = *a.n_mtiles;
+    const int NT1 = (int)D.nt_gu(), NT2 = (int)D.nt_dn(), EL = (int)D.EL();
+    const int n1 = MT * NT1, n2 = MT * NT2;
+    const int S = D.dn_parts();
+    const int nsp = dn_split_tiles(S, n2, G);
+    const int n2c = n2 + (S - 1) * nsp;
+    const int tid = threadIdx.x;
+    auto mt_of = [&](int LS, int *nt) {
+        int L, part, st, mt;
+        dn_claim(LS, n2, nsp, S, &L, &part, &st);
+        expert_tile(L, MT, NT2, EL, a.mtiles, a.mtile_base, &mt, nt);
+        return mt;
+    };
+    if (a.order == 2) {
+        __shared__ int s_pre[1024];
+        int32_t *P = a.order_tmp;
+        const int q = (n2c + 1023) / 1024, lo = min(n2c, tid * q), hi = min(n2c, lo + q);
+        int m = -1;
+        for (int LS = lo; LS < hi; ++LS) {
+            int nt;
+            const int mt = mt_of(LS, &nt);
+            const int need = min(n1, gu_last_pos(mt, MT, NT1, EL, a.mtiles, a.mtile_base) + 1 +
+                                         a.lead);
+            m = max(m, need);
+            P[LS] = m;
         }
+        s_pre[tid] = m;
+        __syncthreads();
+        for (int w = 1; w < 1024; w <<= 1) {  // inclusive max-scan over the threads
+            const int o = tid >= w ? s_pre[tid - w] : -1;
+            __syncthreads();
+            s_pre[tid] = max(s_pre[tid], o);
+            __syncthreads();
+        }
+        const int before = tid > 0 ? s_pre[tid - 1] : -1;
+        for (int LS = lo; LS < hi; ++LS) {
+            const int p = max(P[LS], before);
+            P[LS] = p;
+            a.order_tab[p + LS] = LS | (1 << 30);
+        }
+        __syncthreads();
+        const int q1 = (n1 + 1023) / 1024, lo1 = min(n1, tid * q1), hi1 = min(n1, lo1 + q1);
+        for (int i = lo1; i < hi1; ++i) {
+            int l = 0, h = n2c;  // first LS with P(LS) > i
+            while (l < h) {
+                const int mid = (l + h) >> 1;
+                if (P[mid] <= i) l = mid + 1;
+                else h = mid;
+            }
+            a.order_tab[i + l] = i;
+        }
+    } else if (a.order == 3) {
+        __shared__ int s_cnt[1024][ORDER3_MAX_CG];
+        __shared__ int s_start[NUM_XCD][ORDER3_MAX_CG];
+        const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
+        const int per = (n2c + NUM_XCD - 1) / NUM_XCD;
+        const int r = tid / 128, j = tid % 128;
+        const int rlo = min(n2c, r * per), rhi = min(n2c, rlo + per);
+        const int q = (rhi - rlo + 127) / 128, lo = min(rhi, rlo + j * q), hi = min(rhi, lo + q);
+        for (int c = 0; c < ORDER3_MAX_CG; ++c) s_cnt[tid][c] = 0;
+        for (int LS = lo; LS < hi; ++LS) {
+            int nt;
+            mt_of(LS, &nt);
+            s_cnt[tid][nt / COMB_CB] += 1;
+        }
+        __syncthreads();
+        if (j < NCG) {  // thread (r, c = j): exclusive scan of group c over the range's threads
+            int run = 0;
+            for (int t = 0; t < 128; ++t) {
+                const int v = s_cnt[r * 128 + t][j];
+                s_cnt[r * 128 + t][j] = run;
+                run += v;
+            }
+            s_start[r][j] = run;  // the group's total, turned into its start below
+        }
+        __syncthreads();
+        if (j == 0) {
+            int run = 0;
+            for (int c = 0; c < NCG; ++c) {
+                const int v = s_start[r][c];
+                s_start[r][c] = run;
+                run += v;
+            }
+        }
+        __syncthreads();
+        for (int LS = lo; LS < hi; ++LS) {
+            int nt;
+            mt_of(LS, &nt);
+            const int c = nt / COMB_CB;
+            a.order_tab[rlo + s_start[r][c] + s_cnt[tid][c]++] = LS;
+        }
+    }
 }
 
 }  // namespace
+
+hipError_t launch_build_order(const LayerArgs &a, int grid, hipStream_t s) {
+    if (a.order != 2 && a.order != 3) return hipSuccess;
+    hipLaunchKernelGGL(build_order_kernel, dim3(1), dim3(1024), 0, s, a, grid);
+    return hipGetLastError();
+}
 
 int layer_grid_size() {
     static int cached = 0;

@@ -1,10 +1,8 @@
 // Host runtime of the C ABI declared in include/moe.h: argument checks (run
 // before any HIP call, so they also work on a machine without a GPU),
-// workspace layout, the launch sequences of every entry point, and the
-// optional stage timing used by the benchmark.
-#include <mutex>
-#include <vector>
-
+// workspace layout and the launch sequences of every entry point.  Nothing is
+// kept between calls but a per-device property cache (grid size, clock rate):
+// every option travels with its call.
 #include "moe_internal.h"
 
 namespace moe {
@@ -29,11 +27,17 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.queues = take(layer ? 3 * NUM_XCD * QSTRIDE * sizeof(int32_t) : 0);
     L.gu_done = take(layer ? MT * sizeof(int32_t) : 0);
     L.gu_xcd = take(layer ? MT * sizeof(int32_t) : 0);
+    L.dn_cg = take(layer ? (size_t)comb_groups(D.d) * sizeof(int32_t) : 0);
     L.dn_flag = take(layer ? MT * (size_t)D.nt_dn() * sizeof(int32_t) : 0);
     // cut down tiles (deep down GEMMs only): arrival counters, then partials
     const bool split = ffn && D.dn_parts() > 1;
     L.dn_cnt = take(split ? SPLIT_MAX * sizeof(int32_t) : 0);
     L.dn_part = take(split ? (size_t)SPLIT_MAX * CUT_MAX * BM * BN_DN * sizeof(float) : 0);
+    // claim tables of tile orders 2 and 3 (written whole by their builder)
+    const size_t n1max = MT * (size_t)D.nt_gu();
+    const size_t n2max = MT * (size_t)D.nt_dn() + (CUT_MAX - 1) * (size_t)SPLIT_MAX;
+    L.order_tab = take(layer ? (n1max + n2max) * sizeof(int32_t) : 0);
+    L.order_tmp = take(layer ? n2max * sizeof(int32_t) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
@@ -63,30 +67,6 @@ using namespace moe;
 
 namespace {
 
-std::mutex g_mu;
-int64_t g_wait_us = 2000000;  // device flag-wait timeout
-int64_t *g_trace = nullptr;   // per-tile trace buffer of moe_layer (device), or null
-int64_t g_trace_cap = 0;
-bool g_timing = false;
-bool g_gather = false;  // gather-on-load dispatch in moe_layer
-int g_tile_order = 0;   // persistent-kernel tile order of moe_layer
-struct CallEvents {
-    hipEvent_t ev[4];
-};
-std::vector<CallEvents> g_events;   // recorded, not yet read
-std::vector<hipEvent_t> g_pool;     // free events
-
-hipEvent_t pool_event() {
-    if (!g_pool.empty()) {
-        hipEvent_t e = g_pool.back();
-        g_pool.pop_back();
-        return e;
-    }
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-}
-
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 moe_status check_dims(const moe_dims *dm, Dims *out) {
@@ -110,6 +90,29 @@ moe_status check_ws(void *ws, size_t ws_bytes, size_t need) {
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Range checks of per-call options; the W8A8 layer takes events only.
+moe_status check_opts(const moe_layer_opts *o, bool staged_fp8) {
+    if (!o) return MOE_OK;
+    if (staged_fp8)
+        return (o->dispatch || o->tile_order || o->lead || o->perturb_seed ||
+                o->wait_timeout_us || o->trace || o->trace_records)
+                   ? MOE_ERR_INVALID_ARG
+                   : MOE_OK;
+    if (o->dispatch != MOE_DISPATCH_PACKED && o->dispatch != MOE_DISPATCH_GATHER)
+        return MOE_ERR_INVALID_ARG;
+    if (o->tile_order < MOE_ORDER_BY_KIND || o->tile_order > MOE_ORDER_COMBINE_FIRST)
+        return MOE_ERR_INVALID_ARG;
+    if (o->lead < 0 || o->wait_timeout_us < 0 || o->trace_records < 0) return MOE_ERR_INVALID_ARG;
+    if (o->trace_records > 0 && !o->trace) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// Records opts->events[i] (if given) on the stream.
+hipError_t mark_event(const moe_layer_opts *o, int i, hipStream_t s) {
+    if (!o || !o->events[i]) return hipSuccess;
+    return hipEventRecord((hipEvent_t)o->events[i], s);
+}
 
 }  // namespace
 
@@ -147,6 +150,32 @@ moe_status moe_route(const moe_dims *dims, const void *x, const void *w_router, 
     if (ws && ((uintptr_t)ws & 255u) != 0) return MOE_ERR_WORKSPACE;
     return hip_status(launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, topk_ids,
                                    topk_w, logits, ws, ws ? ws_bytes : 0, (hipStream_t)stream));
+}
+
+moe_status moe_route_bounds(const moe_dims *dims, const void *x, const void *w_router,
+                            const float *bias, float *approx, float *eps, void *ws,
+                            size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (!route_uses_fast_path(D)) return MOE_ERR_UNSUPPORTED;
+    if (D.T == 0) return MOE_OK;
+    if (!x || !w_router || !approx || !eps) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if ((st = check_ws(ws, ws_bytes, route_workspace_bytes(D))) != MOE_OK) return st;
+    return hip_status(launch_route_bounds(D, (const bf16_t *)x, (const bf16_t *)w_router, bias,
+                                          approx, eps, ws, (hipStream_t)stream));
+}
+
+moe_status moe_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
+                          const float *c, float *d, void *stream) {
+    if ((kind != 0 && kind != 1) || n < 0 || n >= ((int64_t)1 << 31) || steps < 1 ||
+        steps > 4096)
+        return MOE_ERR_INVALID_ARG;
+    if (n == 0) return MOE_OK;
+    if (!a || !b || !c || !d || !aligned16(a) || !aligned16(b) || !aligned16(c) || !aligned16(d))
+        return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_probe_mfma(kind, n, steps, a, b, c, d, (hipStream_t)stream));
 }
 
 size_t moe_permute_workspace_bytes(const moe_dims *dims) {
@@ -337,11 +366,12 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
                          const void *wq_up, const float *s_up, const void *wq_down,
                          const float *s_down, void *out, moe_dtype out_dtype,
                          int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
-                         void *stream) {
+                         const moe_layer_opts *opts, void *stream) {
     Dims D;
     moe_status st = check_dims_fp8(dims, &D);
     if (st != MOE_OK) return st;
     if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+    if ((st = check_opts(opts, true)) != MOE_OK) return st;
     if (D.T == 0) return MOE_OK;
     if (!x || !w_router || !wq_gate || !s_gate || !wq_up || !s_up || !wq_down || !s_down || !out)
         return MOE_ERR_INVALID_ARG;
@@ -357,9 +387,12 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
     bf16_t *y = at<bf16_t>(ws, L.y);
     int32_t *perm_src = at<int32_t>(ws, L.perm_src);
     bool hist_done = false;  // the router may also count the permute's histogram
-    hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
-                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s,
-                                at<int32_t>(ws, L.blk_counts), &hist_done);
+    hipError_t e = mark_event(opts, 0, s);
+    if (e == hipSuccess)
+        e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates, nullptr,
+                         at<char>(ws, L.route), route_workspace_bytes(D), s,
+                         at<int32_t>(ws, L.blk_counts), &hist_done);
+    if (e == hipSuccess) e = mark_event(opts, 1, s);
     // No x_perm: the FFN quantises each token's row of x once and places its
     // codes at every routed row of that token through perm_src.
     if (e == hipSuccess)
@@ -367,11 +400,73 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
                            inv_perm, nullptr, at<int32_t>(ws, L.blk_counts),
                            at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr, nullptr,
                            nullptr, 0, s, hist_done);
+    if (e == hipSuccess) e = mark_event(opts, 2, s);
     if (e == hipSuccess)
         e = run_ffn_fp8(D, (const bf16_t *)x, offsets, (const uint8_t *)wq_gate, s_gate,
                         (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
                         at<char>(ws, L.ffn), s, perm_src);
     if (e == hipSuccess) e = launch_combine(D, y, inv_perm, gates, out, out_dtype == MOE_F32, s);
+    if (e == hipSuccess) e = mark_event(opts, 3, s);
+    return hip_status(e);
+}
+
+moe_status moe_gate_up_fp8(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
+                           const void *wq_gate, const float *s_gate, const void *wq_up,
+                           const float *s_up, void *h, void *ws, size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims_fp8(dims, &D);
+    if (st != MOE_OK) return st;
+    if (D.T == 0) return MOE_OK;
+    if (!x_perm || !offsets || !wq_gate || !s_gate || !wq_up || !s_up || !h)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm) || !aligned16(wq_gate) || !aligned16(wq_up) || !aligned16(h))
+        return MOE_ERR_INVALID_ARG;
+    const Layout8 L = make_layout8(D);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base),
+                                       at<int32_t>(ws, L.pstart), at<int32_t>(ws, L.hmax), D.cap(),
+                                       s);
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.d, (const bf16_t *)x_perm, offsets, at<int32_t>(ws, L.pstart),
+                              at<float>(ws, L.amax), false, at<uint8_t>(ws, L.xq),
+                              at<float>(ws, L.sx), s);
+    if (e == hipSuccess)
+        e = launch_gemm_gate_up_f8(D, at<uint8_t>(ws, L.xq), at<float>(ws, L.sx), mt, nmt,
+                                   at<int32_t>(ws, L.mtile_base), (const uint8_t *)wq_gate, s_gate,
+                                   (const uint8_t *)wq_up, s_up, (bf16_t *)h,
+                                   at<uint32_t>(ws, L.hmax), s);
+    return hip_status(e);
+}
+
+moe_status moe_down_fp8(const moe_dims *dims, const void *h, const int32_t *offsets,
+                        const void *wq_down, const float *s_down, void *y_perm, void *ws,
+                        size_t ws_bytes, void *stream) {
+    Dims D;
+    moe_status st = check_dims_fp8(dims, &D);
+    if (st != MOE_OK) return st;
+    if (D.T == 0) return MOE_OK;
+    if (!h || !offsets || !wq_down || !s_down || !y_perm) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(wq_down) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARG;
+    const Layout8 L = make_layout8(D);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    MTile *mt = at<MTile>(ws, L.mtiles);
+    int32_t *nmt = at<int32_t>(ws, L.n_mtiles);
+    hipError_t e = launch_build_mtiles(D, offsets, mt, nmt, at<int32_t>(ws, L.mtile_base),
+                                       at<int32_t>(ws, L.pstart), nullptr, 0, s);
+    // row maxima of h computed here (moe_expert_ffn_fp8 takes them from the
+    // gate/up epilogue: the same values, so the same codes and scales)
+    if (e == hipSuccess)
+        e = launch_quant_pack(D, D.f, (const bf16_t *)h, offsets, at<int32_t>(ws, L.pstart),
+                              at<float>(ws, L.hmax), false, at<uint8_t>(ws, L.hq),
+                              at<float>(ws, L.sh), s);
+    if (e == hipSuccess)
+        e = launch_gemm_down_f8(D, at<uint8_t>(ws, L.hq), at<float>(ws, L.sh), mt, nmt,
+                                at<int32_t>(ws, L.mtile_base), (const uint8_t *)wq_down, s_down,
+                                (bf16_t *)y_perm, s);
     return hip_status(e);
 }
 
@@ -424,11 +519,14 @@ size_t moe_layer_workspace_bytes(const moe_dims *dims) {
 moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, const float *bias,
                      const void *w_gate, const void *w_up, const void *w_down, void *out,
                      moe_dtype out_dtype, int32_t *topk_ids_out, float *topk_w_out, void *ws,
-                     size_t ws_bytes, void *stream) {
+                     size_t ws_bytes, const moe_layer_opts *opts, void *stream) {
     Dims D;
     moe_status st = check_dims(dims, &D);
     if (st != MOE_OK) return st;
     if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_INVALID_ARG;
+    if ((st = check_opts(opts, false)) != MOE_OK) return st;
+    if (opts && opts->tile_order == MOE_ORDER_COMBINE_FIRST && comb_groups(D.d) > ORDER3_MAX_CG)
+        return MOE_ERR_UNSUPPORTED;
     if (D.T == 0) return MOE_OK;
     if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate) || !aligned16(w_up) ||
@@ -440,27 +538,11 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
 
     const int grid = layer_grid_size();
     if (grid <= 0) return MOE_ERR_HIP;
-    int64_t wait_us;
-    CallEvents ce{};
-    bool timing, gather;
-    int tile_order;
-    int64_t *trace;
-    int64_t trace_cap;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        wait_us = g_wait_us;
-        timing = g_timing;
-        // 32-bit buffer offsets address x in gather mode
-        gather = g_gather && D.T * D.d * 2 < ((int64_t)1 << 31);
-        tile_order = g_tile_order;
-        trace = g_trace;
-        trace_cap = g_trace_cap;
-        if (timing)
-            for (int i = 0; i < 4; ++i) ce.ev[i] = pool_event();
-    }
-    auto mark = [&](int i) {
-        if (timing && ce.ev[i]) (void)hipEventRecord(ce.ev[i], s);
-    };
+    moe_layer_opts o{};
+    if (opts) o = *opts;
+    // 32-bit buffer offsets address x in gather mode
+    const bool gather = o.dispatch == MOE_DISPATCH_GATHER && D.T * D.d * 2 < ((int64_t)1 << 31);
+    const int64_t wait_us = o.wait_timeout_us > 0 ? o.wait_timeout_us : 2000000;
 
     int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
     float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
@@ -474,25 +556,28 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         D.dn_parts() > 1 ? (int64_t)((L.dn_cnt - L.status) / 4) + SPLIT_MAX
                     : (int64_t)((L.dn_flag - L.status) / 4) + D.max_mtiles() * D.nt_dn();
 
-    mark(0);
     bool hist_done = false;  // the router may also count the permute's histogram
-    hipError_t e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates,
-                                nullptr, at<char>(ws, L.route), route_workspace_bytes(D), s,
-                                at<int32_t>(ws, L.blk_counts), &hist_done);
-    mark(1);
+    hipError_t e = mark_event(opts, 0, s);
+    if (e == hipSuccess)
+        e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates, nullptr,
+                         at<char>(ws, L.route), route_workspace_bytes(D), s,
+                         at<int32_t>(ws, L.blk_counts), &hist_done);
+    if (e == hipSuccess) e = mark_event(opts, 1, s);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
                            at<int32_t>(ws, L.perm_src), inv_perm, gather ? nullptr : x_perm,
                            at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
                            at<int32_t>(ws, L.pstart), mt, nmt, mtile_base,
                            at<int32_t>(ws, L.status), sched_ints, s, hist_done);
-    mark(2);
+    if (e == hipSuccess) e = mark_event(opts, 2, s);
     if (e == hipSuccess) {
         LayerArgs a;
         a.D = D;
         a.x_perm = x_perm;
         a.gather = gather ? 1 : 0;
-        a.interleave = tile_order;
+        a.order = o.tile_order;
+        a.lead = o.lead > 0 ? o.lead : grid;
+        a.perturb = o.perturb_seed;
         a.x = (const bf16_t *)x;
         a.perm_src = at<int32_t>(ws, L.perm_src);
         a.w_gate = (const bf16_t *)w_gate;
@@ -515,18 +600,18 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.dn_part = at<float>(ws, L.dn_part);
         a.status = at<int32_t>(ws, L.status);
         a.dn_done = at<int32_t>(ws, L.status) + 32;  // 128 bytes past the status word
+        a.dn_cg = at<int32_t>(ws, L.dn_cg);
+        a.order_tab = at<int32_t>(ws, L.order_tab);
+        a.order_tmp = at<int32_t>(ws, L.order_tmp);
         a.out = out;
         a.out_f32 = out_dtype == MOE_F32;
         a.wait_ticks = wait_us * (wall_clock_hz() / 1000000);
-        a.trace = trace;
-        a.trace_cap = trace_cap;
-        e = launch_layer_persistent(a, grid, s);
+        a.trace = o.trace_records > 0 ? o.trace : nullptr;
+        a.trace_cap = o.trace_records > 0 ? o.trace_records : 0;
+        e = launch_build_order(a, grid, s);
+        if (e == hipSuccess) e = launch_layer_persistent(a, grid, s);
     }
-    mark(3);
-    if (timing) {
-        std::lock_guard<std::mutex> lk(g_mu);
-        g_events.push_back(ce);
-    }
+    if (e == hipSuccess) e = mark_event(opts, 3, s);
     return hip_status(e);
 }
 
@@ -544,65 +629,6 @@ moe_status moe_device_status(const moe_dims *dims, const void *ws, size_t ws_byt
     return v == 0 ? MOE_OK : (moe_status)v;
 }
 
-void moe_timing_enable(int on) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_timing = on != 0;
-    for (auto &ce : g_events)
-        for (auto ev : ce.ev)
-            if (ev) {
-                (void)hipEventSynchronize(ev);
-                g_pool.push_back(ev);
-            }
-    g_events.clear();
-}
-
-int moe_timing_read(float *stage_ms, int n_stages) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    double sum[3] = {0, 0, 0};
-    int n = 0;
-    for (auto &ce : g_events) {
-        bool ok = true;
-        float ms[3] = {0, 0, 0};
-        for (int i = 0; i < 3 && ok; ++i) {
-            if (!ce.ev[i] || !ce.ev[i + 1] || hipEventSynchronize(ce.ev[i + 1]) != hipSuccess ||
-                hipEventElapsedTime(&ms[i], ce.ev[i], ce.ev[i + 1]) != hipSuccess)
-                ok = false;
-        }
-        if (ok) {
-            for (int i = 0; i < 3; ++i) sum[i] += ms[i];
-            ++n;
-        }
-        for (auto ev : ce.ev)
-            if (ev) g_pool.push_back(ev);
-    }
-    g_events.clear();
-    for (int i = 0; i < n_stages && i < 3; ++i) stage_ms[i] = n ? (float)(sum[i] / n) : 0.0f;
-    return n;
-}
-
-void moe_set_trace(void *buf, int64_t n_records) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_trace = (buf && n_records > 0) ? (int64_t *)buf : nullptr;
-    g_trace_cap = g_trace ? n_records : 0;
-}
-
 int64_t moe_wall_clock_hz(void) { return wall_clock_hz(); }
-
-int moe_set_tile_order(int policy) {
-    if (policy != 0 && policy != 1) return MOE_ERR_INVALID_ARG;
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_tile_order = policy;
-    return MOE_OK;
-}
-
-void moe_set_gather_dispatch(int on) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_gather = on != 0;
-}
-
-void moe_set_wait_timeout_us(int64_t us) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    g_wait_us = us < 1 ? 2000000 : us;
-}
 
 }  // extern "C"

@@ -136,7 +136,8 @@ struct MTile {
 
 // Byte offsets of every region in a workspace (each 256-byte aligned).
 struct Layout {
-    size_t status, queues, gu_done, gu_xcd, dn_flag, dn_cnt, dn_part, route, ids, gates,
+    size_t status, queues, gu_done, gu_xcd, dn_cg, dn_flag, dn_cnt, dn_part, order_tab, order_tmp,
+        route, ids, gates,
         blk_counts,
         blk_base, counts, offsets, pstart, perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm,
         h, y, total;
@@ -165,6 +166,16 @@ int route_splits(const Dims &D);
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
                         hipStream_t s, int32_t *blk_counts = nullptr, bool *hist_done = nullptr);
+
+// The fast router's approximate logits and their error bounds (E > 16 with a
+// workspace of route_workspace_bytes): approx, eps [T, E].
+hipError_t launch_route_bounds(const Dims &D, const bf16_t *x, const bf16_t *w_router,
+                               const float *bias, float *approx, float *eps, void *ws,
+                               hipStream_t s);
+
+// Matrix-core probe (probe.hip): kind 0 bf16 32x32x16, kind 1 E4M3 32x32x64.
+hipError_t launch_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
+                             const float *c, float *d, hipStream_t s);
 
 // Permute.  With pstart != NULL (the fused layer) x_perm is written in the
 // packed fragment layout of gemm_pa.h at the 32-aligned segment starts
@@ -236,9 +247,19 @@ struct LayerArgs {
     // gather-on-load dispatch: gate/up tiles read their rows of x through
     // perm_src (x_perm is not written); 0 = packed x_perm from the permute
     int gather;
-    // tile order: 0 = by kind (gate/up, then down), 1 = ready down tiles of
-    // the own XCD's range taken between gate/up tiles
-    int interleave;
+    // tile order (moe_tile_order): 0 by kind, 1 ready down tiles of the own
+    // XCD's range taken between gate/up tiles, 2 one merged stream with a
+    // dependency lead, 3 down tiles by combine column group, ready combine
+    // tiles first
+    int order;
+    int lead;          // order 2: the lead in gate/up tiles
+    uint32_t perturb;  // schedule perturbation seed (0 = off)
+    // orders 2 and 3: claim table built on the device (build_order_kernel):
+    // order 2 the merged stream (gate/up index, or down claim | 1 << 30),
+    // order 3 the down claims of every XCD range sorted by column group
+    int32_t *order_tab;
+    int32_t *order_tmp;  // order 2: scratch of the table builder
+    int32_t *dn_cg;      // published down tiles per combine column group (cleared per call)
     const bf16_t *x;
     const int32_t *perm_src;
     bf16_t *h, *y;
@@ -255,6 +276,16 @@ struct LayerArgs {
     int64_t trace_cap;   // records that fit after the count
 };
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s);
+// The claim table of tile orders 2 and 3 (a.order_tab), from the m-tile table
+// on the device; nothing for the other orders.
+hipError_t launch_build_order(const LayerArgs &a, int grid, hipStream_t s);
+// Column groups of the combine tiles (COMB_CB column blocks each).
+__host__ __device__ inline int64_t comb_groups(int64_t d) {
+    return (d / BN_DN + COMB_CB - 1) / COMB_CB;
+}
+// Largest column-group count tile order 3 supports (its table builder keeps
+// per-thread counts of every group in LDS).
+constexpr int ORDER3_MAX_CG = 16;
 int layer_grid_size();  // resident workgroups of the persistent kernel (cached)
 int64_t wall_clock_hz(); // frequency of wall_clock64 on the current device (cached)
 

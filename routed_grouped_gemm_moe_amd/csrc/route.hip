@@ -22,8 +22,8 @@
 //    staged in LDS and the activations prefetched.
 //  - fast path (E > 16, with a workspace): bf16 MFMA logits (split-K float32
 //    partials) are an approximation l~ with |l~ - l| <= eps, eps bounded from
-//    ||x_t||, ||w_e|| and the float32 unit roundoff (any summation order of d
-//    products errs by at most d*u*sum|x_i w_i| <= d*u*||x||*||w||).  An expert
+//    ||x_t||, ||w_e||, the float32 unit roundoff and the measured rounding of
+//    one matrix-core step (see route_refine_kernel).  An expert
 //    whose upper bound l~ + eps is below the k-th largest lower bound l~ - eps
 //    has at least k experts strictly above it and cannot be selected; the
 //    remaining candidates (typically k plus a few) get their logits evaluated
@@ -554,11 +554,15 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void route_gemm_kernel(
 constexpr int RF_WAVES = 4;
 // RMAX = expert slots per lane (E <= 64 * RMAX), a template parameter so the
 // bound, selection and compaction loops run over only the slots E needs.
-template <int RMAX>
+// BOUNDS: instead of selecting, write every (t, e)'s approximate logit and its
+// bound eps to approx / eps_out [T, E] and return (the verification entry
+// point moe_route_bounds; the arithmetic is the selection path's own).
+template <int RMAX, bool BOUNDS = false>
 __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     int64_t T, int64_t d, int64_t E, int64_t k, int S, const bf16_t *__restrict__ x,
     const bf16_t *__restrict__ wt, const float *__restrict__ wnorm, const float *__restrict__ bias,
-    const float *__restrict__ part, int32_t *__restrict__ ids, float *__restrict__ gates) {
+    const float *__restrict__ part, int32_t *__restrict__ ids, float *__restrict__ gates,
+    float *__restrict__ approx = nullptr, float *__restrict__ eps_out = nullptr) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -596,13 +600,21 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
     const float xn = sqrtf(ss) * norm_inflation(d);
-    // |l~ - l| <= (d*2^-23 + (d/16 + 4)*2^-24) * sum|x_i w_i| + bias roundings:
-    // the MFMA split-K sum, whatever its internal order, passes each of the d
-    // exact products through at most d roundings of at most 2^-23 (round to
-    // nearest or toward zero); the defined-order sum through at most d/16 + 4
-    // of 2^-24; sum|x_i w_i| <= ||x|| ||w|| (Cauchy-Schwarz).  +8 and 2^-10
-    // cover the float32 evaluation of the bound itself.
-    const float gam = ((float)(2 * d + d / 16 + 8) * 0x1p-24f) * (1.0f + 0x1p-10f);
+    // |l~ - l| <= gam * sum|x_i w_i| + bias roundings, A = sum|x_i w_i| <=
+    // ||x|| ||w|| (Cauchy-Schwarz).  Terms of gam, in units of 2^-24:
+    //  - each split-K partial is a chain of n = d/(16 S) 32x32x16 bf16 matrix-
+    //    core steps; one step errs by at most 2^-20 (sum over its products of
+    //    |p| + |accumulator|) -- the premise, measured on gfx950 against exact
+    //    sums on adversarial operands (at most 2^-21.3 seen); every running
+    //    accumulator is at most the partial's A_s, so a chain errs by at most
+    //    16 (n + 1) A_s, and the partials by 16 (n + 1) A together;
+    //  - the S partials are added in float32: S roundings of at most 2^-24 A;
+    //  - the defined-order logit l itself: d/16 sequential additions per chunk
+    //    and 4 tree levels, at most d/16 + 4 roundings of 2^-24 A.
+    // +4 and 2^-10 cover the float32 evaluation of the bound itself.
+    const int64_t n_steps = d / (16 * (int64_t)S);
+    const float gam =
+        ((float)(16 * (n_steps + 1) + S + d / 16 + 8) * 0x1p-24f) * (1.0f + 0x1p-10f);
 
     // bounds of this lane's experts e = lane + 64*r2
     float lo[RMAX], hi[RMAX];
@@ -636,8 +648,13 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
             const float eps = g + 0x1p-21f * (fabsf(la) + g) + 1e-30f;
             lo[r0 + q] = la - eps;
             hi[r0 + q] = la + eps;
+            if (BOUNDS) {
+                approx[t * E + e] = la;
+                eps_out[t * E + e] = eps;
+            }
         }
     }
+    if (BOUNDS) return;
     // Lk = k-th largest lower bound (k rounds of a wave max)
     uint32_t taken = 0;
     float Lk = -__builtin_inff();
@@ -790,6 +807,65 @@ static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, 
     return hipGetLastError();
 }
 
+// The E > 16 fast path: re-laid-out W_r and its norms, the MFMA split-K
+// logit partials, then one wave per token for the bounds, the exact logits of
+// the candidates and the selection -- or, with approx != NULL, only the
+// bounds, written out (moe_route_bounds).
+static hipError_t launch_route_fast(const Dims &D, const bf16_t *x, const bf16_t *w_router,
+                                    const float *bias, int32_t *ids, float *gates, void *ws,
+                                    hipStream_t s, float *approx, float *eps) {
+    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const int S = route_splits(D);
+    float *part = reinterpret_cast<float *>(ws);
+    bf16_t *wt = reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(ws) +
+                                            al((size_t)S * D.T * D.E * 4));
+    float *wnorm = reinterpret_cast<float *>(reinterpret_cast<char *>(wt) + al((size_t)D.E * D.d * 2));
+    hipLaunchKernelGGL(route_wprep_kernel, dim3((unsigned)D.E), dim3(256), 0, s, D.d, w_router, wt,
+                       wnorm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void *)route_gemm_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((D.T + BM - 1) / BM) * ((D.E + BN_TILE - 1) / BN_TILE) * S;
+    hipLaunchKernelGGL(route_gemm_kernel, dim3((unsigned)tiles), dim3(GEMM_THREADS), GEMM_LDS_BYTES,
+                       s, D.T, D.d, D.E, S, x, w_router, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds = (size_t)RF_WAVES * refine_per_wave(D.d, D.E);
+    const dim3 grid((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES));
+    auto refine = [&](auto rk) -> hipError_t {
+        constexpr int R = decltype(rk)::value;
+        hipError_t er;
+        if (approx) {
+            er = hipFuncSetAttribute((const void *)route_refine_kernel<R, true>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (er != hipSuccess) return er;
+            hipLaunchKernelGGL((route_refine_kernel<R, true>), grid, dim3(64 * RF_WAVES), lds, s,
+                               D.T, D.d, D.E, D.k, S, x, wt, wnorm, bias, part, ids, gates, approx,
+                               eps);
+        } else {
+            er = hipFuncSetAttribute((const void *)route_refine_kernel<R>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (er != hipSuccess) return er;
+            hipLaunchKernelGGL(route_refine_kernel<R>, grid, dim3(64 * RF_WAVES), lds, s, D.T, D.d,
+                               D.E, D.k, S, x, wt, wnorm, bias, part, ids, gates, nullptr, nullptr);
+        }
+        return hipSuccess;
+    };
+    if (D.E <= 128) e = refine(std::integral_constant<int, 2>{});
+    else if (D.E <= 256) e = refine(std::integral_constant<int, 4>{});
+    else e = refine(std::integral_constant<int, 16>{});
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_route_bounds(const Dims &D, const bf16_t *x, const bf16_t *w_router,
+                               const float *bias, float *approx, float *eps, void *ws,
+                               hipStream_t s) {
+    if (D.T == 0) return hipSuccess;
+    return launch_route_fast(D, x, w_router, bias, nullptr, nullptr, ws, s, approx, eps);
+}
+
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
                         hipStream_t s, int32_t *blk_counts, bool *hist_done) {
@@ -816,40 +892,7 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
         if (D.E <= 8) return launch_small_t<8>(D, x, w_router, bias, ids, gates, s);
         return launch_small_t<16>(D, x, w_router, bias, ids, gates, s);
     }
-    // fast path
-    auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
-    const int S = route_splits(D);
-    float *part = reinterpret_cast<float *>(ws);
-    bf16_t *wt = reinterpret_cast<bf16_t *>(reinterpret_cast<char *>(ws) +
-                                            al((size_t)S * D.T * D.E * 4));
-    float *wnorm = reinterpret_cast<float *>(reinterpret_cast<char *>(wt) + al((size_t)D.E * D.d * 2));
-    hipLaunchKernelGGL(route_wprep_kernel, dim3((unsigned)D.E), dim3(256), 0, s, D.d, w_router, wt,
-                       wnorm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)route_gemm_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = ((D.T + BM - 1) / BM) * ((D.E + BN_TILE - 1) / BN_TILE) * S;
-    hipLaunchKernelGGL(route_gemm_kernel, dim3((unsigned)tiles), dim3(GEMM_THREADS), GEMM_LDS_BYTES,
-                       s, D.T, D.d, D.E, S, x, w_router, part);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds = (size_t)RF_WAVES * refine_per_wave(D.d, D.E);
-    auto refine = [&](auto rk) -> hipError_t {
-        constexpr int R = decltype(rk)::value;
-        hipError_t er = hipFuncSetAttribute((const void *)route_refine_kernel<R>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (er != hipSuccess) return er;
-        hipLaunchKernelGGL(route_refine_kernel<R>, dim3((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES)),
-                           dim3(64 * RF_WAVES), lds, s, D.T, D.d, D.E, D.k, S, x, wt, wnorm, bias,
-                           part, ids, gates);
-        return hipSuccess;
-    };
-    if (D.E <= 128) e = refine(std::integral_constant<int, 2>{});
-    else if (D.E <= 256) e = refine(std::integral_constant<int, 4>{});
-    else e = refine(std::integral_constant<int, 16>{});
-    if (e != hipSuccess) return e;
-    return hipGetLastError();
+    return launch_route_fast(D, x, w_router, bias, ids, gates, ws, s, nullptr, nullptr);
 }
 
 }  // namespace moe

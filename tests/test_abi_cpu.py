@@ -72,7 +72,7 @@ def test_bad_dims_rejected_by_every_entry_point(bad, status):
                               None) == status
     assert lib.moe_combine(C.byref(D), FAKE, FAKE, FAKE, FAKE, 0, None) == status
     assert lib.moe_layer(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None, None,
-                         FAKE_WS, 1 << 40, None) == status
+                         FAKE_WS, 1 << 40, None, None) == status
 
 
 def test_null_and_misaligned_pointers_rejected():
@@ -87,7 +87,7 @@ def test_null_and_misaligned_pointers_rejected():
                          1 << 20, None) == WORKSPACE
     assert lib.moe_combine(C.byref(D), FAKE, FAKE, FAKE, FAKE, 7, None) == INVALID
     assert lib.moe_layer(C.byref(D), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, None, None,
-                         FAKE_WS, 1 << 40, None) == INVALID
+                         FAKE_WS, 1 << 40, None, None) == INVALID
 
 
 def test_workspace_checks():
@@ -95,9 +95,9 @@ def test_workspace_checks():
     D = dims()
     need = M.moe_layer_workspace_bytes(D)
     args = (C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None, None)
-    assert lib.moe_layer(*args, None, need, None) == WORKSPACE
-    assert lib.moe_layer(*args, FAKE_WS, need - 1, None) == WORKSPACE
-    assert lib.moe_layer(*args, C.c_void_p(0x100010), need, None) == WORKSPACE
+    assert lib.moe_layer(*args, None, need, None, None) == WORKSPACE
+    assert lib.moe_layer(*args, FAKE_WS, need - 1, None, None) == WORKSPACE
+    assert lib.moe_layer(*args, C.c_void_p(0x100010), need, None, None) == WORKSPACE
     pneed = M.moe_permute_workspace_bytes(D)
     assert lib.moe_permute(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE_WS,
                            pneed - 1, None) == WORKSPACE
@@ -112,7 +112,7 @@ def test_empty_batch_is_a_no_op():
     assert lib.moe_route(C.byref(D), None, None, None, None, None, None, None, 0, None) == OK
     assert lib.moe_combine(C.byref(D), None, None, None, None, 0, None) == OK
     assert lib.moe_layer(C.byref(D), None, None, None, None, None, None, None, 0, None, None, None,
-                         0, None) == OK
+                         0, None, None) == OK
 
 
 def test_fp8_entry_points_check_arguments_before_any_gpu_call():
@@ -145,20 +145,76 @@ def test_fp8_layer_checks_arguments_before_any_gpu_call():
     assert need > M.moe_expert_ffn_fp8_workspace_bytes(D)
     assert M.moe_layer_fp8_workspace_bytes(dims(f=384)) == 0
     w = (FAKE,) * 9  # x, w_router, bias, wq_gate, s_gate, wq_up, s_up, wq_down, s_down
-    assert lib.moe_layer_fp8(C.byref(dims(f=384)), *w, FAKE, 0, None, None, FAKE_WS, 1 << 40,
+    assert lib.moe_layer_fp8(C.byref(dims(f=384)), *w, FAKE, 0, None, None, FAKE_WS, 1 << 40, None,
                              None) == UNSUPPORTED
-    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 5, None, None, FAKE_WS, 1 << 40, None) == INVALID
-    assert lib.moe_layer_fp8(C.byref(D), None, *w[1:], FAKE, 0, None, None, FAKE_WS, 1 << 40,
+    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 5, None, None, FAKE_WS, 1 << 40, None, None) == INVALID
+    assert lib.moe_layer_fp8(C.byref(D), None, *w[1:], FAKE, 0, None, None, FAKE_WS, 1 << 40, None,
                              None) == INVALID
-    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need - 1,
+    assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need - 1, None,
                              None) == WORKSPACE
-    assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0,
+    assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0, None,
                              None) == OK
 
 
-def test_tile_order_values():
+def test_layer_options_are_checked_per_call():
     lib = M.load()
-    assert lib.moe_set_tile_order(2) == INVALID
-    assert lib.moe_set_tile_order(-1) == INVALID
-    assert lib.moe_set_tile_order(1) == OK
-    assert lib.moe_set_tile_order(0) == OK
+    D = dims()
+    need = M.moe_layer_workspace_bytes(D)
+    args = (C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None, None, FAKE_WS, need)
+
+    def opts(**kw):
+        o = M.MoELayerOpts()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return C.byref(o)
+
+    for bad in (dict(dispatch=2), dict(dispatch=-1), dict(tile_order=4), dict(tile_order=-1),
+                dict(lead=-1), dict(wait_timeout_us=-5), dict(trace_records=-1),
+                dict(trace_records=8)):  # records without a buffer
+        assert lib.moe_layer(*args, opts(**bad), None) == INVALID, bad
+    # the W8A8 layer takes events only
+    w = (FAKE,) * 9
+    need8 = M.moe_layer_fp8_workspace_bytes(D)
+    for bad in (dict(dispatch=1), dict(tile_order=1), dict(perturb_seed=3),
+                dict(wait_timeout_us=10)):
+        assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need8,
+                                 opts(**bad), None) == INVALID, bad
+    # the old process-wide setters are gone: options travel with the call
+    for name in ("moe_set_tile_order", "moe_set_gather_dispatch", "moe_set_trace",
+                 "moe_set_wait_timeout_us", "moe_timing_enable", "moe_timing_read"):
+        assert not hasattr(lib, name), name
+    assert C.sizeof(M.MoELayerOpts) == 72
+
+
+def test_verification_entry_points_check_arguments():
+    lib = M.load()
+    # matrix-core probe: kind, counts and alignment
+    assert lib.moe_probe_mfma(2, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 1, 0, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 1, 4097, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(1, -1, 1, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 1, 1, C.c_void_p(0x10002), FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 1, 1, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 0, 1, None, None, None, None, None) == OK
+    # router bounds: only where the fast path applies (E > 16), workspace required
+    D = dims(E=8)
+    assert lib.moe_route_bounds(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE_WS, 1 << 40,
+                                None) == UNSUPPORTED
+    D = dims(E=64, k=4)
+    need = M.moe_route_workspace_bytes(D)
+    assert need > 0
+    assert lib.moe_route_bounds(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE_WS, need - 1,
+                                None) == WORKSPACE
+    assert lib.moe_route_bounds(C.byref(D), FAKE, FAKE, None, None, FAKE, FAKE_WS, need,
+                                None) == INVALID
+    # the two halves of the W8A8 FFN
+    D = dims()
+    need = M.moe_expert_ffn_fp8_workspace_bytes(D)
+    gu = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)  # x_perm, offsets, wq/s gate, wq/s up, h
+    assert lib.moe_gate_up_fp8(C.byref(D), *gu, FAKE_WS, need - 1, None) == WORKSPACE
+    assert lib.moe_gate_up_fp8(C.byref(D), None, *gu[1:], FAKE_WS, need, None) == INVALID
+    assert lib.moe_gate_up_fp8(C.byref(dims(f=384)), *gu, FAKE_WS, need, None) == UNSUPPORTED
+    dn = (FAKE, FAKE, FAKE, FAKE, FAKE)  # h, offsets, wq_down, s_down, y
+    assert lib.moe_down_fp8(C.byref(D), *dn, FAKE_WS, need - 1, None) == WORKSPACE
+    assert lib.moe_down_fp8(C.byref(D), C.c_void_p(0x10002), *dn[1:], FAKE_WS, need,
+                            None) == INVALID

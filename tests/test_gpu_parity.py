@@ -1,11 +1,12 @@
 """GPU parity: every C-ABI call against the CPU oracle.
 
 Small and ragged cases are compared element by element; the five workload
-shapes at full size are compared bit-exactly on routing and dispatch and on
-sampled tokens/rows for the FFN and layer outputs.  The fused moe_layer must
-also equal the staged route -> permute -> expert_ffn -> combine path bit for
-bit: both run the same tiles, so any difference is a scheduling or signaling
-error in the persistent kernel.
+shapes at full size are compared bit-exactly on routing and dispatch, on the
+layer output of every token, and on FFN rows (all of them, or the first and
+last row of every m-tile).  The fused moe_layer must also equal the staged
+route -> permute -> expert_ffn -> combine path bit for bit: both run the same
+tiles, so any difference is a scheduling or signaling error in the persistent
+kernel -- under every tile order, and under a seeded adversarial schedule.
 """
 import numpy as np
 import pytest
@@ -116,7 +117,7 @@ def _check_combine(cfg, t, y, inv, gates_dev, ri, r_g, N):
         assert rel_err(host_f32(out), ref) <= tol
 
 
-def _check_layer(cfg, t, arrs, staged_out=None, tokens=None):
+def _check_layer(cfg, t, arrs, staged_out=None, tokens=None, opts=None):
     D = _dims(cfg)
     dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
     say(f"moe_layer {cfg.name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} "
@@ -125,7 +126,7 @@ def _check_layer(cfg, t, arrs, staged_out=None, tokens=None):
     gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
-                      out_dtype=dt, topk_ids_out=ids, topk_w_out=gates, ws=ws)
+                      out_dtype=dt, topk_ids_out=ids, topk_w_out=gates, ws=ws, opts=opts)
     assert M.moe_device_status(D, ws) == 0
     tokens = np.arange(cfg.T) if tokens is None else tokens
     ref, r_ids, r_g = oracle.layer_tokens(tokens, arrs["x"], arrs["w_router"], arrs["w_gate"],
@@ -253,13 +254,10 @@ def test_bounded_wait_reports_timeout_then_recovers():
     D = _dims(cfg)
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     say("moe_layer with a 1 us flag-wait timeout")
-    try:
-        M.moe_set_wait_timeout_us(1)
-        M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws)
-        st = M.moe_device_status(D, ws)
-        assert st in (0, -5)
-    finally:
-        M.moe_set_wait_timeout_us(0)
+    M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws,
+                opts=M.layer_opts(wait_timeout_us=1))
+    st = M.moe_device_status(D, ws)
+    assert st in (0, -5)
     say("moe_layer with the default timeout")
     M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], ws=ws)
     assert M.moe_device_status(D, ws) == 0
@@ -270,26 +268,35 @@ def test_bounded_wait_reports_timeout_then_recovers():
 FULL = ["tiny", "mixtral", "fine", "skewed", "dsv3_share"]
 
 
+def _mtile_rows(ro, rng, extra=16):
+    """The first and last row of every 256-row m-tile of every expert segment
+    (so every m-tile of the grouped GEMMs is compared), plus random rows."""
+    rows = []
+    for e in range(len(ro) - 1):
+        for r0 in range(int(ro[e]), int(ro[e + 1]), 256):
+            rows += [r0, min(r0 + 255, int(ro[e + 1]) - 1)]
+    N = int(ro[-1])
+    return np.unique(np.concatenate([np.array(rows, np.int64),
+                                     rng.choice(N, size=min(N, extra), replace=False)]))
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workload(name):
+    """The five workloads at full size: routing and dispatch bit-exact, the
+    FFN on every row (tiny, fine) or on the first and last row of every
+    m-tile (the rest), and the layer output of EVERY token against the
+    oracle, fused == staged bit for bit."""
     cfg = W.CONFIGS[name]
     say(f"generate {name}")
     arrs = W.generate(cfg)
     t = upload(cfg, arrs)
     ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
     offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
-    # FFN rows: first and last row of a few experts plus random rows
-    rng = np.random.default_rng(1)
-    edges = np.concatenate([ro[:-1][np.diff(ro) > 0][:6], (ro[1:] - 1)[np.diff(ro) > 0][-6:]])
-    rows = np.unique(np.concatenate([edges, rng.choice(N, size=min(N, 12), replace=False)]))
+    rows = None if name in ("tiny", "fine") else _mtile_rows(ro, np.random.default_rng(1))
     y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N, rows=rows)
     staged = _staged(cfg, t, y, inv, gates)
-    local_tok = np.nonzero((ri >= 0).any(1))[0]
-    must = local_tok[:3].tolist() + local_tok[-3:].tolist()
-    if cfg.E_loc < cfg.E:
-        must += np.nonzero(~(ri >= 0).any(1))[0][:2].tolist()
-    toks = sample_tokens(cfg.T, 48, seed=2, must=must)
-    _check_layer(cfg, t, arrs, staged_out=staged, tokens=toks)
+    _check_layer(cfg, t, arrs, staged_out=staged, tokens=np.arange(cfg.T))
     del t, xp, y, staged
     torch.cuda.empty_cache()
 
@@ -393,17 +400,14 @@ def test_gather_on_load_dispatch(name):
     packed = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
                          out_dtype=dt)
     torch.cuda.synchronize()
-    try:
-        M.moe_set_gather_dispatch(True)
-        say(f"moe_layer gather dispatch {cfg.name}")
-        ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
-        ws.fill_(0xFF)  # a packed x_perm left from elsewhere must not be read
-        out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
-                          t["bias"], out_dtype=dt, ws=ws)
-        torch.cuda.synchronize()
-        assert M.moe_device_status(D, ws) == 0
-    finally:
-        M.moe_set_gather_dispatch(False)
+    say(f"moe_layer gather dispatch {cfg.name}")
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)  # a packed x_perm left from elsewhere must not be read
+    out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
+                      t["bias"], out_dtype=dt, ws=ws,
+                      opts=M.layer_opts(dispatch=M.MOE_DISPATCH_GATHER))
+    torch.cuda.synchronize()
+    assert M.moe_device_status(D, ws) == 0
     bits = torch.int32 if dt == M.MOE_F32 else torch.int16
     assert torch.equal(out.view(bits), packed.view(bits)), "gather != packed dispatch"
     toks = sample_tokens(cfg.T, 32, seed=5)
@@ -416,11 +420,15 @@ def test_gather_on_load_dispatch(name):
     torch.cuda.empty_cache()
 
 
+ORDERS = [1, 2, 3]
+
+
+@pytest.mark.parametrize("order", ORDERS)
 @pytest.mark.parametrize("name", ["tiny", "local_subset_e16k4", "e128k8", "mixtral",
                                   "rand1", "rand2", "rand6", "rand9"])
-def test_interleaved_tile_order_same_bits(name):
-    """moe_set_tile_order(1) takes ready down tiles between gate/up tiles; the
-    tiles and their arithmetic are unchanged, so the output bits are too."""
+def test_tile_orders_same_bits_and_match_oracle(name, order):
+    """Every tile order runs the same tiles with the same arithmetic: the
+    output bits equal the default order's, and match the oracle."""
     cfg = _named_case(name)
     arrs = W.generate(cfg)
     t = upload(cfg, arrs)
@@ -431,15 +439,72 @@ def test_interleaved_tile_order_same_bits(name):
     ref = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
                       out_dtype=dt, ws=ws)
     torch.cuda.synchronize()
-    try:
-        M.moe_set_tile_order(1)
-        ws.fill_(0xFF)
-        say(f"moe_layer tile order 1 {name}")
-        out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
-                          t["bias"], out_dtype=dt, ws=ws)
-        torch.cuda.synchronize()
-    finally:
-        M.moe_set_tile_order(0)
+    ws.fill_(0xFF)
+    say(f"moe_layer tile order {order} {name}")
+    out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"],
+                      t["bias"], out_dtype=dt, ws=ws, opts=M.layer_opts(tile_order=order))
+    torch.cuda.synchronize()
     assert M.moe_device_status(D, ws) == 0
     bits = torch.int32 if dt == M.MOE_F32 else torch.int16
     assert torch.equal(out.view(bits), ref.view(bits))
+    toks = np.arange(cfg.T) if cfg.T <= 1200 else sample_tokens(cfg.T, 64, seed=8)
+    oref, _, _ = oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"],
+                                     arrs["w_up"], arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi,
+                                     bias=arrs["bias"])
+    err = rel_err(host_f32(out[torch.as_tensor(toks, device="cuda")]), oref)
+    say(f"  tile order {order} rel err {err:.3e} over {len(toks)} tokens")
+    assert err <= TOL_LAYER
+    del t
+    torch.cuda.empty_cache()
+
+
+def _perturb_case(name):
+    if name == "cut4":
+        return W.CONFIGS["tiny"].scaled(name="cut4", T=2400, d=4096, f=8192, E=2, k=2, seed=17)
+    if name == "hot18":
+        return W.CONFIGS["tiny"].scaled(name="hot18", T=4600, d=256, f=256, E=8, k=1, seed=19)
+    return _named_case(name)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("name,seed", [("tiny", 1), ("multi_tile_rows", 2), ("e128k8", 3),
+                                       ("local_subset_e16k4", 4), ("hot18", 5), ("cut4", 6),
+                                       ("fine", 7)])
+def test_adversarial_schedule_same_bits_and_match_oracle(name, seed, order):
+    """The flag protocol under adversarial timing: producers wait seeded
+    pseudo-random delays (up to ~100 us) between writing their tiles and
+    publishing them, and each kind's tiles are claimed from the far end of
+    every range (not in the dependency-lead order, whose merged stream must
+    be claimed in order).  A consumer that read before its producer's release would
+    see the NaN bytes the workspace starts with, or stale rows; the output
+    must instead equal the staged calls bit for bit and match the oracle."""
+    cfg = _perturb_case(name)
+    arrs = W.generate(cfg, bias_override=_bias_all_to_one(8, 2) if name == "hot18" else None)
+    t = upload(cfg, arrs)
+    D = _dims(cfg)
+    dt = M.MOE_F32 if cfg.out_fp32 else M.MOE_BF16
+    say(f"staged calls {name}")
+    ids, gates, _ = M.moe_route(D, t["x"], t["w_router"], t["bias"])
+    _, offsets, _, inv, xp = M.moe_permute(D, t["x"], ids)
+    y = M.moe_expert_ffn(D, xp, offsets, t["w_gate"], t["w_up"], t["w_down"], check_status=True)
+    staged = M.moe_combine(D, y, inv, gates, out_dtype=dt)
+    torch.cuda.synchronize()
+    del xp, y
+    ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    say(f"moe_layer perturbed schedule {name} seed={seed} order={order}")
+    out = M.moe_layer(D, t["x"], t["w_router"], t["w_gate"], t["w_up"], t["w_down"], t["bias"],
+                      out_dtype=dt, ws=ws, opts=M.layer_opts(tile_order=order, perturb_seed=seed),
+                      check_status=True)
+    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
+    assert torch.equal(out.view(bits), staged.view(bits)), "perturbed fused != staged"
+    toks = np.arange(cfg.T) if cfg.T <= 600 else sample_tokens(cfg.T, 48, seed=seed)
+    oref, _, _ = oracle.layer_tokens(toks, arrs["x"], arrs["w_router"], arrs["w_gate"],
+                                     arrs["w_up"], arrs["w_down"], cfg.k, cfg.e_lo, cfg.E_hi,
+                                     bias=arrs["bias"])
+    err = rel_err(host_f32(out[torch.as_tensor(toks, device="cuda")]), oref)
+    say(f"  perturbed rel err {err:.3e} over {len(toks)} tokens")
+    assert err <= TOL_LAYER
+    del t, ws
+    torch.cuda.empty_cache()

@@ -204,3 +204,47 @@ def test_fp8_ffn_close_to_unquantised_ffn():
     rel = np.sqrt(((y8 - y) ** 2).mean(axis=1) / (y ** 2).mean(axis=1))
     assert np.all(rel < 0.15), rel
     assert np.all(rel > 1e-3), rel  # the quantisation is really applied
+
+
+def test_fp8_gemm_halves_equal_dense_products_and_the_whole_ffn():
+    """oracle.gate_up_rows_fp8 against numpy float64 dense products of the
+    decoded codes with the row and channel scales (the textbook definition,
+    computed here independently of the oracle's loops); its bf16 rounding is
+    expert_rows_fp8's h.  oracle.down_rows_fp8 against a numpy dense product
+    of given codes and scales; fed the oracle's own quantised h it reproduces
+    expert_rows_fp8's y.  Non-uniform scales catch a scale on the wrong axis,
+    random signs a dropped or mis-signed term, f != d a transposed operand."""
+    rng = np.random.default_rng(31)
+    n, d, f, EL = 7, 96, 48, 3
+    x = to_bf16(rng.standard_normal((n, d)) * 2.0 ** rng.integers(-4, 4, (n, 1)))
+    q = lambda w: oracle.quantize_rows_e4m3(w.reshape(-1, w.shape[-1]))
+    wg = to_bf16(rng.standard_normal((EL, f, d)) * 2.0 ** rng.integers(-9, -2, (EL, f, 1)))
+    wu = to_bf16(rng.standard_normal((EL, f, d)) * 2.0 ** rng.integers(-9, -2, (EL, f, 1)))
+    wd = to_bf16(rng.standard_normal((EL, d, f)) * 2.0 ** rng.integers(-9, -2, (EL, d, 1)))
+    (gq, gs), (uq, us), (dq, ds) = q(wg), q(wu), q(wd)
+    gq, uq, dq = gq.reshape(wg.shape), uq.reshape(wu.shape), dq.reshape(wd.shape)
+    gs, us, ds = gs.reshape(EL, f), us.reshape(EL, f), ds.reshape(EL, d)
+    eor = rng.integers(0, EL, n).astype(np.int32)
+    h = oracle.gate_up_rows_fp8(x, eor, gq, gs, uq, us)
+    xq, xs = oracle.quantize_rows_e4m3(x)
+    for r in range(n):
+        e = eor[r]
+        xr = dec(xq[r]) * float(xs[r])
+        g = (dec(gq[e]) * gs[e][:, None].astype(np.float64)) @ xr
+        u = (dec(uq[e]) * us[e][:, None].astype(np.float64)) @ xr
+        href = g / (1.0 + np.exp(-g)) * u
+        assert np.allclose(h[r], href, rtol=1e-12, atol=1e-300)
+    y_whole, h_whole = oracle.expert_rows_fp8(x, eor, gq, gs, uq, us, dq, ds, want_h=True)
+    hb = to_bf16(h)
+    assert np.array_equal(W.bf16_bits_to_f32(hb).astype(np.float64), h_whole)
+    # GEMM1 from arbitrary codes and scales
+    hq = (rng.integers(0, 0x7F, (n, f)) | (rng.integers(0, 2, (n, f)) << 7)).astype(np.uint8)
+    hs = (2.0 ** rng.integers(-10, 3, n)).astype(np.float32)
+    y = oracle.down_rows_fp8(hq, hs, eor, dq, ds)
+    for r in range(n):
+        e = eor[r]
+        yref = (dec(dq[e]) * ds[e][:, None].astype(np.float64)) @ (dec(hq[r]) * float(hs[r]))
+        assert np.allclose(y[r], yref, rtol=1e-12, atol=1e-300)
+    # the oracle's own quantised h reproduces the whole FFN
+    hq2, hs2 = oracle.quantize_rows_e4m3(hb)
+    assert np.array_equal(oracle.down_rows_fp8(hq2, hs2, eor, dq, ds), y_whole)
