@@ -221,6 +221,24 @@ moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_
  * once in float32, exactly as moe_layer does, so both give the same bits.
  * The workspace starts with the status word read by moe_device_status.
  */
+/* ---- moe_permute_noalloc: moe_permute for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments and results as moe_permute, without the
+ * workspace: the per-token-block counts and bases go to a scratch array that
+ * the library holds in device memory, one per GPU, for the life of the
+ * process (moe_permute_noalloc_max_ints() int32s; 2 * ceil(T / 256) * E_loc
+ * of them are used, MOE_ERR_UNSUPPORTED beyond that).  The call allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library routine.  Every
+ * call writes the scratch it reads, so nothing needs clearing between calls;
+ * but all calls on one GPU share it, so calls that may overlap on one GPU
+ * (concurrent streams, or several host threads) race and must be ordered by
+ * the caller.  The first call on a device looks up the array's device
+ * address (MOE_ERR_HIP if that fails). */
+size_t moe_permute_noalloc_max_ints(void);
+moe_status moe_permute_noalloc(const moe_dims *dims, const void *x, const int32_t *topk_ids,
+                               int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                               int32_t *inv_perm, void *x_perm, void *stream);
+
 size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims);
 moe_status moe_expert_ffn(const moe_dims *dims, const void *x_perm, const int32_t *offsets,
                           const void *w_gate, const void *w_up, const void *w_down, void *y_perm,

@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MoEDims", "lib_path", "load", "exported_abi_names", "header_abi_names",
     "moe_route", "moe_route_bounds", "moe_probe_mfma", "moe_gate_up_fp8", "moe_down_fp8",
-    "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer",
+    "moe_permute", "moe_permute_noalloc", "moe_expert_ffn", "moe_combine", "moe_layer",
     "moe_route_workspace_bytes",
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
@@ -118,6 +118,8 @@ def load():
         "moe_down_fp8": ([dp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_permute_workspace_bytes": ([dp], sz),
         "moe_permute": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_permute_noalloc_max_ints": ([], sz),
+        "moe_permute_noalloc": ([dp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_expert_ffn_workspace_bytes": ([dp], sz),
         "moe_expert_ffn": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_quantize_fp8": ([vp, i64, i64, vp, vp, vp], i32),
@@ -307,6 +309,30 @@ def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv
                             _ptr(perm_src), _ptr(inv_perm), _ptr(x_perm), _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "moe_permute")
+    return counts, offsets, perm_src, inv_perm, x_perm
+
+
+def moe_permute_noalloc(dims, x, topk_ids, counts, offsets, perm_src, inv_perm, x_perm,
+                        stream=None):
+    """moe_permute without a workspace and without any allocation: the caller
+    passes every output (counts [E_loc], offsets [E_loc+1], perm_src [T*k],
+    inv_perm [T,k], x_perm [T*k, d]); the library's per-GPU scratch array holds
+    the per-block counts.  Calls that overlap on one GPU race."""
+    import torch
+    D = _dims(dims)
+    EL, cap = D.e_hi - D.e_lo, D.T * D.k
+    _require(x, torch.bfloat16, (D.T, D.d), "x")
+    _require(topk_ids, torch.int32, (D.T, D.k), "topk_ids")
+    _require(counts, torch.int32, (EL,), "counts")
+    _require(offsets, torch.int32, (EL + 1,), "offsets")
+    _require(inv_perm, torch.int32, (D.T, D.k), "inv_perm")
+    if perm_src.dtype != torch.int32 or perm_src.numel() < cap or x_perm.dtype != torch.bfloat16 \
+            or x_perm.shape[0] < cap or x_perm.shape[1] != D.d:
+        raise ValueError("perm_src must hold T*k int32 rows, x_perm T*k bf16 rows of d")
+    rc = load().moe_permute_noalloc(C.byref(D), _ptr(x), _ptr(topk_ids), _ptr(counts),
+                                    _ptr(offsets), _ptr(perm_src), _ptr(inv_perm), _ptr(x_perm),
+                                    _stream(stream))
+    _check(rc, "moe_permute_noalloc")
     return counts, offsets, perm_src, inv_perm, x_perm
 
 

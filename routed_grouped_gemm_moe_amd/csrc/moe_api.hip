@@ -3,6 +3,8 @@
 // workspace layout and the launch sequences of every entry point.  Nothing is
 // kept between calls but a per-device property cache (grid size, clock rate):
 // every option travels with its call.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -108,6 +110,31 @@ moe_status check_opts(const moe_layer_opts *o, bool staged_fp8) {
     return MOE_OK;
 }
 
+// The scratch of moe_permute_noalloc: a file-scope device array, one copy per
+// GPU, kept until the process ends.  Host code never passes its name to a
+// kernel (on the host that name is only a stand-in): the device address is
+// taken once per device with hipGetSymbolAddress, with that device current,
+// and kept per device.
+constexpr int64_t NOALLOC_SCRATCH_INTS = 1 << 18;  // 1 MiB
+static __device__ __align__(256) int32_t scratch[NOALLOC_SCRATCH_INTS];
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+moe_status noalloc_scratch(int32_t **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 // Records opts->events[i] (if given) on the stream.
 hipError_t mark_event(const moe_layer_opts *o, int i, hipStream_t s) {
     if (!o || !o->events[i]) return hipSuccess;
@@ -200,6 +227,28 @@ moe_status moe_permute(const moe_dims *dims, const void *x, const int32_t *topk_
                                      inv_perm, (bf16_t *)x_perm, at<int32_t>(ws, L.blk_counts),
                                      at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr,
                                      nullptr, nullptr, 0, (hipStream_t)stream));
+}
+
+size_t moe_permute_noalloc_max_ints(void) { return NOALLOC_SCRATCH_INTS; }
+
+moe_status moe_permute_noalloc(const moe_dims *dims, const void *x, const int32_t *topk_ids,
+                               int32_t *counts, int32_t *offsets, int32_t *perm_src,
+                               int32_t *inv_perm, void *x_perm, void *stream) {
+    Dims D;
+    moe_status st = check_dims(dims, &D);
+    if (st != MOE_OK) return st;
+    if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+    if (D.T > 0 && (!x || !topk_ids || !perm_src || !inv_perm || !x_perm))
+        return MOE_ERR_INVALID_ARG;
+    if (D.T > 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARG;
+    // per-block counts and bases of the permute, both written whole by every call
+    const int64_t blk = D.perm_blocks() * D.EL();
+    if (2 * blk > NOALLOC_SCRATCH_INTS) return MOE_ERR_UNSUPPORTED;
+    int32_t *scr = nullptr;
+    if ((st = noalloc_scratch(&scr)) != MOE_OK) return st;
+    return hip_status(launch_permute(D, (const bf16_t *)x, topk_ids, counts, offsets, perm_src,
+                                     inv_perm, (bf16_t *)x_perm, scr, scr + blk, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, 0, (hipStream_t)stream));
 }
 
 size_t moe_expert_ffn_workspace_bytes(const moe_dims *dims) {

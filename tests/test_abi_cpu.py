@@ -218,3 +218,19 @@ def test_verification_entry_points_check_arguments():
     assert lib.moe_down_fp8(C.byref(D), *dn, FAKE_WS, need - 1, None) == WORKSPACE
     assert lib.moe_down_fp8(C.byref(D), C.c_void_p(0x10002), *dn[1:], FAKE_WS, need,
                             None) == INVALID
+
+
+def test_noalloc_permute_checks_sizes_before_any_gpu_call():
+    lib = M.load()
+    assert lib.moe_permute_noalloc_max_ints() == 1 << 18
+    # 2 * ceil(T / 256) * E_loc scratch ints: beyond the array is unsupported
+    D = dims(T=32768 + 256, d=256, E=1024, k=2)
+    assert lib.moe_permute_noalloc(C.byref(D), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == UNSUPPORTED
+    D = dims()
+    assert lib.moe_permute_noalloc(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                   None) == INVALID
+    assert lib.moe_permute_noalloc(C.byref(D), C.c_void_p(0x10002), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, None) == INVALID
+    assert lib.moe_permute_noalloc(C.byref(dims(k=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == INVALID
