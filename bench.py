@@ -26,6 +26,8 @@ Other modes:
                      per-kernel medians of the timed dispatches in the
                      rocprofv3 kernel trace (csv) under DIR, skipping the
                      warm-up dispatches (give the run's --warmup / --steps)
+  --summarize-counters DIR
+                     per-kernel means of the rocprofv3 counters (csv) under DIR
 """
 from __future__ import annotations
 
@@ -109,6 +111,23 @@ def summarize_trace(args) -> None:
               f"median_us={median(timed):10.2f} mean_us={sum(timed) / len(timed):10.2f} "
               f"min_us={min(timed):10.2f} max_us={max(timed):10.2f} "
               f"pct_all={100 * sum(v) / total:6.2f}" + ("" if per else "  (not per-step)"))
+
+
+def summarize_counters(args) -> None:
+    """Per-kernel mean of every counter in the rocprofv3 counter collections
+    (csv) under DIR, over all dispatches of that kernel."""
+    acc = {}
+    for p in sorted(glob.glob(os.path.join(args.summarize_counters, "**",
+                                           "*counter_collection.csv"), recursive=True)):
+        with open(p) as fh:
+            for r in csv.DictReader(fh):
+                key = (short_name(r["Kernel_Name"]), r["Counter_Name"])
+                acc.setdefault(key, {})
+                d = acc[key]
+                d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    for (k, c), d in sorted(acc.items()):
+        v = list(d.values())
+        print(f"  {k:40s} {c:28s} dispatches={len(v):3d} mean={sum(v) / len(v):.6e}")
 
 
 # ------------------------------------------------------------ modes
@@ -332,10 +351,14 @@ def main() -> None:
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
                     help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
     ap.add_argument("--summarize-trace", default=None, metavar="DIR")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR")
     args = ap.parse_args()
 
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "

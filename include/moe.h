@@ -104,11 +104,18 @@ typedef enum {
                                  tile follows the last gate/up tile it reads by
                                  at least `lead` gate/up tiles (down first
                                  whenever it is eligible) */
-    MOE_ORDER_COMBINE_FIRST = 3 /* tile-level signaling, consumers first: down
+    MOE_ORDER_COMBINE_FIRST = 3, /* tile-level signaling, consumers first: down
                                  tiles are claimed column group by column group
                                  (the columns one combine tile covers), and
                                  before each down claim a workgroup takes a
                                  combine tile whose column group is complete */
+    MOE_ORDER_CHUNKED = 4     /* Weave §3.2.1's chunk pipeline: the tokens are
+                                 cut into `chunks` ranges; an m-tile belongs to
+                                 the chunk of its last token, a combine tile to
+                                 the latest chunk its rows live in; gate/up,
+                                 down and combine tiles form one stream ordered
+                                 by (chunk, kind), so chunk c's combine runs
+                                 while chunk c+1's GEMMs do */
 } moe_tile_order;
 
 typedef struct {
@@ -116,12 +123,15 @@ typedef struct {
     int32_t tile_order;      /* moe_tile_order (moe_layer only) */
     int32_t lead;            /* MOE_ORDER_LEAD: the lead in gate/up tiles; 0 =
                                 one round of the persistent grid */
+    int32_t chunks;          /* MOE_ORDER_CHUNKED: token chunks, 1..8; 0 = 4 */
     uint32_t perturb_seed;   /* moe_layer only; 0 = off.  A test aid for the
                                 flag protocol: every producer tile waits a
                                 seeded pseudo-random delay (0 to about 100 us)
                                 between writing its output and publishing it,
                                 and (orders 0, 1, 3) the tiles of each kind are
-                                claimed in reverse order.  The result bits are
+                                claimed in reverse order (orders 2 and 4 hand
+                                out one dependency-ordered stream, which must be
+                                claimed in order).  The result bits are
                                 unchanged; only the timing is adversarial. */
     int64_t wait_timeout_us; /* moe_layer only: bound of each device-side flag
                                 wait; 0 = 2 s.  A wait that times out records

@@ -26,7 +26,7 @@ __all__ = [
     "moe_layer_workspace_bytes", "moe_device_status", "moe_status_string",
     "MoELayerOpts", "layer_opts", "moe_wall_clock_hz", "MoEError",
     "MOE_DISPATCH_PACKED", "MOE_DISPATCH_GATHER", "MOE_ORDER_BY_KIND", "MOE_ORDER_READY_DOWN",
-    "MOE_ORDER_LEAD", "MOE_ORDER_COMBINE_FIRST",
+    "MOE_ORDER_LEAD", "MOE_ORDER_COMBINE_FIRST", "MOE_ORDER_CHUNKED",
     "MOE_BF16", "MOE_F32",
 ]
 
@@ -37,6 +37,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
 MOE_BF16, MOE_F32 = 0, 1
 MOE_DISPATCH_PACKED, MOE_DISPATCH_GATHER = 0, 1
 MOE_ORDER_BY_KIND, MOE_ORDER_READY_DOWN, MOE_ORDER_LEAD, MOE_ORDER_COMBINE_FIRST = 0, 1, 2, 3
+MOE_ORDER_CHUNKED = 4
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_TIMEOUT"}
 
@@ -59,7 +60,7 @@ class MoEDims(C.Structure):
 class MoELayerOpts(C.Structure):
     """Per-call options of moe_layer / moe_layer_fp8 (include/moe.h)."""
     _fields_ = [("dispatch", C.c_int32), ("tile_order", C.c_int32), ("lead", C.c_int32),
-                ("perturb_seed", C.c_uint32), ("wait_timeout_us", C.c_int64),
+                ("chunks", C.c_int32), ("perturb_seed", C.c_uint32), ("wait_timeout_us", C.c_int64),
                 ("trace", C.c_void_p), ("trace_records", C.c_int64),
                 ("events", C.c_void_p * 4)]
 
@@ -74,14 +75,14 @@ def _event_handle(ev) -> Optional[int]:
 
 
 def layer_opts(dispatch: int = MOE_DISPATCH_PACKED, tile_order: int = MOE_ORDER_BY_KIND,
-               lead: int = 0, perturb_seed: int = 0, wait_timeout_us: int = 0, trace=None,
-               trace_records: int = 0, events=None) -> MoELayerOpts:
+               lead: int = 0, chunks: int = 0, perturb_seed: int = 0, wait_timeout_us: int = 0,
+               trace=None, trace_records: int = 0, events=None) -> MoELayerOpts:
     """Build a MoELayerOpts.  trace: int64 device tensor of 1 + 4*trace_records
     elements (element 0 zeroed by the caller); events: up to 4 torch.cuda.Event
     (or None) recorded before the route, after the route, after the permute
     and after the last launch."""
     o = MoELayerOpts()
-    o.dispatch, o.tile_order, o.lead = int(dispatch), int(tile_order), int(lead)
+    o.dispatch, o.tile_order, o.lead, o.chunks = int(dispatch), int(tile_order), int(lead), int(chunks)
     o.perturb_seed, o.wait_timeout_us = int(perturb_seed), int(wait_timeout_us)
     if trace is not None:
         o.trace, o.trace_records = trace.data_ptr(), int(trace_records)

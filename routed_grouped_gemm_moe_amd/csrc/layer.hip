@@ -369,17 +369,18 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
     // sorted table, each preceded by a try for a combine tile whose column
     // group is complete (kind bit COMB) -- and phase 3 the remaining combine
     // tiles.  The dependency-lead order replaces phases 1 and 2 by phase 0:
-    // the merged stream of its table, in the gate/up queues.
+    // the merged stream of its table, in the gate/up queues; the chunked order
+    // replaces all three by phase 0 (its stream holds the combine tiles too).
     const int n1 = MT * NT1;
     constexpr int DOWN = 1 << 30, COMB = 1 << 29;
-    const int nM = a.order == 2 ? n1 + n2c : 0;
-    int phase = a.order == 2 ? 0 : n1 > 0 ? 1 : 2;
+    const int nM = a.order == 2 ? n1 + n2c : a.order == 4 ? n1 + n2c + n3 : 0;
+    int phase = a.order == 2 || a.order == 4 ? 0 : n1 > 0 ? 1 : 2;
     if (n1 > 0 || n2 > 0 || n3 > 0)
         for (;;) {
             if (wave_id() == 0) {
                 int v;
                 if (phase == 0) {
-                    const int p = claim_tile(q1, nM, xcd);  // never reversed: see launch_build_order
+                    const int p = claim_tile(q1, nM, xcd);  // never reversed: see build_order_kernel
                     v = p >= 0 ? uniform(a.order_tab[p]) : -1;
                 } else if (phase == 1) {
                     const int r = a.order == 1 && n2 > 0
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 continue;
             }
             if (v < 0) {
-                if (phase == 0) {  // the merged stream is drained: combine tiles
+                if (phase == 0 && a.order == 2) {  // the merged stream is drained: combine tiles
                     phase = 3;
                     continue;
                 }
@@ -481,7 +482,22 @@ __device__ __forceinline__ int gu_last_pos(int mt, int MT, int NT1, int EL, cons
 // each XCD finishes its share of column group 0 first.  128 threads per
 // range count their run of claims per group (LDS), exclusive scans give every
 // thread its slots, and a second pass places the claims.
+//
+// Order 4 (chunk pipeline, Weave §3.2.1): the tokens are cut into `chunks`
+// equal ranges; an m-tile belongs to the chunk of its last row's token (rows
+// are in token order inside an expert), a combine tile to the latest chunk of
+// any m-tile its tokens' rows live in.  Every gate/up tile, down claim and
+// combine tile gets the key (chunk, kind) and the stream is the stable sort by
+// key: chunk by chunk, gate/up before down before combine.  A down claim's
+// producers (its m-tile's gate/up tiles) and a combine tile's (the down tiles
+// of its rows) have smaller keys, so they sit earlier in the stream, and the
+// argument of order 2 applies.  Counting sort as in order 3, over all the
+// stream's elements.
 __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
+    // LDS of every order: order 2 a scan over the threads, order 3 per-thread
+    // counts of each column group, order 4 per-thread counts of each key
+    __shared__ int s_buf[1024 * 3 * ORDER4_MAX_CHUNKS];
+    __shared__ int s_small[NUM_XCD * ORDER3_MAX_CG];
     const Dims &D = a.D;
     const int MT = *a.n_mtiles;
     const int NT1 = (int)D.nt_gu(), NT2 = (int)D.nt_dn(), EL = (int)D.EL();
@@ -497,7 +513,7 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
         return mt;
     };
     if (a.order == 2) {
-        __shared__ int s_pre[1024];
+        int *s_pre = s_buf;
         int32_t *P = a.order_tmp;
         const int q = (n2c + 1023) / 1024, lo = min(n2c, tid * q), hi = min(n2c, lo + q);
         int m = -1;
@@ -535,8 +551,8 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
             a.order_tab[i + l] = i;
         }
     } else if (a.order == 3) {
-        __shared__ int s_cnt[1024][ORDER3_MAX_CG];
-        __shared__ int s_start[NUM_XCD][ORDER3_MAX_CG];
+        int(*s_cnt)[ORDER3_MAX_CG] = reinterpret_cast<int(*)[ORDER3_MAX_CG]>(s_buf);
+        int(*s_start)[ORDER3_MAX_CG] = reinterpret_cast<int(*)[ORDER3_MAX_CG]>(s_small);
         const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
         const int per = (n2c + NUM_XCD - 1) / NUM_XCD;
         const int r = tid / 128, j = tid % 128;
@@ -574,13 +590,79 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
             const int c = nt / COMB_CB;
             a.order_tab[rlo + s_start[r][c] + s_cnt[tid][c]++] = LS;
         }
+    } else if (a.order == 4) {
+        constexpr int NKMAX = 3 * ORDER4_MAX_CHUNKS;
+        int(*s_cnt)[NKMAX] = reinterpret_cast<int(*)[NKMAX]>(s_buf);
+        int *s_base = s_small;
+        const int K = a.chunks, NK = 3 * K;
+        const int64_t k = D.k;
+        const int NTB = (int)D.comb_blocks(), NCG = (NT2 + COMB_CB - 1) / COMB_CB;
+        const int n3 = NTB * NCG;
+        auto chunk_of_mtile = [&](int m) {
+            const MTile t = a.mtiles[m];
+            const int64_t last = a.perm_src[t.row0 + t.rows - 1];
+            return (int)min((int64_t)K - 1, (int64_t)K * last / D.T);
+        };
+        // the chunk of every combine token block, into order_tmp
+        for (int tb = tid; tb < NTB; tb += 1024) {
+            int c = 0;
+            for (int64_t i = 0; i < COMB_TOK * k; ++i) {
+                const int64_t t = (int64_t)tb * COMB_TOK + i / k, j = i % k;
+                if (t >= D.T) break;
+                const int32_t p = a.inv_perm[t * k + j];
+                if (p < 0) continue;
+                const int32_t e = a.ids[t * k + j] - (int32_t)D.e_lo;
+                c = max(c, chunk_of_mtile(a.mtile_base[e] + (p - a.offsets[e]) / BM));
+            }
+            a.order_tmp[tb] = c;
+        }
+        __syncthreads();
+        const int total = n1 + n2c + n3;
+        auto key_of = [&](int x) {
+            int nt;
+            if (x < n1) {
+                int m;
+                expert_tile(x, MT, NT1, EL, a.mtiles, a.mtile_base, &m, &nt);
+                return 3 * chunk_of_mtile(m);
+            }
+            if (x < n1 + n2c) return 3 * chunk_of_mtile(mt_of(x - n1, &nt)) + 1;
+            return 3 * a.order_tmp[(x - n1 - n2c) % NTB] + 2;
+        };
+        const int q = (total + 1023) / 1024, lo = min(total, tid * q), hi = min(total, lo + q);
+        for (int c = 0; c < NK; ++c) s_cnt[tid][c] = 0;
+        for (int x = lo; x < hi; ++x) s_cnt[tid][key_of(x)] += 1;
+        __syncthreads();
+        if (tid < NK) {  // exclusive scan of key tid over the threads
+            int run = 0;
+            for (int t = 0; t < 1024; ++t) {
+                const int v = s_cnt[t][tid];
+                s_cnt[t][tid] = run;
+                run += v;
+            }
+            s_base[tid] = run;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int run = 0;
+            for (int c = 0; c < NK; ++c) {
+                const int v = s_base[c];
+                s_base[c] = run;
+                run += v;
+            }
+        }
+        __syncthreads();
+        for (int x = lo; x < hi; ++x) {
+            const int key = key_of(x);
+            const int v = x < n1 ? x : x < n1 + n2c ? (x - n1) | (1 << 30) : (x - n1 - n2c) | (1 << 29);
+            a.order_tab[s_base[key] + s_cnt[tid][key]++] = v;
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_build_order(const LayerArgs &a, int grid, hipStream_t s) {
-    if (a.order != 2 && a.order != 3) return hipSuccess;
+    if (a.order < 2 || a.order > 4) return hipSuccess;
     hipLaunchKernelGGL(build_order_kernel, dim3(1), dim3(1024), 0, s, a, grid);
     return hipGetLastError();
 }

@@ -3,6 +3,7 @@
 // workspace layout and the launch sequences of every entry point.  Nothing is
 // kept between calls but a per-device property cache (grid size, clock rate):
 // every option travels with its call.
+#include <algorithm>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -38,8 +39,9 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     // claim tables of tile orders 2 and 3 (written whole by their builder)
     const size_t n1max = MT * (size_t)D.nt_gu();
     const size_t n2max = MT * (size_t)D.nt_dn() + (CUT_MAX - 1) * (size_t)SPLIT_MAX;
-    L.order_tab = take(layer ? (n1max + n2max) * sizeof(int32_t) : 0);
-    L.order_tmp = take(layer ? n2max * sizeof(int32_t) : 0);
+    const size_t n3 = (size_t)(D.comb_blocks() * comb_groups(D.d));
+    L.order_tab = take(layer ? (n1max + n2max + n3) * sizeof(int32_t) : 0);
+    L.order_tmp = take(layer ? std::max(n2max, (size_t)D.comb_blocks()) * sizeof(int32_t) : 0);
     L.route = take(layer ? route_workspace_bytes(D) : 0);
     L.ids = take(layer ? Tk * sizeof(int32_t) : 0);
     L.gates = take(layer ? Tk * sizeof(float) : 0);
@@ -97,15 +99,17 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 moe_status check_opts(const moe_layer_opts *o, bool staged_fp8) {
     if (!o) return MOE_OK;
     if (staged_fp8)
-        return (o->dispatch || o->tile_order || o->lead || o->perturb_seed ||
+        return (o->dispatch || o->tile_order || o->lead || o->chunks || o->perturb_seed ||
                 o->wait_timeout_us || o->trace || o->trace_records)
                    ? MOE_ERR_INVALID_ARG
                    : MOE_OK;
     if (o->dispatch != MOE_DISPATCH_PACKED && o->dispatch != MOE_DISPATCH_GATHER)
         return MOE_ERR_INVALID_ARG;
-    if (o->tile_order < MOE_ORDER_BY_KIND || o->tile_order > MOE_ORDER_COMBINE_FIRST)
+    if (o->tile_order < MOE_ORDER_BY_KIND || o->tile_order > MOE_ORDER_CHUNKED)
         return MOE_ERR_INVALID_ARG;
-    if (o->lead < 0 || o->wait_timeout_us < 0 || o->trace_records < 0) return MOE_ERR_INVALID_ARG;
+    if (o->lead < 0 || o->chunks < 0 || o->chunks > ORDER4_MAX_CHUNKS || o->wait_timeout_us < 0 ||
+        o->trace_records < 0)
+        return MOE_ERR_INVALID_ARG;
     if (o->trace_records > 0 && !o->trace) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
@@ -626,6 +630,7 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         a.gather = gather ? 1 : 0;
         a.order = o.tile_order;
         a.lead = o.lead > 0 ? o.lead : grid;
+        a.chunks = o.chunks > 0 ? o.chunks : 4;
         a.perturb = o.perturb_seed;
         a.x = (const bf16_t *)x;
         a.perm_src = at<int32_t>(ws, L.perm_src);

@@ -253,10 +253,12 @@ struct LayerArgs {
     // tiles first
     int order;
     int lead;          // order 2: the lead in gate/up tiles
+    int chunks;        // order 4: token chunks
     uint32_t perturb;  // schedule perturbation seed (0 = off)
-    // orders 2 and 3: claim table built on the device (build_order_kernel):
+    // orders 2 to 4: claim table built on the device (build_order_kernel):
     // order 2 the merged stream (gate/up index, or down claim | 1 << 30),
-    // order 3 the down claims of every XCD range sorted by column group
+    // order 3 the down claims of every XCD range sorted by column group,
+    // order 4 the chunked stream (as order 2, combine tiles | 1 << 29)
     int32_t *order_tab;
     int32_t *order_tmp;  // order 2: scratch of the table builder
     int32_t *dn_cg;      // published down tiles per combine column group (cleared per call)
@@ -276,7 +278,7 @@ struct LayerArgs {
     int64_t trace_cap;   // records that fit after the count
 };
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s);
-// The claim table of tile orders 2 and 3 (a.order_tab), from the m-tile table
+// The claim table of tile orders 2 to 4 (a.order_tab), from the m-tile table
 // on the device; nothing for the other orders.
 hipError_t launch_build_order(const LayerArgs &a, int grid, hipStream_t s);
 // Column groups of the combine tiles (COMB_CB column blocks each).
@@ -286,6 +288,9 @@ __host__ __device__ inline int64_t comb_groups(int64_t d) {
 // Largest column-group count tile order 3 supports (its table builder keeps
 // per-thread counts of every group in LDS).
 constexpr int ORDER3_MAX_CG = 16;
+// Largest chunk count of tile order 4 (its table builder keeps per-thread
+// counts of every (chunk, kind) key in LDS).
+constexpr int ORDER4_MAX_CHUNKS = 8;
 int layer_grid_size();  // resident workgroups of the persistent kernel (cached)
 int64_t wall_clock_hz(); // frequency of wall_clock64 on the current device (cached)
 

@@ -168,14 +168,15 @@ def test_layer_options_are_checked_per_call():
             setattr(o, k, v)
         return C.byref(o)
 
-    for bad in (dict(dispatch=2), dict(dispatch=-1), dict(tile_order=4), dict(tile_order=-1),
-                dict(lead=-1), dict(wait_timeout_us=-5), dict(trace_records=-1),
+    for bad in (dict(dispatch=2), dict(dispatch=-1), dict(tile_order=5), dict(tile_order=-1),
+                dict(lead=-1), dict(chunks=-1), dict(chunks=9), dict(wait_timeout_us=-5),
+                dict(trace_records=-1),
                 dict(trace_records=8)):  # records without a buffer
         assert lib.moe_layer(*args, opts(**bad), None) == INVALID, bad
     # the W8A8 layer takes events only
     w = (FAKE,) * 9
     need8 = M.moe_layer_fp8_workspace_bytes(D)
-    for bad in (dict(dispatch=1), dict(tile_order=1), dict(perturb_seed=3),
+    for bad in (dict(dispatch=1), dict(tile_order=1), dict(chunks=2), dict(perturb_seed=3),
                 dict(wait_timeout_us=10)):
         assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need8,
                                  opts(**bad), None) == INVALID, bad
@@ -183,7 +184,7 @@ def test_layer_options_are_checked_per_call():
     for name in ("moe_set_tile_order", "moe_set_gather_dispatch", "moe_set_trace",
                  "moe_set_wait_timeout_us", "moe_timing_enable", "moe_timing_read"):
         assert not hasattr(lib, name), name
-    assert C.sizeof(M.MoELayerOpts) == 72
+    assert C.sizeof(M.MoELayerOpts) == 80
 
 
 def test_verification_entry_points_check_arguments():

@@ -420,7 +420,7 @@ def test_gather_on_load_dispatch(name):
     torch.cuda.empty_cache()
 
 
-ORDERS = [1, 2, 3]
+ORDERS = [1, 2, 3, 4]
 
 
 @pytest.mark.parametrize("order", ORDERS)
@@ -467,7 +467,7 @@ def _perturb_case(name):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("order", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("name,seed", [("tiny", 1), ("multi_tile_rows", 2), ("e128k8", 3),
                                        ("local_subset_e16k4", 4), ("hot18", 5), ("cut4", 6),
                                        ("fine", 7)])
@@ -475,8 +475,8 @@ def test_adversarial_schedule_same_bits_and_match_oracle(name, seed, order):
     """The flag protocol under adversarial timing: producers wait seeded
     pseudo-random delays (up to ~100 us) between writing their tiles and
     publishing them, and each kind's tiles are claimed from the far end of
-    every range (not in the dependency-lead order, whose merged stream must
-    be claimed in order).  A consumer that read before its producer's release would
+    every range (not in the dependency-lead and chunked orders, whose merged
+    streams must be claimed in order).  A consumer that read before its producer's release would
     see the NaN bytes the workspace starts with, or stale rows; the output
     must instead equal the staged calls bit for bit and match the oracle."""
     cfg = _perturb_case(name)
