@@ -345,9 +345,10 @@ def main() -> None:
                     help="skip the extra W8A8 layer measurement of the default mode")
     ap.add_argument("--no-stage-probe", action="store_true",
                     help="skip the standalone route / permute / combine measurements")
-    ap.add_argument("--tile-order", type=int, default=0, choices=[0, 1, 2, 3],
+    ap.add_argument("--tile-order", type=int, default=0, choices=[0, 1, 2, 3, 4],
                     help="moe_layer tile order (moe_tile_order)")
     ap.add_argument("--lead", type=int, default=0, help="dependency lead of tile order 2")
+    ap.add_argument("--chunks", type=int, default=0, help="token chunks of tile order 4")
     ap.add_argument("--dispatch", default="packed", choices=["packed", "gather"],
                     help="moe_layer dispatch: packed x_perm (default) or gather rows on load")
     ap.add_argument("--summarize-trace", default=None, metavar="DIR")
@@ -402,7 +403,8 @@ def main() -> None:
         return
 
     base = dict(dispatch=M.MOE_DISPATCH_GATHER if args.dispatch == "gather" else
-                M.MOE_DISPATCH_PACKED, tile_order=args.tile_order, lead=args.lead)
+                M.MOE_DISPATCH_PACKED, tile_order=args.tile_order, lead=args.lead,
+                chunks=args.chunks)
     ws = torch.empty(M.moe_layer_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     gates = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
@@ -473,6 +475,7 @@ def main() -> None:
         "config": {"workload": f"{cfg.name}: {cfg.note}", "T": cfg.T, "d": cfg.d, "f": cfg.f,
                    "E": cfg.E, "k": cfg.k, "local_experts": [cfg.e_lo, cfg.E_hi],
                    "dispatch": args.dispatch, "tile_order": args.tile_order,
+                   "lead": args.lead, "chunks": args.chunks,
                    "parallelism": "none (one GPU)"},
         "grouped_gemm_tflops": round(ffn_tflops, 2),
         "grouped_gemm_pct_mfma_peak": round(100 * ffn_tflops / PEAK_BF16_TFLOPS, 2),

@@ -145,13 +145,15 @@ __device__ __forceinline__ int claim_ready_down(const LayerArgs &a, int32_t *q, 
     return old == cur ? idx : -1;
 }
 
-__device__ __forceinline__ int next_tile(int32_t *q, int n, int xcd, int *s_claim, bool rev) {
-    if (wave_id() == 0) *s_claim = claim_tile(q, n, xcd, rev);  // all lanes store the same value
-    __syncthreads();
-    const int L = uniform(*s_claim);
-    __syncthreads();
-    return L;
+// Claim the next entry of one global stream [0, n): a single counter, so
+// the entries are handed out in stream order in time as well.
+__device__ __forceinline__ int claim_in_order(int32_t *q, int n) {
+    if (uniform(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= n) return -1;
+    const int old = uniform(__hip_atomic_fetch_add(q, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    return old < n ? old : -1;
 }
+
 
 // Wave-uniform wait until every lane's flag satisfies *p >= target (lanes with
 // need == false do not wait).  Bounded in wall-clock time (wall_clock64
@@ -268,10 +270,12 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
     trace_tile(a, part < 0 ? 2 : 4, LS, xcd, t0);
 }
 
-// Combine-first order: the next combine tile of the first range whose next
-// tile's column group has every down tile published (the group's count in
-// dn_cg), claimed with a compare-and-swap as in claim_ready_down; -1 if none
-// is ready.  Such a tile's flag waits pass at once, so it never blocks.
+// Combine-first order: the next combine tile of the first range that still
+// has one, if that tile's column group has every down tile published (the
+// group's count in dn_cg), claimed with a compare-and-swap as in
+// claim_ready_down; -1 otherwise.  Such a tile's flag waits pass at once, so
+// it never blocks.  Only the first open range is looked at: each look is a
+// chain of L2 round trips paid before every down claim.
 __device__ __forceinline__ int claim_ready_combine(const LayerArgs &a, int32_t *q, int n3,
                                                    int NTB, int NT2, int MT, bool rev) {
     const int per = (n3 + NUM_XCD - 1) / NUM_XCD;
@@ -287,7 +291,7 @@ __device__ __forceinline__ int claim_ready_combine(const LayerArgs &a, int32_t *
         const int ncb = min(COMB_CB, NT2 - cg * COMB_CB);
         if (uniform(__hip_atomic_load(a.dn_cg + cg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
             MT * ncb)
-            continue;
+            return -1;
         const int old = uniform(atomicCAS(c, cur, lane_id() == 0 ? cur + 1 : cur));
         return old == cur ? idx : -1;
     }
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             if (wave_id() == 0) {
                 int v;
                 if (phase == 0) {
-                    const int p = claim_tile(q1, nM, xcd);  // never reversed: see build_order_kernel
+                    const int p = claim_in_order(q1, nM);  // never reversed: see build_order_kernel
                     v = p >= 0 ? uniform(a.order_tab[p]) : -1;
                 } else if (phase == 1) {
                     const int r = a.order == 1 && n2 > 0
@@ -471,17 +475,20 @@ __device__ __forceinline__ int gu_last_pos(int mt, int MT, int NT1, int EL, cons
 // gate/up tiles before it (at most n1), P(LS) = the running maximum of need
 // (down claims keep their order), so down claim LS lands at P(LS) + LS and
 // gate/up tile i at i + #{LS : P(LS) <= i}.  Every claim's producers sit at
-// earlier positions of the stream, which the persistent kernel hands out as
-// contiguous per-XCD ranges, own range first; the earliest unfinished claim
-// is therefore always runnable, so the stream cannot deadlock.  (That
-// argument needs claims in increasing order within a range, which is why the
-// schedule perturbation does not reverse this order.)
+// earlier positions of the stream, which the persistent kernel hands out in
+// order from one global counter (per-XCD ranges would let a later range run
+// ahead of the producers its down tiles need, so a lead in stream positions
+// would not be a lead in time); the earliest unfinished claim is therefore
+// always runnable, so the stream cannot deadlock.  (That argument needs
+// claims in stream order, which is why the schedule perturbation does not
+// reverse this order.)
 //
 // Order 3 (combine first): the down claims of every per-XCD range, stably
 // sorted by the combine column group of their tile (n-tile / COMB_CB), so
-// each XCD finishes its share of column group 0 first.  128 threads per
-// range count their run of claims per group (LDS), exclusive scans give every
-// thread its slots, and a second pass places the claims.
+// each XCD finishes its share of column group 0 first; the K parts of cut
+// tiles stay at the end of their range, where they fill its tail.  128
+// threads per range count their run of claims per group (LDS), exclusive
+// scans give every thread its slots, and a second pass places the claims.
 //
 // Order 4 (chunk pipeline, Weave §3.2.1): the tokens are cut into `chunks`
 // equal ranges; an m-tile belongs to the chunk of its last row's token (rows
@@ -497,7 +504,8 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
     // LDS of every order: order 2 a scan over the threads, order 3 per-thread
     // counts of each column group, order 4 per-thread counts of each key
     __shared__ int s_buf[1024 * 3 * ORDER4_MAX_CHUNKS];
-    __shared__ int s_small[NUM_XCD * ORDER3_MAX_CG];
+    constexpr int K3 = ORDER3_MAX_CG + 1;  // order 3's keys: the column groups, then cut parts
+    __shared__ int s_small[NUM_XCD * K3];
     const Dims &D = a.D;
     const int MT = *a.n_mtiles;
     const int NT1 = (int)D.nt_gu(), NT2 = (int)D.nt_dn(), EL = (int)D.EL();
@@ -551,21 +559,25 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
             a.order_tab[i + l] = i;
         }
     } else if (a.order == 3) {
-        int(*s_cnt)[ORDER3_MAX_CG] = reinterpret_cast<int(*)[ORDER3_MAX_CG]>(s_buf);
-        int(*s_start)[ORDER3_MAX_CG] = reinterpret_cast<int(*)[ORDER3_MAX_CG]>(s_small);
+        int(*s_cnt)[K3] = reinterpret_cast<int(*)[K3]>(s_buf);
+        int(*s_start)[K3] = reinterpret_cast<int(*)[K3]>(s_small);
         const int NCG = (NT2 + COMB_CB - 1) / COMB_CB;
         const int per = (n2c + NUM_XCD - 1) / NUM_XCD;
         const int r = tid / 128, j = tid % 128;
         const int rlo = min(n2c, r * per), rhi = min(n2c, rlo + per);
         const int q = (rhi - rlo + 127) / 128, lo = min(rhi, rlo + j * q), hi = min(rhi, lo + q);
-        for (int c = 0; c < ORDER3_MAX_CG; ++c) s_cnt[tid][c] = 0;
-        for (int LS = lo; LS < hi; ++LS) {
-            int nt;
+        // key: the column group of a whole tile; NCG (last) for a cut tile's part
+        auto key3 = [&](int LS) {
+            int L, part, st, nt;
+            dn_claim(LS, n2, nsp, S, &L, &part, &st);
+            if (part >= 0) return NCG;
             mt_of(LS, &nt);
-            s_cnt[tid][nt / COMB_CB] += 1;
-        }
+            return nt / COMB_CB;
+        };
+        for (int c = 0; c < K3; ++c) s_cnt[tid][c] = 0;
+        for (int LS = lo; LS < hi; ++LS) s_cnt[tid][key3(LS)] += 1;
         __syncthreads();
-        if (j < NCG) {  // thread (r, c = j): exclusive scan of group c over the range's threads
+        if (j <= NCG) {  // thread (r, c = j): exclusive scan of key c over the range's threads
             int run = 0;
             for (int t = 0; t < 128; ++t) {
                 const int v = s_cnt[r * 128 + t][j];
@@ -577,7 +589,7 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
         __syncthreads();
         if (j == 0) {
             int run = 0;
-            for (int c = 0; c < NCG; ++c) {
+            for (int c = 0; c <= NCG; ++c) {
                 const int v = s_start[r][c];
                 s_start[r][c] = run;
                 run += v;
@@ -585,9 +597,7 @@ __global__ __launch_bounds__(1024) void build_order_kernel(LayerArgs a, int G) {
         }
         __syncthreads();
         for (int LS = lo; LS < hi; ++LS) {
-            int nt;
-            mt_of(LS, &nt);
-            const int c = nt / COMB_CB;
+            const int c = key3(LS);
             a.order_tab[rlo + s_start[r][c] + s_cnt[tid][c]++] = LS;
         }
     } else if (a.order == 4) {

@@ -287,7 +287,7 @@ __host__ __device__ inline int64_t comb_groups(int64_t d) {
 }
 // Largest column-group count tile order 3 supports (its table builder keeps
 // per-thread counts of every group in LDS).
-constexpr int ORDER3_MAX_CG = 16;
+constexpr int ORDER3_MAX_CG = 15;  // + 1 key for the cut tiles' parts
 // Largest chunk count of tile order 4 (its table builder keeps per-thread
 // counts of every (chunk, kind) key in LDS).
 constexpr int ORDER4_MAX_CHUNKS = 8;
