@@ -1,9 +1,10 @@
 // Persistent expert-FFN + combine kernel of moe_layer.
 //
-// One workgroup per CU stays resident and claims tiles until none are left
-// (Weave, §4: a persistent kernel in which each SM claims its next tile with
-// an atomicAdd on a global counter, in the order of the chunk pipeline's
-// dependency graph).  Three tile kinds, claimed in dependency order:
+// The grid is sized to the CUs that fit at once; each workgroup keeps taking
+// work from device counters until every tile has been handed out, so the
+// tiles of all stages share one launch and their order is a property of the
+// queues rather than of kernel boundaries (the persistent scheduling of
+// Weave, §4).  Three tile kinds, claimed in dependency order:
 //   1. gate/up tiles (m-tile, 128 h columns): GEMM0 + SiLU-mul epilogue;
 //      each finished tile bumps gu_done[m-tile].
 //   2. down tiles (m-tile, 256 y columns): wait until gu_done[m-tile] counts
@@ -22,6 +23,9 @@
 // workgroup takes the next down tile of its XCD's range if that tile's m-tile
 // has all its gate/up tiles published (compare-and-swap, so only a ready
 // tile is taken); such a tile never waits, so the argument below holds.
+// The dependency-lead, combine-first and chunked orders replace the queues
+// by a claim table that build_order_kernel writes before the launch; their
+// rules sit beside that kernel.
 //
 // Queues: gate/up and down tiles follow the blocked order of gemm_tile.h and
 // each kind is split into 8 contiguous ranges, one per XCD.  A workgroup reads

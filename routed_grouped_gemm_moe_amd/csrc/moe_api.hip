@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "moe_internal.h"
+#include "scan.h"
 
 namespace moe {
 
@@ -47,6 +48,7 @@ Layout make_layout(const Dims &D, LayoutKind kind) {
     L.gates = take(layer ? Tk * sizeof(float) : 0);
     L.blk_counts = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
     L.blk_base = take(perm ? (size_t)D.perm_blocks() * EL * sizeof(int32_t) : 0);
+    L.arrive = take(layer ? sizeof(int32_t) : 0);
     L.counts = take(layer ? EL * sizeof(int32_t) : 0);
     L.offsets = take(layer ? (EL + 1) * sizeof(int32_t) : 0);
     L.pstart = take(ffn ? (EL + 1) * sizeof(int32_t) : 0);
@@ -379,8 +381,8 @@ hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offse
 // Workspace of moe_layer_fp8: routing, the row-major permute, x_perm and y
 // rows, then the FFN's Layout8 region.
 struct LayoutL8 {
-    size_t route, ids, gates, blk_counts, blk_base, counts, offsets, perm_src, inv_perm, x_perm, y,
-        ffn, total;
+    size_t route, ids, gates, blk_counts, blk_base, arrive, counts, offsets, perm_src, inv_perm,
+        x_perm, y, ffn, total;
 };
 LayoutL8 make_layout_l8(const Dims &D) {
     LayoutL8 L{};
@@ -396,6 +398,7 @@ LayoutL8 make_layout_l8(const Dims &D) {
     L.gates = take(Tk * sizeof(float));
     L.blk_counts = take((size_t)D.perm_blocks() * EL * sizeof(int32_t));
     L.blk_base = take((size_t)D.perm_blocks() * EL * sizeof(int32_t));
+    L.arrive = take(sizeof(int32_t));
     L.counts = take(EL * sizeof(int32_t));
     L.offsets = take((EL + 1) * sizeof(int32_t));
     L.perm_src = take(cap * sizeof(int32_t));
@@ -439,12 +442,15 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
     int32_t *offsets = at<int32_t>(ws, L.offsets), *inv_perm = at<int32_t>(ws, L.inv_perm);
     bf16_t *y = at<bf16_t>(ws, L.y);
     int32_t *perm_src = at<int32_t>(ws, L.perm_src);
-    bool hist_done = false;  // the router may also count the permute's histogram
+    // the router may also take over the permute's histogram and scan
+    const ScanArgs sa = make_scan_args(D, at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
+                                       at<int32_t>(ws, L.counts), offsets, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, 0, at<int32_t>(ws, L.arrive));
+    int prep = PREP_NONE;
     hipError_t e = mark_event(opts, 0, s);
     if (e == hipSuccess)
         e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates, nullptr,
-                         at<char>(ws, L.route), route_workspace_bytes(D), s,
-                         at<int32_t>(ws, L.blk_counts), &hist_done);
+                         at<char>(ws, L.route), route_workspace_bytes(D), s, &sa, &prep);
     if (e == hipSuccess) e = mark_event(opts, 1, s);
     // No x_perm: the FFN quantises each token's row of x once and places its
     // codes at every routed row of that token through perm_src.
@@ -452,7 +458,7 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets, perm_src,
                            inv_perm, nullptr, at<int32_t>(ws, L.blk_counts),
                            at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr, nullptr,
-                           nullptr, 0, s, hist_done);
+                           nullptr, 0, s, prep, sa.arrive);
     if (e == hipSuccess) e = mark_event(opts, 2, s);
     if (e == hipSuccess)
         e = run_ffn_fp8(D, (const bf16_t *)x, offsets, (const uint8_t *)wq_gate, s_gate,
@@ -609,19 +615,23 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
         D.dn_parts() > 1 ? (int64_t)((L.dn_cnt - L.status) / 4) + SPLIT_MAX
                     : (int64_t)((L.dn_flag - L.status) / 4) + D.max_mtiles() * D.nt_dn();
 
-    bool hist_done = false;  // the router may also count the permute's histogram
+    // the router may also take over the permute's histogram and scan
+    const ScanArgs sa = make_scan_args(D, at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
+                                       at<int32_t>(ws, L.counts), offsets, at<int32_t>(ws, L.pstart),
+                                       mt, nmt, mtile_base, at<int32_t>(ws, L.status), sched_ints,
+                                       at<int32_t>(ws, L.arrive));
+    int prep = PREP_NONE;
     hipError_t e = mark_event(opts, 0, s);
     if (e == hipSuccess)
         e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates, nullptr,
-                         at<char>(ws, L.route), route_workspace_bytes(D), s,
-                         at<int32_t>(ws, L.blk_counts), &hist_done);
+                         at<char>(ws, L.route), route_workspace_bytes(D), s, &sa, &prep);
     if (e == hipSuccess) e = mark_event(opts, 1, s);
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets,
                            at<int32_t>(ws, L.perm_src), inv_perm, gather ? nullptr : x_perm,
                            at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
                            at<int32_t>(ws, L.pstart), mt, nmt, mtile_base,
-                           at<int32_t>(ws, L.status), sched_ints, s, hist_done);
+                           at<int32_t>(ws, L.status), sched_ints, s, prep, sa.arrive);
     if (e == hipSuccess) e = mark_event(opts, 2, s);
     if (e == hipSuccess) {
         LayerArgs a;

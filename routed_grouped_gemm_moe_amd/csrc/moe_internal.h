@@ -139,7 +139,8 @@ struct Layout {
     size_t status, queues, gu_done, gu_xcd, dn_cg, dn_flag, dn_cnt, dn_part, order_tab, order_tmp,
         route, ids, gates,
         blk_counts,
-        blk_base, counts, offsets, pstart, perm_src, inv_perm, mtiles, n_mtiles, mtile_base, x_perm,
+        blk_base, arrive, counts, offsets, pstart, perm_src, inv_perm, mtiles, n_mtiles, mtile_base,
+        x_perm,
         h, y, total;
 };
 
@@ -153,19 +154,26 @@ __host__ __device__ inline T *at(void *ws, size_t off) {
 
 // ---------------------------------------------------------------- launches
 // All return hipSuccess or the launch error.
+struct ScanArgs;  // scan.h
+enum { PREP_NONE = 0, PREP_SCAN_DONE = 1, PREP_ARRIVE_CLEARED = 2 };
+
 // Router.  With logits != NULL, or without a large enough workspace when the
 // fast path applies, every logit is evaluated in the defined order; otherwise
 // E <= 16 uses the LDS-staged exact kernel and E > 16 the MFMA + exact-refine
-// fast path (same ids and gates).  With hist_done != NULL and the E <= 16
-// token-lane path taken, the router also writes the permute's histogram
-// (blk_counts, per token block of PERM_TB tokens and local expert) and sets
-// *hist_done; otherwise *hist_done is false and blk_counts is untouched.
+// fast path (same ids and gates).  With scan != NULL the router also takes
+// over part of the permute's dispatch scan and says how much in *prep:
+//  - PREP_SCAN_DONE (E <= 16 token-lane path): it counted the histogram
+//    (scan->blk_counts, per token block of PERM_TB tokens and local expert)
+//    and its last workgroup ran the whole scan;
+//  - PREP_ARRIVE_CLEARED (fast path): it set *scan->arrive to zero, so the
+//    permute's histogram kernel can run the scan in its last workgroup;
+//  - PREP_NONE: nothing (scan's buffers untouched).
 size_t route_workspace_bytes(const Dims &D);
 bool route_uses_fast_path(const Dims &D);
 int route_splits(const Dims &D);
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
-                        hipStream_t s, int32_t *blk_counts = nullptr, bool *hist_done = nullptr);
+                        hipStream_t s, const ScanArgs *scan = nullptr, int *prep = nullptr);
 
 // The fast router's approximate logits and their error bounds (E > 16 with a
 // workspace of route_workspace_bytes): approx, eps [T, E].
@@ -182,14 +190,14 @@ hipError_t launch_probe_mfma(int kind, int64_t n, int steps, const void *a, cons
 // pstart[] (not at all when x_perm is NULL: gather-on-load dispatch), and the
 // GEMM m-tile table is built and the scheduler state of the persistent kernel
 // cleared; otherwise x_perm is row-major at offsets[] (not written when
-// NULL: only the indices are produced).  hist_done: blk_counts
-// already holds the histogram (written by the router), so it is not recounted.
+// NULL: only the indices are produced).  prep: what the router already did
+// (launch_route); arrive: the arrival counter it cleared.
 hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, int32_t *counts,
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
                           int32_t *blk_counts, int32_t *blk_base, int32_t *pstart,
                           MTile *mtiles, int32_t *n_mtiles, int32_t *mtile_base,
                           int32_t *sched_state, int64_t sched_state_ints, hipStream_t s,
-                          bool hist_done = false);
+                          int prep = PREP_NONE, int32_t *arrive = nullptr);
 
 // Staged FFN: m-tile table and pstart[] from offsets[], then the row-major
 // x_perm repacked into xp (packed, pcap rows).

@@ -15,88 +15,47 @@
 // inside the segment is the same as in the row-major x_perm.  The same packed
 // gather repacks a caller's row-major x_perm for the staged FFN.
 #include "gemm_pa.h"
+#include "scan.h"
 
 namespace moe {
 namespace {
 
-// counts of local assignments per (token block, local expert)
+// counts of local assignments per (token block, local expert); with
+// scan.arrive set, the last workgroup to finish also runs the scan.
 __global__ __launch_bounds__(PERM_TB) void hist_kernel(int64_t T, int64_t k, int64_t e_lo,
                                                        int64_t EL, const int32_t *__restrict__ ids,
-                                                       int32_t *__restrict__ blk_counts) {
-    extern __shared__ int32_t s_cnt[];  // [EL]
+                                                       int32_t *__restrict__ blk_counts,
+                                                       ScanArgs scan) {
+    extern __shared__ int32_t s_cnt[];  // [EL], then the scan's LDS
     for (int64_t e = threadIdx.x; e < EL; e += PERM_TB) s_cnt[e] = 0;
     __syncthreads();
     const int64_t t = (int64_t)blockIdx.x * PERM_TB + threadIdx.x;
     if (t < T)
-        for (int64_t j = 0; j < k; ++j) {
-            int64_t e = (int64_t)ids[t * k + j] - e_lo;
-            if (e >= 0 && e < EL) atomicAdd(&s_cnt[e], 1);
-        }
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e < EL; e += PERM_TB) blk_counts[blockIdx.x * EL + e] = s_cnt[e];
-}
-
-// One workgroup: per-expert running sums over token blocks, counts, offsets,
-// optionally the GEMM m-tile table and a cleared scheduler state.
-constexpr int SCAN_THREADS = 1024;
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
-    int64_t EL, int64_t nblk, const int32_t *__restrict__ blk_counts, int32_t *__restrict__ blk_base,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ pstart,
-    MTile *__restrict__ mtiles, int32_t *__restrict__ n_mtiles, int32_t *__restrict__ mtile_base,
-    int32_t *__restrict__ sched, int64_t sched_ints) {
-    extern __shared__ int32_t s_tmp[];  // [3*EL + 3]
-    int32_t *s_cnt = s_tmp;
-    int32_t *s_mt = s_tmp + EL + 1;
-    int32_t *s_ps = s_tmp + 2 * EL + 2;
-    for (int64_t e = threadIdx.x; e < EL; e += SCAN_THREADS) {
-        int32_t run = 0;
-        for (int64_t b = 0; b < nblk; ++b) {
-            int32_t c = blk_counts[b * EL + e];
-            blk_base[b * EL + e] = run;
-            run += c;
-        }
-        s_cnt[e] = run;
-        counts[e] = run;
-        s_mt[e] = (run + BM - 1) / BM;
-        s_ps[e] = (run + 31) & ~31;
-    }
-    for (int64_t i = threadIdx.x; i < sched_ints; i += SCAN_THREADS) sched[i] = 0;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        // exclusive scans over at most 1024 experts
-        int32_t off = 0, mt = 0, ps = 0;
-        for (int64_t e = 0; e < EL; ++e) {
-            int32_t c = s_cnt[e], m = s_mt[e], p = s_ps[e];
-            s_cnt[e] = off;
-            s_mt[e] = mt;
-            s_ps[e] = ps;
-            off += c;
-            mt += m;
-            ps += p;
-        }
-        s_cnt[EL] = off;
-        s_mt[EL] = mt;
-        s_ps[EL] = ps;
-    }
-    __syncthreads();
-    for (int64_t e = threadIdx.x; e <= EL; e += SCAN_THREADS) offsets[e] = s_cnt[e];
-    if (pstart) {
-        for (int64_t e = threadIdx.x; e <= EL; e += SCAN_THREADS) pstart[e] = s_ps[e];
-        if (threadIdx.x == 0) *n_mtiles = s_mt[EL];
-        for (int64_t e = threadIdx.x; e < EL; e += SCAN_THREADS) {
-            int32_t base = s_mt[e], n = s_mt[e + 1] - base;
-            int32_t row0 = s_cnt[e], cnt = s_cnt[e + 1] - row0;
-            mtile_base[e] = base;
-            for (int32_t m = 0; m < n; ++m) {
-                MTile t;
-                t.e = (int32_t)e;
-                t.row0 = row0 + m * BM;
-                t.rows = min(BM, cnt - m * BM);
-                t.prow0 = s_ps[e] + m * BM;
-                mtiles[base + m] = t;
+        for (int64_t j0 = 0; j0 < k; j0 += 8) {  // 8 ids in flight at a time
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t e = (int64_t)v[u] - e_lo;
+                if (j0 + u < k && e >= 0 && e < EL) atomicAdd(&s_cnt[e], 1);
             }
         }
-    }
+    __syncthreads();
+    // device-scope stores: the last workgroup of the folded scan reads them
+    for (int64_t e = threadIdx.x; e < EL; e += PERM_TB)
+        __hip_atomic_store(blk_counts + blockIdx.x * EL + e, s_cnt[e], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (!scan.arrive) return;
+    __shared__ int32_t s_last;
+    if (scan_arrive_last(scan.arrive, gridDim.x, &s_last)) scan_block<PERM_TB>(scan, s_cnt);
+}
+
+// The scan as a kernel of its own (one workgroup).
+constexpr int SCAN_THREADS = 1024;
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs scan) {
+    extern __shared__ int32_t s_scan[];
+    scan_block<SCAN_THREADS>(scan, s_scan);
 }
 
 // Stable rank of each (token, slot) inside its token block via per-expert
@@ -108,29 +67,49 @@ __global__ __launch_bounds__(PERM_TB) void rank_kernel(int64_t T, int64_t k, int
                                                        int32_t *__restrict__ perm_src,
                                                        int32_t *__restrict__ inv_perm) {
     constexpr int WORDS = PERM_TB / 32;
-    extern __shared__ uint32_t s_bits[];  // [EL][WORDS]
+    extern __shared__ uint32_t s_bits[];  // [EL][WORDS], then the block's segment bases [EL]
+    int32_t *s_base = reinterpret_cast<int32_t *>(s_bits + EL * WORDS);
     for (int64_t i = threadIdx.x; i < EL * WORDS; i += PERM_TB) s_bits[i] = 0;
+    for (int64_t e = threadIdx.x; e < EL; e += PERM_TB)
+        s_base[e] = offsets[e] + blk_base[blockIdx.x * EL + e];
     __syncthreads();
     const int tl = threadIdx.x;
     const int64_t t = (int64_t)blockIdx.x * PERM_TB + tl;
+    // ids 8 at a time, loaded before they are used
+    auto load8 = [&](int32_t (&v)[8], int64_t j0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = j0 + u < k ? ids[t * k + j0 + u] : -1;
+    };
     if (t < T)
-        for (int64_t j = 0; j < k; ++j) {
-            int64_t e = (int64_t)ids[t * k + j] - e_lo;
-            if (e >= 0 && e < EL) atomicOr(&s_bits[e * WORDS + (tl >> 5)], 1u << (tl & 31));
+        for (int64_t j0 = 0; j0 < k; j0 += 8) {
+            int32_t v[8];
+            load8(v, j0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t e = (int64_t)v[u] - e_lo;
+                if (j0 + u < k && e >= 0 && e < EL)
+                    atomicOr(&s_bits[e * WORDS + (tl >> 5)], 1u << (tl & 31));
+            }
         }
     __syncthreads();
     if (t < T)
-        for (int64_t j = 0; j < k; ++j) {
-            int64_t e = (int64_t)ids[t * k + j] - e_lo;
-            if (e >= 0 && e < EL) {
-                const uint32_t *b = s_bits + e * WORDS;
-                int32_t r = __popc(b[tl >> 5] & ((1u << (tl & 31)) - 1u));
-                for (int w = 0; w < (tl >> 5); ++w) r += __popc(b[w]);
-                int32_t pos = offsets[e] + blk_base[blockIdx.x * EL + e] + r;
-                perm_src[pos] = (int32_t)t;
-                inv_perm[t * k + j] = pos;
-            } else {
-                inv_perm[t * k + j] = -1;
+        for (int64_t j0 = 0; j0 < k; j0 += 8) {
+            int32_t v[8];
+            load8(v, j0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u >= k) break;
+                const int64_t e = (int64_t)v[u] - e_lo;
+                if (e >= 0 && e < EL) {
+                    const uint32_t *b = s_bits + e * WORDS;
+                    int32_t r = __popc(b[tl >> 5] & ((1u << (tl & 31)) - 1u));
+                    for (int w = 0; w < (tl >> 5); ++w) r += __popc(b[w]);
+                    const int32_t pos = s_base[e] + r;
+                    perm_src[pos] = (int32_t)t;
+                    inv_perm[t * k + j0 + u] = pos;
+                } else {
+                    inv_perm[t * k + j0 + u] = -1;
+                }
             }
         }
 }
@@ -234,21 +213,30 @@ hipError_t launch_permute(const Dims &D, const bf16_t *x, const int32_t *ids, in
                           int32_t *offsets, int32_t *perm_src, int32_t *inv_perm, bf16_t *x_perm,
                           int32_t *blk_counts, int32_t *blk_base, int32_t *pstart, MTile *mtiles,
                           int32_t *n_mtiles, int32_t *mtile_base, int32_t *sched_state,
-                          int64_t sched_state_ints, hipStream_t s, bool hist_done) {
+                          int64_t sched_state_ints, hipStream_t s, int prep, int32_t *arrive) {
     const int64_t EL = D.EL(), nblk = D.perm_blocks();
+    ScanArgs sa = make_scan_args(D, blk_counts, blk_base, counts, offsets, pstart, mtiles, n_mtiles,
+                                 mtile_base, sched_state, sched_state_ints, nullptr);
+    const size_t scan_lds = (size_t)scan_lds_ints(EL) * sizeof(int32_t);
     hipError_t e;
-    if (nblk > 0 && !hist_done) {
-        hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblk), dim3(PERM_TB), EL * sizeof(int32_t),
-                           s, D.T, D.k, D.e_lo, EL, ids, blk_counts);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (prep != PREP_SCAN_DONE) {
+        if (nblk > 0) {
+            // with the arrival counter cleared by the router, the last
+            // histogram workgroup runs the scan
+            if (prep == PREP_ARRIVE_CLEARED) sa.arrive = arrive;
+            const size_t lds = sa.arrive ? scan_lds : EL * sizeof(int32_t);
+            hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblk), dim3(PERM_TB), lds, s, D.T, D.k,
+                               D.e_lo, EL, ids, blk_counts, sa);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (!sa.arrive) {
+            hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), scan_lds, s, sa);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), (3 * EL + 3) * sizeof(int32_t), s,
-                       EL, nblk, blk_counts, blk_base, counts, offsets, pstart, mtiles, n_mtiles,
-                       mtile_base, sched_state, sched_state ? sched_state_ints : 0);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nblk > 0) {
         hipLaunchKernelGGL(rank_kernel, dim3((unsigned)nblk), dim3(PERM_TB),
-                           EL * (PERM_TB / 32) * sizeof(uint32_t), s, D.T, D.k, D.e_lo, EL, ids,
+                           EL * (PERM_TB / 32 + 1) * sizeof(uint32_t), s, D.T, D.k, D.e_lo, EL, ids,
                            offsets, blk_base, perm_src, inv_perm);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (pstart) {

@@ -11,13 +11,17 @@
 // (logit desc, id asc); gates are the float32 softmax over the selected
 // logits.
 //
-// Three implementations of that one definition:
+// Implementations of that one definition:
 //  - route_exact_kernel: every logit in the defined order (also the optional
 //    logits output).  Used for the logits output and when no workspace is given.
-//  - route_tok_* (E <= 16, with a workspace): lane = token, wave = chunk, the
-//    router weights (widened to float32 once) wave-uniform: scalar loads and
-//    operands; chunk sums go through the workspace to a kernel that folds
-//    and selects.
+//  - route_tok_* (E <= 16, with a workspace): lane = token, wave = chunk;
+//    chunk sums go through the workspace to a kernel that folds and selects
+//    (and, inside moe_layer, counts the dispatch histogram and runs the
+//    dispatch scan in its last workgroup).  When d is a multiple of 1024 the
+//    activations and weights are staged through LDS by DMA loads and each
+//    weight reaches its multiply-adds by a DPP row broadcast
+//    (route_tok_lds_kernel); otherwise the weights are wave-uniform scalar
+//    loads (route_tok_chunks_kernel).
 //  - route_small_kernel (E <= 16, no workspace): the same order with W_r
 //    staged in LDS and the activations prefetched.
 //  - fast path (E > 16, with a workspace): bf16 MFMA logits (split-K float32
@@ -32,6 +36,7 @@
 #include <type_traits>
 
 #include "gemm_tile.h"
+#include "scan.h"
 
 namespace moe {
 namespace {
@@ -331,13 +336,17 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
                                                                const bf16_t *__restrict__ w,
                                                                float *__restrict__ part,
                                                                int32_t *__restrict__ hist,
-                                                               int64_t hist_n) {
+                                                               int64_t hist_n,
+                                                               int32_t *__restrict__ arrive) {
     constexpr int NG = EP / RT_EG;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // the permute's histogram, filled by the finish kernel, starts at zero
-    if (hist && blockIdx.x == 0)
+    // the permute's histogram, filled by the finish kernel, and the finish
+    // kernel's arrival counter start at zero
+    if (hist && blockIdx.x == 0) {
         for (int64_t i = threadIdx.x; i < hist_n; i += 256) hist[i] = 0;
+        if (arrive && threadIdx.x == 0) *arrive = 0;
+    }
     const int64_t rest = blockIdx.x / 8;
     const int64_t unit = (rest / NG) * 8 + blockIdx.x % 8;
     if (unit >= route_tok_units(T)) return;
@@ -402,6 +411,188 @@ __global__ __launch_bounds__(256) void route_tok_chunks_kernel(int64_t T, int64_
         if (e0 + e < E) pp[e * RTOK] = acc[e];
 }
 
+// Chunk sums with the activations and router weights staged through LDS
+// (d a multiple of 1024).  The kernel above reads each lane's own row, so one
+// load instruction touches 64 cache lines for 16 bytes of each, and widens
+// every weight on the scalar unit between scalar loads whose latency it
+// cannot hide.  Here:
+//  - workgroup = 64 tokens x chunk quad q x NG groups of EG = 4 experts,
+//    4*NG waves (two per SIMD for E <= 8); wave (j, g): chunk 4q + j,
+//    experts EG*g .. EG*g + EG - 1;
+//  - a step covers elements 64s .. 64s + 63 of every chunk.  Its activations
+//    (one 128-byte line per token and chunk, 32 KiB) and weights (one line
+//    per chunk and expert) come in by coalesced DMA loads (global -> LDS, no
+//    registers) into one slot of a ring; all of d = 4096 is in flight at once;
+//  - activation slot layout [chunk j][token t][16-byte piece], piece u of
+//    token t at position u ^ ((t >> 1) & 7), so the 16 lanes of one LDS bank
+//    sweep hit distinct banks; weights [chunk j][expert][128 bytes];
+//  - lane = token; the weights are read 16 to a register (lane n of each
+//    16-lane row holds element 2n or 2n + 1 of a 32-element half) and each
+//    multiply-add takes its weight by a DPP row broadcast of lane n, so the
+//    weight costs neither a scalar load nor a widening per use.
+// Every sum is the same chain of float32 fmas, in the same order, as in the
+// kernels above.
+template <int EP, int EG>
+struct RtlGeom {
+    static constexpr int NG = EP / EG;                       // expert groups of EG
+    static constexpr int WAVES = 4 * NG;
+    static constexpr int X_BYTES = 4 * RTOK * 128;           // 32 KiB
+    static constexpr int W_BYTES = WAVES * 1024;             // one weight DMA per wave
+    static constexpr int SLOT = X_BYTES + W_BYTES;
+    static constexpr int SLOTS = SLOT <= 36 * 1024 ? 4 : 3;  // ring depth (LDS <= 144 KiB)
+    static constexpr int DPW = 32 / WAVES;                   // activation DMAs per wave and step
+};
+
+constexpr int RTL_EG = 4;  // experts per wave (measured: 4 beats 2 and 8)
+
+__host__ __device__ constexpr bool route_tok_lds_ok(int64_t d) {
+    return d % 1024 == 0 && d >= 1024;
+}
+template <int EP, int EG>
+__host__ constexpr size_t route_tok_lds_bytes(int64_t d) {
+    using G = RtlGeom<EP, EG>;
+    return (size_t)(d / 1024 < G::SLOTS ? d / 1024 : G::SLOTS) * G::SLOT;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// acc = fma(w of lane n of this lane's 16-lane row, x, acc): one v_fmac_f32
+// whose first operand is a DPP row broadcast (gfx950 row_newbcast).
+#define RTL_FB(N)                                                                          \
+    case N:                                                                                \
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"     \
+            : "+v"(acc)                                                                    \
+            : "v"(w), "v"(x));                                                             \
+        break;
+__device__ __forceinline__ void fma_row_bcast(float &acc, float w, float x, int n) {
+    switch (n) {
+        RTL_FB(0) RTL_FB(1) RTL_FB(2) RTL_FB(3) RTL_FB(4) RTL_FB(5) RTL_FB(6) RTL_FB(7)
+        RTL_FB(8) RTL_FB(9) RTL_FB(10) RTL_FB(11) RTL_FB(12) RTL_FB(13) RTL_FB(14) RTL_FB(15)
+    }
+}
+#undef RTL_FB
+// The two bf16 of a 32-bit word widened to float32 (exact).  A DPP operand
+// written by a VALU instruction needs two wait states before it is read; the
+// s_nop inside the same statement provides them whatever the compiler places
+// after it.
+__device__ __forceinline__ void widen_pair(uint32_t raw, float &lo, float &hi) {
+    asm("v_lshlrev_b32 %0, 16, %2\n\tv_and_b32 %1, 0xffff0000, %2\n\ts_nop 1"
+        : "=&v"(lo), "=&v"(hi)
+        : "v"(raw));
+}
+
+template <int EP, int EG>
+__global__ __launch_bounds__(64 * (RtlGeom<EP, EG>::WAVES)) void route_tok_lds_kernel(
+    int64_t T, int64_t d, int64_t E, const bf16_t *__restrict__ x, const bf16_t *__restrict__ w,
+    float *__restrict__ part, int32_t *__restrict__ hist, int64_t hist_n,
+    int32_t *__restrict__ arrive) {
+    using G = RtlGeom<EP, EG>;
+    constexpr int NTH = 64 * G::WAVES;
+    constexpr int DPW = G::DPW;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (hist && blockIdx.x == 0) {  // the finish kernel's histogram and arrival counter
+        for (int64_t i = threadIdx.x; i < hist_n; i += NTH) hist[i] = 0;
+        if (arrive && threadIdx.x == 0) *arrive = 0;
+    }
+    const int64_t blk = blockIdx.x / 4;
+    const int q = (int)(blockIdx.x % 4);
+    const int j = wave & 3;           // chunk of this wave inside the quad
+    const int e0 = (wave >> 2) * EG;  // first expert of this wave
+    const int c = 4 * q + j;
+    const int64_t dc = d / 16;
+    const int NS = (int)(dc / 64);    // steps
+    const int NSL = NS < G::SLOTS ? NS : G::SLOTS;
+
+    // activation rows of this token block (rows past T read as zeros) and W_r
+    const int64_t rows = T - blk * RTOK < RTOK ? T - blk * RTOK : RTOK;
+    i32x4_t rx = make_rsrc(x + blk * RTOK * d, (uint32_t)(rows * d * 2));
+    i32x4_t rw = make_rsrc(w, (uint32_t)(E * d * 2));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        rx[v] = __builtin_amdgcn_readfirstlane(rx[v]);
+        rw[v] = __builtin_amdgcn_readfirstlane(rw[v]);
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    // activation DMA i = wave * DPW + r of a step: chunk i / 8, tokens
+    // 8 (i % 8) .. + 7; lane L fetches piece (L & 7) ^ ((t >> 1) & 7) of token
+    // t = 8 (i % 8) + L / 8 into LDS position L.  Weight DMA of wave m: (chunk,
+    // expert) pairs 8m .. 8m + 7 (pair = chunk * EP + expert), lane L piece
+    // L & 7 of pair 8m + L / 8; experts past E re-read row E - 1.
+    uint32_t voff[DPW];
+#pragma unroll
+    for (int r = 0; r < DPW; ++r) {
+        const int i = wave * DPW + r;
+        const int t = 8 * (i % 8) + (lane >> 3);
+        const int p = (lane & 7) ^ ((t >> 1) & 7);
+        voff[r] = (uint32_t)(t * d * 2 + (4 * q + i / 8) * dc * 2 + p * 16);
+    }
+    // (pairs past 4 * EP, when there are more waves than weight lines, load a
+    // second copy that nobody reads)
+    const int wpair = (8 * wave + (lane >> 3)) % (4 * EP);
+    const int we = wpair % EP < E ? wpair % EP : (int)E - 1;
+    const uint32_t woff = (uint32_t)(we * d * 2 + (4 * q + wpair / EP) * dc * 2 + (lane & 7) * 16);
+    auto issue = [&](int s) {
+        const uint32_t sb = lds_base + (s % G::SLOTS) * G::SLOT;
+#pragma unroll
+        for (int r = 0; r < DPW; ++r) {
+            const uint32_t m = __builtin_amdgcn_readfirstlane(sb + (wave * DPW + r) * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(m), "v"(voff[r] + (uint32_t)s * 128u), "s"(rx) : "memory", "m0");
+        }
+        const uint32_t m = __builtin_amdgcn_readfirstlane(sb + G::X_BYTES + wave * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m), "v"(woff + (uint32_t)s * 128u), "s"(rw) : "memory", "m0");
+    };
+    for (int s = 0; s < NSL; ++s) issue(s);
+
+    float acc[EG];
+#pragma unroll
+    for (int e = 0; e < EG; ++e) acc[e] = 0.0f;
+    const int sw = (lane >> 1) & 7;
+    const int n16 = lane & 15;
+    for (int s = 0; s < NS; ++s) {
+        // DMA steps issued after step s: min(NS - 1, s + NSL - 1) - s
+        const int later = (s + NSL - 1 < NS - 1 ? s + NSL - 1 : NS - 1) - s;
+        if (later >= 3) wait_vmcnt<3 * (DPW + 1)>();
+        else if (later == 2) wait_vmcnt<2 * (DPW + 1)>();
+        else if (later == 1) wait_vmcnt<DPW + 1>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's DMA of step s has landed
+        const char *slot = lds + (s % G::SLOTS) * G::SLOT;
+        const char *xrow = slot + (j * RTOK + lane) * 128;
+        const uint32_t *wrow =
+            reinterpret_cast<const uint32_t *>(slot + G::X_BYTES + (j * EP + e0) * 128) + n16;
+        for (int h = 0; h < 2; ++h) {  // the two 32-element halves of the step
+            float lo[EG], hi[EG];  // lane n: elements 32h + 2n, 32h + 2n + 1 of each expert
+#pragma unroll
+            for (int e = 0; e < EG; ++e) widen_pair(wrow[e * 32 + h * 16], lo[e], hi[e]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4_t xv =
+                    *reinterpret_cast<const u32x4_t *>(xrow + (((4 * h + u) ^ sw) << 4));
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const float xf = bf16x8_elem(xv, qq);
+#pragma unroll
+                    for (int e = 0; e < EG; ++e)
+                        fma_row_bcast(acc[e], (qq & 1) ? hi[e] : lo[e], xf, 4 * u + (qq >> 1));
+                }
+            }
+        }
+        if (s + NSL < NS) {
+            __syncthreads();  // every wave is done with slot s % SLOTS
+            issue(s + NSL);
+        }
+    }
+    float *pp = part + ((blk * 16 + c) * EP + e0) * RTOK + lane;
+#pragma unroll
+    for (int e = 0; e < EG; ++e)
+        if (e0 + e < E) pp[e * RTOK] = acc[e];
+}
+#pragma clang diagnostic pop
+
 template <int EP>
 __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_t E, int64_t k,
                                                                const float *__restrict__ part,
@@ -409,7 +600,8 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
                                                                int32_t *__restrict__ ids,
                                                                float *__restrict__ gates,
                                                                int64_t e_lo, int64_t EL,
-                                                               int32_t *__restrict__ hist) {
+                                                               int32_t *__restrict__ hist,
+                                                               ScanArgs scan) {
     __shared__ float s_l[EP][RTOK];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -430,7 +622,7 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
     }
     __syncthreads();
     const int64_t t = blk * RTOK + lane;
-    if (wave != 0) return;
+    auto select = [&]() {  // wave 0: one lane per token
     const bool valid = t < T;  // lanes past T select on clamped rows, store nothing
     float l[EP];
 #pragma unroll
@@ -489,6 +681,14 @@ __global__ __launch_bounds__(256) void route_tok_finish_kernel(int64_t T, int64_
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < EL && s_h[lane]) atomicAdd(&hist[(blk * RTOK / PERM_TB) * EL + lane], s_h[lane]);
+    };
+    if (wave == 0) select();
+    // the permute's dispatch scan, by the last workgroup to finish counting
+    if (hist && scan.arrive) {
+        __shared__ int32_t s_last;
+        __shared__ int32_t s_scan[scan_lds_ints(16)];  // EL <= E <= 16
+        if (scan_arrive_last(scan.arrive, gridDim.x, &s_last)) scan_block<256>(scan, s_scan);
+    }
 }
 
 // ------------------------------------------------------------ fast path
@@ -504,9 +704,12 @@ __device__ __forceinline__ float norm_inflation(int64_t d) {
 // ||w_e|| (float32, rounded up by a relative 2^-10 to cover its own rounding).
 __global__ __launch_bounds__(256) void route_wprep_kernel(int64_t d, const bf16_t *__restrict__ w,
                                                           bf16_t *__restrict__ wt,
-                                                          float *__restrict__ wnorm) {
+                                                          float *__restrict__ wnorm,
+                                                          int32_t *__restrict__ arrive) {
     __shared__ float s_red[256];
     const int64_t e = blockIdx.x;
+    // the permute's histogram kernel counts its arrivals from zero
+    if (arrive && e == 0 && threadIdx.x == 0) *arrive = 0;
     const int64_t ppr = d / 8, ppc = d / 16 / 8;
     float ss = 0.0f;
     for (int64_t p = threadIdx.x; p < ppr; p += 256) {
@@ -794,16 +997,34 @@ size_t route_workspace_bytes(const Dims &D) {
 
 template <int EP>
 static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, const float *bias,
-                               int32_t *ids, float *gates, void *ws, int32_t *hist, hipStream_t s) {
+                               int32_t *ids, float *gates, void *ws, const ScanArgs *scan,
+                               hipStream_t s) {
     const unsigned nblk = (unsigned)((D.T + RTOK - 1) / RTOK);
+    int32_t *hist = scan ? scan->blk_counts : nullptr;
+    int32_t *arrive = scan ? scan->arrive : nullptr;
     float *part = reinterpret_cast<float *>(ws);
-    hipLaunchKernelGGL((route_tok_chunks_kernel<EP>), dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)),
-                       dim3(256), 0, s, D.T, D.d, D.E, x, w, part, hist,
-                       D.perm_blocks() * D.EL());
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (route_tok_lds_ok(D.d)) {
+        constexpr int EG = RTL_EG;
+        const size_t lds = route_tok_lds_bytes<EP, EG>(D.d);
+        e = hipFuncSetAttribute((const void *)route_tok_lds_kernel<EP, EG>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((route_tok_lds_kernel<EP, EG>), dim3(nblk * 4),
+                           dim3(64 * RtlGeom<EP, EG>::WAVES),
+                           lds, s, D.T, D.d, D.E, x, w, part, hist, D.perm_blocks() * D.EL(),
+                           arrive);
+    } else {
+        hipLaunchKernelGGL((route_tok_chunks_kernel<EP>),
+                           dim3((unsigned)route_tok_grid(D.T, EP / RT_EG)), dim3(256), 0, s, D.T,
+                           D.d, D.E, x, w, part, hist, D.perm_blocks() * D.EL(), arrive);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
+    ScanArgs sa{};
+    if (scan) sa = *scan;
     hipLaunchKernelGGL((route_tok_finish_kernel<EP>), dim3(nblk), dim3(256), 0, s, D.T, D.E, D.k,
-                       part, bias, ids, gates, D.e_lo, D.EL(), hist);
+                       part, bias, ids, gates, D.e_lo, D.EL(), hist, sa);
     return hipGetLastError();
 }
 
@@ -813,7 +1034,8 @@ static hipError_t launch_tok_t(const Dims &D, const bf16_t *x, const bf16_t *w, 
 // bounds, written out (moe_route_bounds).
 static hipError_t launch_route_fast(const Dims &D, const bf16_t *x, const bf16_t *w_router,
                                     const float *bias, int32_t *ids, float *gates, void *ws,
-                                    hipStream_t s, float *approx, float *eps) {
+                                    hipStream_t s, float *approx, float *eps,
+                                    int32_t *arrive = nullptr) {
     auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const int S = route_splits(D);
     float *part = reinterpret_cast<float *>(ws);
@@ -821,7 +1043,7 @@ static hipError_t launch_route_fast(const Dims &D, const bf16_t *x, const bf16_t
                                             al((size_t)S * D.T * D.E * 4));
     float *wnorm = reinterpret_cast<float *>(reinterpret_cast<char *>(wt) + al((size_t)D.E * D.d * 2));
     hipLaunchKernelGGL(route_wprep_kernel, dim3((unsigned)D.E), dim3(256), 0, s, D.d, w_router, wt,
-                       wnorm);
+                       wnorm, arrive);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void *)route_gemm_kernel,
@@ -868,8 +1090,9 @@ hipError_t launch_route_bounds(const Dims &D, const bf16_t *x, const bf16_t *w_r
 
 hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, const float *bias,
                         int32_t *ids, float *gates, float *logits, void *ws, size_t ws_bytes,
-                        hipStream_t s, int32_t *blk_counts, bool *hist_done) {
-    if (hist_done) *hist_done = false;
+                        hipStream_t s, const ScanArgs *scan, int *prep) {
+    if (prep) *prep = PREP_NONE;
+    if (!prep || (scan && !scan->arrive)) scan = nullptr;
     if (D.T == 0) return hipSuccess;
     if (logits || (route_uses_fast_path(D) && (!ws || ws_bytes < route_workspace_bytes(D)))) {
         // every logit in the defined order
@@ -878,10 +1101,9 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
         return launch_exact_t<4, 8>(D, x, w_router, bias, ids, gates, logits, s);
     }
     if (D.E <= 16 && ws && ws_bytes >= route_workspace_bytes(D)) {
-        int32_t *hist = hist_done ? blk_counts : nullptr;
-        if (hist) *hist_done = true;
-        if (D.E <= 8) return launch_tok_t<8>(D, x, w_router, bias, ids, gates, ws, hist, s);
-        return launch_tok_t<16>(D, x, w_router, bias, ids, gates, ws, hist, s);
+        if (scan) *prep = PREP_SCAN_DONE;
+        if (D.E <= 8) return launch_tok_t<8>(D, x, w_router, bias, ids, gates, ws, scan, s);
+        return launch_tok_t<16>(D, x, w_router, bias, ids, gates, ws, scan, s);
     }
     if (!route_uses_fast_path(D)) {
         const size_t lds = (size_t)(D.E * stag_pitch(D.d) + RT_TOK * D.E * sizeof(float));
@@ -892,7 +1114,9 @@ hipError_t launch_route(const Dims &D, const bf16_t *x, const bf16_t *w_router, 
         if (D.E <= 8) return launch_small_t<8>(D, x, w_router, bias, ids, gates, s);
         return launch_small_t<16>(D, x, w_router, bias, ids, gates, s);
     }
-    return launch_route_fast(D, x, w_router, bias, ids, gates, ws, s, nullptr, nullptr);
+    if (scan && scan->arrive) *prep = PREP_ARRIVE_CLEARED;
+    return launch_route_fast(D, x, w_router, bias, ids, gates, ws, s, nullptr, nullptr,
+                             scan ? scan->arrive : nullptr);
 }
 
 }  // namespace moe

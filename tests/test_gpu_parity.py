@@ -352,6 +352,35 @@ def test_router_fast_path_on_constructed_ties(pattern):
         assert np.array_equal(r_ids[0], np.arange(cfg.k))
 
 
+# The E <= 16 router stages the activations through LDS when d is a multiple
+# of 1024 (up to four 32 KiB steps in flight, a ring beyond that): step
+# counts 1, 2, 3, 5 and 8, ragged and single-token blocks, E below 8 and
+# between 9 and 16; every stage, and the layer, whose router also counts the
+# permute's histogram.
+LDS_ROUTER = {
+    "d1024_e8": dict(T=1000, d=1024, E=8, k=2),
+    "d2048_e16": dict(T=333, d=2048, E=16, k=4),
+    "d3072_e5": dict(T=130, d=3072, E=5, k=2),
+    "d5120_e12": dict(T=200, d=5120, E=12, k=3),
+    "d8192_e8": dict(T=64, d=8192, E=8, k=1),
+    "d4096_t65": dict(T=65, d=4096, E=8, k=2),
+    "d1024_one_token": dict(T=1, d=1024, E=2, k=1),
+}
+
+
+@pytest.mark.parametrize("name", list(LDS_ROUTER))
+def test_router_lds_staged_shapes(name):
+    cfg = W.CONFIGS["tiny"].scaled(name=name, f=128, seed=40 + list(LDS_ROUTER).index(name),
+                                   **LDS_ROUTER[name])
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    offsets, inv, xp, ro, rp, ri, N = _check_permute(cfg, t, arrs, ids, r_ids)
+    y = _check_ffn(cfg, t, arrs, xp, offsets, ro, rp, N)
+    staged = _staged(cfg, t, y, inv, gates)
+    _check_layer(cfg, t, arrs, staged_out=staged)
+
+
 @pytest.mark.parametrize("f,parts", [(8448, 2), (8192, 4)])
 def test_cut_down_tiles(f, parts):
     # Deep down GEMMs (f >= 8192) cut the down tiles of the schedule's last
