@@ -22,6 +22,7 @@ Other modes:
                      and WRITE_SIZE counters of rocprofv3 to bytes)
   --mode ffn_fp8 / ffn_bf16 / layer_fp8
                      the staged W8A8 or bf16 expert FFN alone, or the W8A8 layer
+                     (persistent kernel, and its staged schedule for comparison)
   --summarize-trace DIR
                      per-kernel medians of the timed dispatches in the
                      rocprofv3 kernel trace (csv) under DIR, skipping the
@@ -306,27 +307,45 @@ def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
     }), flush=True)
 
 
-def w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt):
+def w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt, n_local=None):
     """The same workload through moe_layer_fp8 (weights quantised once,
-    outside the timed steps)."""
+    outside the timed steps): its persistent kernel (the default) and, for
+    comparison, its staged schedule.  fp8_tflops: Weave §3.1's 6*H*I per
+    routed row over the median of the launches after the permute (the x
+    quantisation and the persistent kernel), against the 5 PF dense fp8 peak."""
     (gq, gs), (uq, us), (dq, ds) = (M.moe_quantize_fp8(w) for w in (wg, wu, wd))
     ws8 = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
-    step8 = lambda o=None: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
-                                           out_dtype=dt, ws=ws8, opts=o)
-    for _ in range(args.warmup):
-        step8()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    opts = [M.layer_opts(events=e) for e in evs]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for o in opts:
-        step8(o)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    return {"value": round(cfg.T * args.steps / el, 1), "unit": "tokens/s",
-            "ms_per_step": round(el / args.steps * 1e3, 4),
-            "ms_per_step_median": round(median([e[0].elapsed_time(e[3]) for e in evs]), 4),
-            "dtype": "fp8_e4m3", "entry_point": "moe_layer_fp8 (staged)"}
+
+    def run(schedule):
+        step8 = lambda o: M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out=out,
+                                          out_dtype=dt, ws=ws8, opts=o)
+        plain = M.layer_opts(schedule=schedule)
+        for _ in range(args.warmup):
+            step8(plain)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        opts = [M.layer_opts(events=e, schedule=schedule) for e in evs]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for o in opts:
+            step8(o)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        ffn_us = median([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+        return el, median([e[0].elapsed_time(e[3]) for e in evs]), ffn_us
+
+    el, med, ffn_us = run(M.MOE_SCHEDULE_PERSISTENT)
+    el_s, med_s, ffn_us_s = run(M.MOE_SCHEDULE_STAGED)
+    rec = {"value": round(cfg.T * args.steps / el, 1), "unit": "tokens/s",
+           "ms_per_step": round(el / args.steps * 1e3, 4), "ms_per_step_median": round(med, 4),
+           "dtype": "fp8_e4m3", "entry_point": "moe_layer_fp8 (persistent kernel)",
+           "ffn_combine_median_us": round(ffn_us, 2),
+           "staged_schedule": {"value": round(cfg.T * args.steps / el_s, 1),
+                               "ms_per_step_median": round(med_s, 4),
+                               "ffn_combine_median_us": round(ffn_us_s, 2)}}
+    if n_local:
+        tf = 6.0 * cfg.d * cfg.f * n_local / (ffn_us * 1e-6) / 1e12
+        rec.update({"fp8_tflops": round(tf, 2), "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)})
+    return rec
 
 
 def main() -> None:
@@ -392,7 +411,9 @@ def main() -> None:
     out = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_fp32 else torch.bfloat16,
                       device="cuda")
     if args.mode == "layer_fp8":
-        rec = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt)
+        ids8 = M.moe_route(D, x, wr, bias)[0].cpu().numpy()
+        n8 = int(((ids8 >= cfg.e_lo) & (ids8 < cfg.E_hi)).sum())
+        rec = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt, n_local=n8)
         rec.update({"mode": "layer_fp8",
                     "metric": "MoE-layer tokens/s with the W8A8 (E4M3) expert FFN, 1 GPU",
                     "steps": args.steps, "warmup": args.warmup,
@@ -497,7 +518,8 @@ def main() -> None:
                                                   t_local)
     if not args.no_w8a8 and cfg.f % 256 == 0:
         print("[bench] W8A8 layer", file=sys.stderr, flush=True)
-        rec["w8a8_layer"] = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt)
+        rec["w8a8_layer"] = w8a8_layer(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias, out, dt,
+                                       n_local=n_local)
     if not args.no_cpu_baseline:
         del x, wr, wg, wu, wd, ws
         torch.cuda.empty_cache()

@@ -118,13 +118,25 @@ typedef enum {
                                  while chunk c+1's GEMMs do */
 } moe_tile_order;
 
+/* How moe_layer_fp8 runs its expert FFN and combine (moe_layer: persistent
+ * only). */
+typedef enum {
+    MOE_SCHEDULE_PERSISTENT = 0, /* one persistent kernel: gate/up, h
+                                    quantisation, down and combine tiles in
+                                    dependency order with device-side flags
+                                    (default) */
+    MOE_SCHEDULE_STAGED = 1      /* one launch per stage (moe_layer_fp8 only);
+                                    the same tiles and arithmetic, so the same
+                                    bits as the persistent kernel */
+} moe_schedule;
+
 typedef struct {
     int32_t dispatch;        /* moe_dispatch (moe_layer only) */
     int32_t tile_order;      /* moe_tile_order (moe_layer only) */
     int32_t lead;            /* MOE_ORDER_LEAD: the lead in gate/up tiles; 0 =
                                 one round of the persistent grid */
     int32_t chunks;          /* MOE_ORDER_CHUNKED: token chunks, 1..8; 0 = 4 */
-    uint32_t perturb_seed;   /* moe_layer only; 0 = off.  A test aid for the
+    uint32_t perturb_seed;   /* 0 = off.  A test aid for the
                                 flag protocol: every producer tile waits a
                                 seeded pseudo-random delay (0 to about 100 us)
                                 between writing its output and publishing it,
@@ -132,13 +144,15 @@ typedef struct {
                                 claimed in reverse order (orders 2 and 4 hand
                                 out one dependency-ordered stream, which must be
                                 claimed in order).  The result bits are
-                                unchanged; only the timing is adversarial. */
-    int64_t wait_timeout_us; /* moe_layer only: bound of each device-side flag
+                                unchanged; only the timing is adversarial.
+                                Also moe_layer_fp8's persistent schedule. */
+    int32_t schedule;        /* moe_schedule; moe_layer requires 0 */
+    int64_t wait_timeout_us; /* bound of each device-side flag
                                 wait; 0 = 2 s.  A wait that times out records
                                 MOE_ERR_DEVICE_TIMEOUT in the workspace and
                                 makes every other wait of that launch return at
                                 once, so the launch still drains. */
-    int64_t *trace;          /* moe_layer only: per-tile trace (measurement aid,
+    int64_t *trace;          /* per-tile trace of the persistent kernel (measurement aid,
                                 after X-Stage §5.1's per-tile clock traces), or
                                 NULL.  Device memory, int64 [1 + 4*trace_records]:
                                 [0] = records written (the caller zeroes it; it
@@ -146,7 +160,8 @@ typedef struct {
                                 dropped), then per tile of the persistent kernel
                                 {kind << 32 | tile index, workgroup << 8 | XCD,
                                 start tick, end tick}: kind 1 gate/up, 2 down,
-                                4 a K part of a cut down tile, 3 combine; ticks
+                                4 a K part of a cut down tile, 3 combine, 5 an
+                                h quantisation tile (moe_layer_fp8); ticks
                                 of moe_wall_clock_hz(). */
     int64_t trace_records;
     void *events[4];         /* hipEvent_t handles or NULL: recorded on `stream`
@@ -304,13 +319,24 @@ moe_status moe_down_fp8(const moe_dims *dims, const void *h, const int32_t *offs
                         const void *wq_down, const float *s_down, void *y_perm, void *ws,
                         size_t ws_bytes, void *stream);
 
-/* moe_layer_fp8: the whole forward pass with the W8A8 FFN, staged: route
- * (as moe_route), row-major permute (as moe_permute), moe_expert_ffn_fp8,
- * moe_combine -- one stream, one workspace, no host synchronisation.
+/* moe_layer_fp8: the whole forward pass with the W8A8 FFN (X-Stage §4.3
+ * fuses the MoE block into one kernel, §5.3 evaluates it in W8A8): route (as
+ * moe_route), permute, the per-row E4M3 quantisation of the routed rows of
+ * x, then by default (opts->schedule = MOE_SCHEDULE_PERSISTENT) one
+ * persistent kernel whose workgroups claim gate/up tiles (E4M3 GEMM0 with
+ * the SiLU-mul epilogue into bf16 h and each row's max |h|), quantisation
+ * tiles (32 rows of h, once their m-tile's gate/up tiles are published),
+ * down tiles (once their m-tile's rows are quantised) and combine tiles
+ * (once the down tiles holding their rows are published) -- or, with
+ * MOE_SCHEDULE_STAGED, moe_expert_ffn_fp8's launches and moe_combine.  Both
+ * give the same bits.  One stream, one workspace, no host synchronisation.
  * Arguments as moe_layer, with the E4M3 weights and scales of
  * moe_expert_ffn_fp8 in place of the bf16 weights.  Requires f % 256 == 0.
- * Of opts only events[] applies (the stages are separate launches); its
- * other fields must be zero (MOE_ERR_INVALID_ARG otherwise). */
+ * Of opts: events[], schedule, and for the persistent schedule
+ * perturb_seed, wait_timeout_us and trace (trace kinds: 1 gate/up, 5
+ * quantisation, 2 down, 3 combine); its status word sits at offset 0 of the
+ * workspace, as moe_layer's: moe_device_status reads it.  dispatch,
+ * tile_order, lead and chunks must be zero (MOE_ERR_INVALID_ARG otherwise). */
 size_t moe_layer_fp8_workspace_bytes(const moe_dims *dims);
 moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_router,
                          const float *bias, const void *wq_gate, const float *s_gate,

@@ -38,6 +38,8 @@ MOE_BF16, MOE_F32 = 0, 1
 MOE_DISPATCH_PACKED, MOE_DISPATCH_GATHER = 0, 1
 MOE_ORDER_BY_KIND, MOE_ORDER_READY_DOWN, MOE_ORDER_LEAD, MOE_ORDER_COMBINE_FIRST = 0, 1, 2, 3
 MOE_ORDER_CHUNKED = 4
+MOE_SCHEDULE_PERSISTENT = 0
+MOE_SCHEDULE_STAGED = 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_TIMEOUT"}
 
@@ -60,7 +62,8 @@ class MoEDims(C.Structure):
 class MoELayerOpts(C.Structure):
     """Per-call options of moe_layer / moe_layer_fp8 (include/moe.h)."""
     _fields_ = [("dispatch", C.c_int32), ("tile_order", C.c_int32), ("lead", C.c_int32),
-                ("chunks", C.c_int32), ("perturb_seed", C.c_uint32), ("wait_timeout_us", C.c_int64),
+                ("chunks", C.c_int32), ("perturb_seed", C.c_uint32), ("schedule", C.c_int32),
+                ("wait_timeout_us", C.c_int64),
                 ("trace", C.c_void_p), ("trace_records", C.c_int64),
                 ("events", C.c_void_p * 4)]
 
@@ -76,7 +79,8 @@ def _event_handle(ev) -> Optional[int]:
 
 def layer_opts(dispatch: int = MOE_DISPATCH_PACKED, tile_order: int = MOE_ORDER_BY_KIND,
                lead: int = 0, chunks: int = 0, perturb_seed: int = 0, wait_timeout_us: int = 0,
-               trace=None, trace_records: int = 0, events=None) -> MoELayerOpts:
+               trace=None, trace_records: int = 0, events=None,
+               schedule: int = 0) -> MoELayerOpts:
     """Build a MoELayerOpts.  trace: int64 device tensor of 1 + 4*trace_records
     elements (element 0 zeroed by the caller); events: up to 4 torch.cuda.Event
     (or None) recorded before the route, after the route, after the permute
@@ -84,6 +88,7 @@ def layer_opts(dispatch: int = MOE_DISPATCH_PACKED, tile_order: int = MOE_ORDER_
     o = MoELayerOpts()
     o.dispatch, o.tile_order, o.lead, o.chunks = int(dispatch), int(tile_order), int(lead), int(chunks)
     o.perturb_seed, o.wait_timeout_us = int(perturb_seed), int(wait_timeout_us)
+    o.schedule = int(schedule)
     if trace is not None:
         o.trace, o.trace_records = trace.data_ptr(), int(trace_records)
     for i, ev in enumerate(list(events or [])[:4]):
@@ -460,7 +465,9 @@ def moe_layer_fp8_workspace_bytes(dims) -> int:
 def moe_layer_fp8(dims, x, w_router, wq_gate, s_gate, wq_up, s_up, wq_down, s_down, bias=None,
                   out=None, out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None,
                   ws=None, opts: Optional[MoELayerOpts] = None, stream=None):
-    """Forward pass with the W8A8 expert FFN (staged).  Returns out [T, d]."""
+    """Forward pass with the W8A8 expert FFN: one persistent kernel by default,
+    separate launches with opts.schedule = MOE_SCHEDULE_STAGED (same bits).
+    Returns out [T, d]."""
     import torch
     D = _dims(dims)
     dev = x.device

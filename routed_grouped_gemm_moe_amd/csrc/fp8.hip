@@ -13,49 +13,6 @@
 namespace moe {
 namespace {
 
-// E4M3 code of a finite float (bit arithmetic on the float32 encoding).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t sign = (b >> 24) & 0x80u;
-    const uint32_t a = b & 0x7FFFFFFFu;
-    if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448: saturate
-    if (a < 0x3C800000u) {                       // |v| < 2^-6: multiples of 2^-9
-        const float t = __uint_as_float(a) * 512.0f;  // exact
-        return sign | (uint32_t)__builtin_rintf(t);   // 0..8 (8 is the smallest normal)
-    }
-    // normal: biased E4M3 exponent (a >> 23) - 120, top 3 mantissa bits, the
-    // 20 bits below rounded to nearest even (a carry moves into the exponent)
-    const uint32_t m = a & 0x7FFFFFu;
-    uint32_t code = (((a >> 23) - 120u) << 3) | (m >> 20);
-    const uint32_t rem = m & 0xFFFFFu;
-    code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
-    return sign | code;
-}
-
-// Exponent of the row scale for a row whose largest magnitude is amax.
-__device__ __forceinline__ int row_scale_exp(float amax) {
-    if (amax == 0.0f) return 0;
-    const uint32_t b = __float_as_uint(amax);
-    const int E = (int)(b >> 23) - 127;  // amax = 1.m * 2^E (subnormal amax: clamped below)
-    // 448 * 2^e = 1.75 * 2^(e+8) >= 1.m * 2^E  <=>  e >= E - 8, or E - 7 if 1.m > 1.75
-    const int e = (b & 0x7FFFFFu) > 0x600000u ? E - 7 : E - 8;
-    return e < -126 ? -126 : e;
-}
-
-__device__ __forceinline__ float amax8(const u32x4_t &v, float m) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(bf16x8_elem(v, q)));
-    return m;
-}
-
-// 8 bf16 values times 2^-e -> 8 codes (two 32-bit words).
-__device__ __forceinline__ uint2 encode8(const u32x4_t &v, float inv) {
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) w[q >> 2] |= e4m3_code(bf16x8_elem(v, q) * inv) << (8 * (q & 3));
-    return make_uint2(w[0], w[1]);
-}
-
 // Row-major quantisation: one wave per row, 4 rows per workgroup.
 __global__ __launch_bounds__(256) void quant_rows_kernel(int64_t rows, int64_t cols,
                                                          const bf16_t *__restrict__ x,
@@ -141,16 +98,9 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(int64_t K, int64_t EL,
     const int64_t kb = K / 32;  // fragments per row block
     const int64_t k_end = min<int64_t>(kb, (int64_t)(blockIdx.y + 1) * PACK_FR);
     u32x4_t *o = reinterpret_cast<u32x4_t *>(dst + rb * kb * 1024);
-    for (int64_t kk = (int64_t)blockIdx.y * PACK_FR + wave; kk < k_end; kk += 4) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (sr >= 0) {
-            const u32x4_t *p =
-                reinterpret_cast<const u32x4_t *>(src + (int64_t)sr * K + kk * 32 + (lane >> 5) * 16);
-            const uint2 lo = encode8(p[0], inv), hi = encode8(p[1], inv);
-            w = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        }
-        o[kk * 64 + lane] = w;
-    }
+    const bf16_t *srow = sr >= 0 ? src + (int64_t)sr * K : nullptr;
+    for (int64_t kk = (int64_t)blockIdx.y * PACK_FR + wave; kk < k_end; kk += 4)
+        o[kk * 64 + lane] = quant_frag(srow, inv, kk, lane);
 }
 
 // Map workgroup b to tile L in [0, n): XCD x = b % 8 takes [x*per, x*per+per).

@@ -43,6 +43,77 @@ __device__ __forceinline__ f32x16_t mfma_f8(const i32x8_t &a, const i32x8_t &b, 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Per-row E4M3 quantisation (the rule of fp8.hip's header: scale 2^e, the
+// smallest power of two with max|x| <= 448 * 2^e, codes rounded to nearest
+// even), shared by the quantisation kernels and the persistent layer.
+//
+// E4M3 code of a finite float (bit arithmetic on the float32 encoding).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    if (a >= 0x43E00000u) return sign | 0x7Eu;  // |v| >= 448: saturate
+    if (a < 0x3C800000u) {                       // |v| < 2^-6: multiples of 2^-9
+        const float t = __uint_as_float(a) * 512.0f;  // exact
+        return sign | (uint32_t)__builtin_rintf(t);   // 0..8 (8 is the smallest normal)
+    }
+    // normal: biased E4M3 exponent (a >> 23) - 120, top 3 mantissa bits, the
+    // 20 bits below rounded to nearest even (a carry moves into the exponent)
+    const uint32_t m = a & 0x7FFFFFu;
+    uint32_t code = (((a >> 23) - 120u) << 3) | (m >> 20);
+    const uint32_t rem = m & 0xFFFFFu;
+    code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+    return sign | code;
+}
+
+// Exponent of the row scale for a row whose largest magnitude is amax.
+__device__ __forceinline__ int row_scale_exp(float amax) {
+    if (amax == 0.0f) return 0;
+    const uint32_t b = __float_as_uint(amax);
+    const int E = (int)(b >> 23) - 127;  // amax = 1.m * 2^E (subnormal amax: clamped below)
+    // 448 * 2^e = 1.75 * 2^(e+8) >= 1.m * 2^E  <=>  e >= E - 8, or E - 7 if 1.m > 1.75
+    const int e = (b & 0x7FFFFFu) > 0x600000u ? E - 7 : E - 8;
+    return e < -126 ? -126 : e;
+}
+
+__device__ __forceinline__ float amax8(const u32x4_t &v, float m) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(bf16x8_elem(v, q)));
+    return m;
+}
+
+// 8 bf16 values times 2^-e -> 8 codes (two 32-bit words).
+//
+// The hardware conversion (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest
+// even, two values per instruction) gives e4m3_code's bits on every input
+// the quantisers produce -- |x * 2^-e| <= 448 by the choice of e, so its
+// overflow case never arises; the GPU tests pin the quantiser against the
+// oracle on every bf16 value up to 448 -- at a tenth of the instructions.
+__device__ __forceinline__ uint2 encode8(const u32x4_t &v, float inv) {
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = bf16x8_elem(v, q) * inv;
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6], x[7], w1, true);
+    return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+// Codes of one 16-byte piece of a packed E4M3 fragment (the layout of
+// gemm_pa.h over bytes): lane l of fragment kk holds row l % 32, k = 32 kk +
+// 16 (l / 32) .. + 15, here taken from row (bf16, scaled by inv = 2^-e before
+// encoding) or zero codes when row is null (padding rows).
+__device__ __forceinline__ u32x4_t encode16(const u32x4_t &a, const u32x4_t &b, float inv) {
+    const uint2 lo = encode8(a, inv), hi = encode8(b, inv);
+    return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+__device__ __forceinline__ u32x4_t quant_frag(const bf16_t *row, float inv, int64_t kk, int lane) {
+    if (!row) return u32x4_t{0u, 0u, 0u, 0u};
+    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(row + kk * 32 + (lane >> 5) * 16);
+    return encode16(p[0], p[1], inv);
+}
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -160,7 +231,9 @@ enum { F8_SILU_ROWS = 0, F8_BF16 = 1 };
 //          written so far (atomic max; non-negative floats order as their
 //          bits); zero before the first tile of a row
 // LDS: PA_LDS_BYTES at lds, free again when the call returns.
-template <int EPI>
+// WT: outputs written with device-scope stores (store16_wt), for a producer
+// that publishes without an L2 write-back.
+template <int EPI, bool WT = false>
 __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int64_t a_kb,
                                              int a_rows, int K, const float *__restrict__ sa,
                                              const uint8_t *__restrict__ B0,
@@ -238,7 +311,9 @@ __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < a_rows * 16; g += GEMM_THREADS) {
             const int r = g >> 4, c = g & 15;
-            reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld)[c] = src[r * 16 + (c ^ (r & 15))];
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld) + c;
+            if (WT) store16_wt(dst, src[r * 16 + (c ^ (r & 15))]);
+            else *dst = src[r * 16 + (c ^ (r & 15))];
         }
         if (rowmax && tid < a_rows) {  // one thread per row: max |h| over the tile's columns
             float m = 0.0f;
@@ -265,7 +340,9 @@ __device__ __forceinline__ void gemm_tile_f8(const uint8_t *__restrict__ Ap, int
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < a_rows * 32; g += GEMM_THREADS) {
             const int r = g >> 5, c = g & 31;
-            reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld)[c] = src[r * 32 + (c ^ (r & 7))];
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld) + c;
+            if (WT) store16_wt(dst, src[r * 32 + (c ^ (r & 7))]);
+            else *dst = src[r * 32 + (c ^ (r & 7))];
         }
     }
     __syncthreads();  // LDS free for the next tile

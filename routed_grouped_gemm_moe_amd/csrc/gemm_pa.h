@@ -56,6 +56,17 @@ __device__ i32x4_t raw_buffer_load_v4(i32x4_t rsrc, int voffset, int soffset, in
 // Cache-policy operand of a buffer load: sc1 (bit 4).
 constexpr int PA_CPOL_SC1 = 16;
 
+// A 16-byte store at device scope (sc1): written through to the device's
+// point of coherence rather than held dirty in this XCD's L2, so a producer
+// whose outputs all go out this way publishes them without an L2 write-back
+// (it waits for the stores, then raises its flag).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void store16_wt(void *p, const u32x4_t &v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+#pragma clang diagnostic pop
+
 // Memory instruction issued after MFMA k (0..15) of sub-step q (0..3):
 // kind 1: B-fragment LDS read idx (of sub-step q+1; of the next stage's
 // sub-step 0 when q = 3), kind 2: A load for row block idx (after that block's
@@ -214,7 +225,9 @@ __device__ __forceinline__ int y_stage_index(int r, int c) {
 // Returns false in all but the last-arriving workgroup.  In the last, the
 // bf16 tile of the part-ordered sum is left in LDS (y_stage_index layout).
 // LDS must be free (the K loop ends with a barrier); the caller copies the
-// tile out.
+// tile out.  WT: the partials go out with device-scope stores, so the
+// arrival needs no L2 write-back.
+template <bool WT>
 __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitCtl &sp, int tid,
                                              int wave, int lane, char *lds) {
     float *mine = sp.part + sp.self * (BM * BN_DN);
@@ -223,20 +236,27 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<f32x4_t *>(mine + split_slot(wave, i, j, g, lane)) =
-                    f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                            acc[i][j][4 * g + 3]};
-    // every wave's stores reached L2; one agent-scope release RMW writes this
-    // XCD's L2 back and counts the arrival
+            for (int g = 0; g < 4; ++g) {
+                const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                   acc[i][j][4 * g + 3]};
+                float *dst = mine + split_slot(wave, i, j, g, lane);
+                if (WT) store16_wt(dst, __builtin_bit_cast(u32x4_t, v));
+                else *reinterpret_cast<f32x4_t *>(dst) = v;
+            }
+    // every wave's stores are performed (WT) or reached L2; one agent-scope
+    // RMW counts the arrival -- a release, which writes this XCD's L2 back,
+    // unless the partials were written through
     wait_vmcnt<0>();
     __syncthreads();
     int *s_x = reinterpret_cast<int *>(lds);
     if (wave == 0) {
         for (int i = 0; i < sp.sleeps; ++i) __builtin_amdgcn_s_sleep(127);
         // lane 0 adds 1, the others 0: lane 0's pre-op value is the arrival
-        const int old = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(
-            sp.cnt, lane == 0 ? 1 : 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
+        const int old = __builtin_amdgcn_readfirstlane(
+            WT ? __hip_atomic_fetch_add(sp.cnt, lane == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT)
+               : __hip_atomic_fetch_add(sp.cnt, lane == 0 ? 1 : 0, __ATOMIC_RELEASE,
+                                        __HIP_MEMORY_SCOPE_AGENT));
         *s_x = old;  // every lane stores the same value
     }
     __syncthreads();
@@ -317,7 +337,10 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
 // Returns whether this call wrote the tile's output (false only for a part
 // of a cut tile that did not arrive last).
 // LDS: PA_LDS_BYTES at lds, free again when the call returns.
-template <int EPI>
+// WT: every output (h, y, cut-tile partials) written with device-scope
+// stores (store16_wt), for a producer that publishes without an L2
+// write-back.
+template <int EPI, bool WT = false>
 __device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int64_t a_kb,
                                              int a_rows, int K, const bf16_t *__restrict__ B0,
                                              const bf16_t *__restrict__ B1, int64_t ldb,
@@ -395,14 +418,16 @@ __device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int6
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < nb_all * 512; g += GEMM_THREADS) {
             const int rb = g >> 9;
-            reinterpret_cast<u32x4_t *>(out + rb * o_ld * 512)[g & 511] = src[g];
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + rb * o_ld * 512) + (g & 511);
+            if (WT) store16_wt(dst, src[g]);
+            else *dst = src[g];
         }
     } else {
         // y tile: 256 rows x 256 columns, row-major in LDS with the 16-byte
         // chunk index of row r xor-ed with r & 7 (even spread of the row
         // writes of the two lane halves over the banks).
         if (sp) {
-            if (!split_reduce(acc, *sp, tid, wave, lane, lds)) return false;
+            if (!split_reduce<WT>(acc, *sp, tid, wave, lane, lds)) return false;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -418,7 +443,9 @@ __device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int6
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < a_rows * 32; g += GEMM_THREADS) {
             const int r = g >> 5, c = g & 31;
-            reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld)[c] = src[r * 32 + (c ^ (r & 7))];
+            u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld) + c;
+            if (WT) store16_wt(dst, src[r * 32 + (c ^ (r & 7))]);
+            else *dst = src[r * 32 + (c ^ (r & 7))];
         }
     }
     return true;

@@ -51,7 +51,7 @@
 // MOE_ERR_DEVICE_TIMEOUT in the status word and carries on (the result is
 // then invalid, but the kernel drains).
 #include "combine_tile.h"
-#include "gemm_pa.h"
+#include "gemm_f8.h"
 
 namespace moe {
 namespace {
@@ -102,7 +102,10 @@ __device__ __forceinline__ void sleep_units(int n) {  // n wave-uniform
 
 // Claim one tile of [0, n) for the calling wave.  Queue y covers
 // [y*per, y*per + per); the own XCD's queue first, then the others.  With
-// rev, each range is handed out from its far end.
+// rev, each range is handed out from its far end.  The own queue is bumped
+// at once (one round trip; a bump past its end is harmless, every claim
+// compares the count with the range's length); the others are read first,
+// so a drained range is passed over without a write.
 __device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd, bool rev = false) {
     const int per = (n + NUM_XCD - 1) / NUM_XCD;
     for (int r = 0; r < NUM_XCD; ++r) {
@@ -111,7 +114,8 @@ __device__ __forceinline__ int claim_tile(int32_t *q, int n, int xcd, bool rev =
         const int len = min(n, lo + per) - lo;
         if (len <= 0) continue;
         int32_t *c = q + y * QSTRIDE;
-        if (uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= len)
+        if (r > 0 &&
+            uniform(__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= len)
             continue;
         // lane 0 adds 1, the others 0: lane 0's pre-op value is the claim
         const int old = uniform(__hip_atomic_fetch_add(c, lane_id() == 0 ? 1 : 0,
@@ -203,6 +207,27 @@ __device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, in
     }
 }
 
+// publish for a tile whose outputs were all written with device-scope stores
+// or atomics: once every wave's writes are performed the counter is raised
+// with a relaxed RMW -- no L2 write-back (which would flush every dirty line
+// of the XCD's L2, other workgroups' included).
+__device__ __forceinline__ void publish_wt(int32_t *p, bool add, int32_t *xmask, int xcd,
+                                           int sleeps) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (wave_id() == 0) {
+        sleep_units(sleeps);
+        const bool l0 = lane_id() == 0;
+        if (xmask)
+            __hip_atomic_fetch_or(xmask, l0 ? (1 << xcd) : 0, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        if (add)
+            __hip_atomic_fetch_add(p, l0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            __hip_atomic_store(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // Optional per-tile trace (measurement aid): one 4 x int64 record per tile,
@@ -253,7 +278,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
     const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
     const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
                       S, perturb_sleeps(a.perturb, 4, (uint32_t)LS)};
-    const bool wrote = gemm_tile_pa<PA_BF16>(
+    const bool wrote = gemm_tile_pa<PA_BF16, true>(
         a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
         nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
         part < 0 ? nullptr : &sc);
@@ -261,10 +286,10 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
         trace_tile(a, 4, LS, xcd, t0);
         return;
     }
-    publish(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
-            perturb_sleeps(a.perturb, 2, (uint32_t)LS));
-    // count published down tiles (after the release above, so a
-    // reader that sees the full count also sees every y row)
+    publish_wt(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
+               perturb_sleeps(a.perturb, 2, (uint32_t)LS));
+    // count published down tiles (y is performed before either atomic, so
+    // a reader that sees the full count also sees every y row)
     if (wave_id() == 0) {
         __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -447,14 +472,201 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                                            (int)d, ho, f / 16, 0, 0, lds, a.perm_src + t.row0,
                                            D.T);
             else
-                gemm_tile_pa<PA_SILU_PACKED>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
+                gemm_tile_pa<PA_SILU_PACKED, true>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
                                              (int)d, a.w_gate + wo, a.w_up + wo, d, ho, f / 16,
                                              lds);
-            publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
-                    perturb_sleeps(a.perturb, 1, (uint32_t)L));
+            // the gathered tile writes h with ordinary stores: a release
+            if (a.gather)
+                publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
+                        perturb_sleeps(a.perturb, 1, (uint32_t)L));
+            else
+                publish_wt(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
+                           perturb_sleeps(a.perturb, 1, (uint32_t)L));
             trace_tile(a, 1, L, xcd, t0);
         }
 
+}
+
+// ---------------------------------------------------------------- W8A8
+// The W8A8 layer in one persistent kernel (X-Stage, §4.3 runs the whole MoE
+// block as one fused kernel and §5.3 evaluates it with W8A8): four tile
+// kinds, claimed in dependency order from per-XCD queues as above --
+//   1. gate/up tiles: E4M3 GEMM0 + SiLU-mul epilogue into bf16 h, with each
+//      row's max |h| collected by atomic max; bump gu_done[m-tile];
+//   2. quantisation tiles (m-tile, qrb row blocks of 32): once every gate/up
+//      tile of the m-tile is published, the rows' power-of-two scales from
+//      their maxima and their E4M3 codes in the packed layout; bump
+//      q_done[m-tile];
+//   3. down tiles: once all quantisation tiles of the m-tile are done, E4M3
+//      GEMM1 into y; set dn_flag;
+//   4. combine tiles, as in the bf16 kernel.
+// Every tile computes exactly what the staged launches compute for it (the
+// same tile functions and the same encoder), so the two give the same bits.
+// Memory ordering: every output of a producer tile (h, its codes and
+// scales, y) is written with device-scope stores, and h's row maxima with
+// device-scope atomics, so a producer publishes with a relaxed RMW once its
+// writes are performed, without writing its XCD's L2 back (measured: the
+// write-backs cost 5-8% of the kernel); consumers acquire as in the bf16
+// kernel and read the row maxima with device-coherent loads.
+
+__device__ __forceinline__ void acquire_from(const int32_t *xmask, int xcd) {
+    const int producers =
+        uniform(__hip_atomic_load(xmask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (producers & ~(1 << xcd))
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    else
+        invalidate_l1();
+}
+
+__device__ __forceinline__ void quant_tile_f8(const LayerF8Args &a8, int Lq, int NT1, int xcd) {
+    const LayerArgs &a = a8.b;
+    const int64_t f = a.D.f;
+    const int qpm = QB_PER_MT / a8.qrb;  // quantisation tiles per m-tile
+    const int mt = Lq / qpm, rb0 = (Lq % qpm) * a8.qrb;
+    const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+    if (wave_id() == 0) wave_wait_geq(a.gu_done + mt, NT1, true, a.wait_ticks, a.status);
+    __syncthreads();
+    acquire_from(a.gu_xcd + mt, xcd);
+    const MTile t = a.mtiles[mt];
+    // row blocks past the m-tile's rows belong to no segment (uniform bound)
+    for (int rb = rb0; rb < rb0 + a8.qrb && rb * 32 < t.rows; ++rb) {
+        const int r0 = rb * 32;
+        const int lane = lane_id(), wave = wave_id();
+        const int r = lane & 31;
+        const bool valid = r0 + r < t.rows;  // padding rows: zero codes, scale 1
+        const int64_t row = (int64_t)t.row0 + r0 + r;
+        const float amax =
+            valid ? __uint_as_float(__hip_atomic_load(a8.hmax + row, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT))
+                  : 0.0f;
+        const int e = row_scale_exp(amax);
+        const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+        if (wave == 0 && lane < 32)
+            __hip_atomic_store(a8.sh + t.prow0 + r0 + r, __uint_as_float((uint32_t)(127 + e) << 23),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u32x4_t *src =
+            reinterpret_cast<const u32x4_t *>(a8.h + row * f + (lane >> 5) * 16);
+        u32x4_t *o = reinterpret_cast<u32x4_t *>(a8.hq + ((int64_t)t.prow0 / 32 + rb) * (f / 32) * 1024);
+        // fragments kk = wave + 4i; QB of them in flight per lane
+        constexpr int QB = 4, NW = GEMM_THREADS / 64;
+        const int64_t nkk = f / 32;
+        for (int64_t kk0 = wave; kk0 < nkk; kk0 += NW * QB) {
+            u32x4_t raw[QB][2];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int64_t kk = kk0 + NW * b;
+                if (valid && kk < nkk) {
+                    raw[b][0] = src[kk * 4];
+                    raw[b][1] = src[kk * 4 + 1];
+                } else {
+                    raw[b][0] = raw[b][1] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int64_t kk = kk0 + NW * b;
+                if (kk < nkk) store16_wt(o + kk * 64 + lane, encode16(raw[b][0], raw[b][1], inv));
+            }
+        }
+    }
+    publish_wt(a8.q_done + mt, true, a8.q_xcd + mt, xcd, perturb_sleeps(a.perturb, 5, (uint32_t)Lq));
+    trace_tile(a, 5, Lq, xcd, t0);
+}
+
+__device__ __forceinline__ void down_tile_f8(const LayerF8Args &a8, int L, int MT, int NT2, int xcd,
+                                             char *lds) {
+    const LayerArgs &a = a8.b;
+    const int64_t d = a.D.d, f = a.D.f;
+    const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+    int mt, nt;
+    expert_tile(L, MT, NT2, (int)a.D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
+    const MTile t = a.mtiles[mt];
+    if (wave_id() == 0)
+        wave_wait_geq(a8.q_done + mt, QB_PER_MT / a8.qrb, true, a.wait_ticks, a.status);
+    __syncthreads();
+    acquire_from(a8.q_xcd + mt, xcd);
+    const int64_t wo = (int64_t)t.e * d + (int64_t)nt * BN_DN;
+    gemm_tile_f8<F8_BF16, true>(a8.hq + (int64_t)(t.prow0 / 32) * (f / 32) * 1024, f / 32, t.rows,
+                          (int)f, a8.sh + t.prow0, a8.wd + wo * f, nullptr, a8.sd + wo, nullptr,
+                          a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
+    publish_wt(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
+               perturb_sleeps(a.perturb, 2, (uint32_t)L));
+    if (wave_id() == 0)  // after the flag, so a reader that sees the full count sees every y row
+        __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    trace_tile(a, 2, L, xcd, t0);
+}
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a8) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ int s_claim;
+    const LayerArgs &a = a8.b;
+    const Dims &D = a.D;
+    const int xcd = hw_xcd();
+    const int MT = *a.n_mtiles;
+    const int NT1 = (int)D.nt_gu();
+    const int NT2 = (int)D.nt_dn();
+    const int64_t d = D.d, f = D.f;
+    const bool rev = a.perturb != 0;
+    const int n1 = MT * NT1, nq = MT * (QB_PER_MT / a8.qrb), n2 = MT * NT2;
+    const int NTB = (int)D.comb_blocks();
+    const int n3 = NTB * ((NT2 + COMB_CB - 1) / COMB_CB);
+    int32_t *const q1 = a.queues, *const qq = a.queues + NUM_XCD * QSTRIDE,
+                   *const q2 = a.queues + 2 * NUM_XCD * QSTRIDE,
+                   *const q3 = a.queues + 3 * NUM_XCD * QSTRIDE;
+    constexpr int KQ = 1 << 28, KD = 1 << 29, KC = 1 << 30;
+    bool all_done = false;
+    int phase = 1;  // 1 gate/up, 2 quantisation, 3 down, 4 combine
+    for (;;) {
+        if (wave_id() == 0) {
+            int v;
+            if (phase == 1) {
+                const int c = claim_tile(q1, n1, xcd, rev);
+                v = c >= 0 ? c : -2;
+            } else if (phase == 2) {
+                const int c = claim_tile(qq, nq, xcd, rev);
+                v = c >= 0 ? (c | KQ) : -2;
+            } else if (phase == 3) {
+                const int c = claim_tile(q2, n2, xcd, rev);
+                v = c >= 0 ? (c | KD) : -2;
+            } else {
+                const int c = claim_tile(q3, n3, xcd, rev);
+                v = c >= 0 ? (c | KC) : -1;
+            }
+            s_claim = v;  // every lane stores the same value
+        }
+        __syncthreads();
+        const int v = uniform(s_claim);
+        __syncthreads();
+        if (v == -2) {  // this kind is drained: the next one
+            ++phase;
+            continue;
+        }
+        if (v < 0) break;
+        if (v & KC) {
+            combine_tile<OUT_F32>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
+        } else if (v & KD) {
+            down_tile_f8(a8, v & ~KD, MT, NT2, xcd, lds);
+        } else if (v & KQ) {
+            quant_tile_f8(a8, v & ~KQ, NT1, xcd);
+        } else {
+            const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
+            int mt, nt;
+            expert_tile(v, MT, NT1, (int)D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
+            const MTile t = a.mtiles[mt];
+            const int64_t wo = (int64_t)t.e * f + (int64_t)nt * BN_GU;
+            gemm_tile_f8<F8_SILU_ROWS, true>(a8.xq + (int64_t)(t.prow0 / 32) * (d / 32) * 1024,
+                                             d / 32,
+                                       t.rows, (int)d, a8.sx + t.prow0, a8.wg + wo * d,
+                                       a8.wu + wo * d, a8.sg + wo, a8.su + wo,
+                                       a8.h + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds,
+                                       a8.hmax + t.row0);
+            publish_wt(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
+                       perturb_sleeps(a.perturb, 1, (uint32_t)v));
+            trace_tile(a, 1, v, xcd, t0);
+        }
+    }
 }
 
 // Position, in the gate/up blocked order (expert_tile), of the last gate/up
@@ -688,11 +900,11 @@ int layer_grid_size() {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipFuncSetAttribute((const void *)layer_kernel<false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) != hipSuccess ||
-        hipFuncSetAttribute((const void *)layer_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) != hipSuccess)
-        return 0;
+    for (const void *k : {(const void *)layer_kernel<false>, (const void *)layer_kernel<true>,
+                          (const void *)layer_f8_kernel<false>, (const void *)layer_f8_kernel<true>})
+        if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) !=
+            hipSuccess)
+            return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)layer_kernel<false>,
                                                      GEMM_THREADS, GEMM_LDS_BYTES) != hipSuccess ||
         occ < 1)
@@ -710,6 +922,16 @@ int64_t wall_clock_hz() {
         khz = 100000;  // 100 MHz, the documented constant rate
     cached = (int64_t)khz * 1000;
     return cached;
+}
+
+hipError_t launch_layer_f8_persistent(const LayerF8Args &a, int grid, hipStream_t s) {
+    if (a.b.out_f32)
+        hipLaunchKernelGGL(layer_f8_kernel<true>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
+                           a);
+    else
+        hipLaunchKernelGGL(layer_f8_kernel<false>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
+                           a);
+    return hipGetLastError();
 }
 
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s) {

@@ -98,13 +98,20 @@ moe_status check_ws(void *ws, size_t ws_bytes, size_t need) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Range checks of per-call options; the W8A8 layer takes events only.
-moe_status check_opts(const moe_layer_opts *o, bool staged_fp8) {
+moe_status check_opts(const moe_layer_opts *o, bool fp8) {
     if (!o) return MOE_OK;
-    if (staged_fp8)
-        return (o->dispatch || o->tile_order || o->lead || o->chunks || o->perturb_seed ||
-                o->wait_timeout_us || o->trace || o->trace_records)
-                   ? MOE_ERR_INVALID_ARG
-                   : MOE_OK;
+    if (fp8) {
+        if (o->dispatch || o->tile_order || o->lead || o->chunks) return MOE_ERR_INVALID_ARG;
+        if (o->schedule == MOE_SCHEDULE_STAGED)  // separate launches: no tiles to perturb or trace
+            return o->perturb_seed || o->wait_timeout_us || o->trace || o->trace_records
+                       ? MOE_ERR_INVALID_ARG
+                       : MOE_OK;
+        if (o->schedule != MOE_SCHEDULE_PERSISTENT || o->wait_timeout_us < 0 ||
+            o->trace_records < 0 || (o->trace_records > 0 && !o->trace))
+            return MOE_ERR_INVALID_ARG;
+        return MOE_OK;
+    }
+    if (o->schedule != MOE_SCHEDULE_PERSISTENT) return MOE_ERR_INVALID_ARG;
     if (o->dispatch != MOE_DISPATCH_PACKED && o->dispatch != MOE_DISPATCH_GATHER)
         return MOE_ERR_INVALID_ARG;
     if (o->tile_order < MOE_ORDER_BY_KIND || o->tile_order > MOE_ORDER_CHUNKED)
@@ -378,11 +385,13 @@ hipError_t run_ffn_fp8(const Dims &D, const bf16_t *x_perm, const int32_t *offse
     return e;
 }
 
-// Workspace of moe_layer_fp8: routing, the row-major permute, x_perm and y
-// rows, then the FFN's Layout8 region.
+// Workspace of moe_layer_fp8: the persistent kernel's scheduler state first
+// (status word at offset 0; cleared by the dispatch scan in one range, h's
+// row maxima included), routing and permute indices, y rows, then the FFN's
+// Layout8 region (m-tile table, packed codes and scales, h).
 struct LayoutL8 {
-    size_t route, ids, gates, blk_counts, blk_base, arrive, counts, offsets, perm_src, inv_perm,
-        x_perm, y, ffn, total;
+    size_t status, queues, gu_done, gu_xcd, q_done, q_xcd, dn_flag, hmax, sched_end, route, ids,
+        gates, blk_counts, blk_base, arrive, counts, offsets, perm_src, inv_perm, y, ffn, total;
 };
 LayoutL8 make_layout_l8(const Dims &D) {
     LayoutL8 L{};
@@ -393,6 +402,16 @@ LayoutL8 make_layout_l8(const Dims &D) {
         return o;
     };
     const size_t Tk = (size_t)(D.T * D.k), EL = (size_t)D.EL(), cap = (size_t)D.cap();
+    const size_t MT = (size_t)D.max_mtiles();
+    L.status = take(256);
+    L.queues = take(4 * NUM_XCD * QSTRIDE * sizeof(int32_t));
+    L.gu_done = take(MT * sizeof(int32_t));
+    L.gu_xcd = take(MT * sizeof(int32_t));
+    L.q_done = take(MT * sizeof(int32_t));
+    L.q_xcd = take(MT * sizeof(int32_t));
+    L.dn_flag = take(MT * (size_t)D.nt_dn() * sizeof(int32_t));
+    L.hmax = take(cap * sizeof(uint32_t));
+    L.sched_end = off;
     L.route = take(route_workspace_bytes(D));
     L.ids = take(Tk * sizeof(int32_t));
     L.gates = take(Tk * sizeof(float));
@@ -403,7 +422,6 @@ LayoutL8 make_layout_l8(const Dims &D) {
     L.offsets = take((EL + 1) * sizeof(int32_t));
     L.perm_src = take(cap * sizeof(int32_t));
     L.inv_perm = take(Tk * sizeof(int32_t));
-    L.x_perm = take(cap * (size_t)D.d * 2);
     L.y = take(cap * (size_t)D.d * 2);
     L.ffn = take(make_layout8(D).total);
     L.total = off;
@@ -437,34 +455,100 @@ moe_status moe_layer_fp8(const moe_dims *dims, const void *x, const void *w_rout
     const LayoutL8 L = make_layout_l8(D);
     if ((st = check_ws(ws, ws_bytes, L.total)) != MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    moe_layer_opts o{};
+    if (opts) o = *opts;
+    const bool persistent = o.schedule == MOE_SCHEDULE_PERSISTENT;
+    const int grid = persistent ? layer_grid_size() : 0;
+    if (persistent && grid <= 0) return MOE_ERR_HIP;
     int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
     float *gates = topk_w_out ? topk_w_out : at<float>(ws, L.gates);
     int32_t *offsets = at<int32_t>(ws, L.offsets), *inv_perm = at<int32_t>(ws, L.inv_perm);
     bf16_t *y = at<bf16_t>(ws, L.y);
     int32_t *perm_src = at<int32_t>(ws, L.perm_src);
+    char *ffn = at<char>(ws, L.ffn);
+    const Layout8 F = make_layout8(D);
+    // The persistent schedule has the dispatch scan build the m-tile table
+    // and clear its scheduler state; the staged FFN builds its own table.
+    int32_t *pstart = persistent ? at<int32_t>(ffn, F.pstart) : nullptr;
+    MTile *mt = persistent ? at<MTile>(ffn, F.mtiles) : nullptr;
+    int32_t *nmt = persistent ? at<int32_t>(ffn, F.n_mtiles) : nullptr;
+    int32_t *mtile_base = persistent ? at<int32_t>(ffn, F.mtile_base) : nullptr;
+    int32_t *sched = persistent ? at<int32_t>(ws, L.status) : nullptr;
+    const int64_t sched_ints = persistent ? (int64_t)((L.sched_end - L.status) / 4) : 0;
     // the router may also take over the permute's histogram and scan
     const ScanArgs sa = make_scan_args(D, at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base),
-                                       at<int32_t>(ws, L.counts), offsets, nullptr, nullptr,
-                                       nullptr, nullptr, nullptr, 0, at<int32_t>(ws, L.arrive));
+                                       at<int32_t>(ws, L.counts), offsets, pstart, mt, nmt,
+                                       mtile_base, sched, sched_ints, at<int32_t>(ws, L.arrive));
     int prep = PREP_NONE;
     hipError_t e = mark_event(opts, 0, s);
     if (e == hipSuccess)
         e = launch_route(D, (const bf16_t *)x, (const bf16_t *)w_router, bias, ids, gates, nullptr,
                          at<char>(ws, L.route), route_workspace_bytes(D), s, &sa, &prep);
     if (e == hipSuccess) e = mark_event(opts, 1, s);
-    // No x_perm: the FFN quantises each token's row of x once and places its
-    // codes at every routed row of that token through perm_src.
+    // No x_perm: each token's row of x is quantised once and its codes placed
+    // at every routed row of that token through perm_src.
     if (e == hipSuccess)
         e = launch_permute(D, (const bf16_t *)x, ids, at<int32_t>(ws, L.counts), offsets, perm_src,
                            inv_perm, nullptr, at<int32_t>(ws, L.blk_counts),
-                           at<int32_t>(ws, L.blk_base), nullptr, nullptr, nullptr, nullptr,
-                           nullptr, 0, s, prep, sa.arrive);
+                           at<int32_t>(ws, L.blk_base), pstart, mt, nmt, mtile_base, sched,
+                           sched_ints, s, prep, sa.arrive);
     if (e == hipSuccess) e = mark_event(opts, 2, s);
-    if (e == hipSuccess)
-        e = run_ffn_fp8(D, (const bf16_t *)x, offsets, (const uint8_t *)wq_gate, s_gate,
-                        (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
-                        at<char>(ws, L.ffn), s, perm_src);
-    if (e == hipSuccess) e = launch_combine(D, y, inv_perm, gates, out, out_dtype == MOE_F32, s);
+    if (!persistent) {
+        if (e == hipSuccess)
+            e = run_ffn_fp8(D, (const bf16_t *)x, offsets, (const uint8_t *)wq_gate, s_gate,
+                            (const uint8_t *)wq_up, s_up, (const uint8_t *)wq_down, s_down, y,
+                            ffn, s, perm_src);
+        if (e == hipSuccess)
+            e = launch_combine(D, y, inv_perm, gates, out, out_dtype == MOE_F32, s);
+    } else {
+        uint8_t *xq = at<uint8_t>(ffn, F.xq);
+        float *sx = at<float>(ffn, F.sx);
+        if (e == hipSuccess)
+            e = launch_quant_pack(D, D.d, (const bf16_t *)x, offsets, pstart, at<float>(ffn, F.amax),
+                                  false, xq, sx, s, perm_src, D.T);
+        if (e == hipSuccess) {
+            const int64_t wait_us = o.wait_timeout_us > 0 ? o.wait_timeout_us : 2000000;
+            LayerF8Args a8{};
+            LayerArgs &a = a8.b;
+            a.D = D;
+            a.perturb = o.perturb_seed;
+            a.ids = ids;
+            a.inv_perm = inv_perm;
+            a.offsets = offsets;
+            a.mtile_base = mtile_base;
+            a.n_mtiles = nmt;
+            a.gates = gates;
+            a.mtiles = mt;
+            a.queues = at<int32_t>(ws, L.queues);
+            a.gu_done = at<int32_t>(ws, L.gu_done);
+            a.gu_xcd = at<int32_t>(ws, L.gu_xcd);
+            a.dn_flag = at<int32_t>(ws, L.dn_flag);
+            a.status = at<int32_t>(ws, L.status);
+            a.dn_done = at<int32_t>(ws, L.status) + 32;  // 128 bytes past the status word
+            a.y = y;
+            a.out = out;
+            a.out_f32 = out_dtype == MOE_F32;
+            a.wait_ticks = wait_us * (wall_clock_hz() / 1000000);
+            a.trace = o.trace_records > 0 ? o.trace : nullptr;
+            a.trace_cap = o.trace_records > 0 ? o.trace_records : 0;
+            a8.xq = xq;
+            a8.sx = sx;
+            a8.wg = (const uint8_t *)wq_gate;
+            a8.wu = (const uint8_t *)wq_up;
+            a8.wd = (const uint8_t *)wq_down;
+            a8.sg = s_gate;
+            a8.su = s_up;
+            a8.sd = s_down;
+            a8.h = at<bf16_t>(ffn, F.h);
+            a8.hmax = at<uint32_t>(ws, L.hmax);
+            a8.hq = at<uint8_t>(ffn, F.hq);
+            a8.sh = at<float>(ffn, F.sh);
+            a8.q_done = at<int32_t>(ws, L.q_done);
+            a8.q_xcd = at<int32_t>(ws, L.q_xcd);
+            a8.qrb = quant_tile_row_blocks(D.f);
+            e = launch_layer_f8_persistent(a8, grid, s);
+        }
+    }
     if (e == hipSuccess) e = mark_event(opts, 3, s);
     return hip_status(e);
 }

@@ -286,6 +286,38 @@ struct LayerArgs {
     int64_t trace_cap;   // records that fit after the count
 };
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s);
+
+// The W8A8 persistent kernel (layer.hip): b carries the shared state (the
+// m-tile table, queues -- four kinds here --, gu_done/gu_xcd, dn_flag,
+// dn_done, status, y, the combine inputs and output; b.order must be 0),
+// plus the packed x codes and scales, the E4M3 weights and their row scales,
+// h with its row maxima, h's packed codes and scales and the per-m-tile
+// count of quantised row blocks.
+struct LayerF8Args {
+    LayerArgs b;
+    const uint8_t *xq;
+    const float *sx;
+    const uint8_t *wg, *wu, *wd;
+    const float *sg, *su, *sd;
+    bf16_t *h;        // [cap][f] row-major
+    uint32_t *hmax;   // [cap] float bits of max |h| per row (zero before the call)
+    uint8_t *hq;      // packed codes of h
+    float *sh;        // [pcap] row scales of hq
+    int32_t *q_done;  // [MT] finished quantisation tiles per m-tile
+    int32_t *q_xcd;   // [MT] XCDs that ran them
+    int qrb;          // row blocks of 32 per quantisation tile: 1, 2, 4 or 8
+};
+// Row blocks of 32 per m-tile.
+constexpr int QB_PER_MT = BM / 32;
+// Row blocks per quantisation tile: enough rows for about 256 Ki elements
+// of h (a tile's fixed costs -- the wait, the acquire, the publish -- then
+// stay small against its memory traffic), at most one m-tile.
+inline int quant_tile_row_blocks(int64_t f) {
+    int q = 1;
+    while (q < QB_PER_MT && (int64_t)q * 32 * f < (int64_t)1 << 18) q *= 2;
+    return q;
+}
+hipError_t launch_layer_f8_persistent(const LayerF8Args &a, int grid, hipStream_t s);
 // The claim table of tile orders 2 to 4 (a.order_tab), from the m-tile table
 // on the device; nothing for the other orders.
 hipError_t launch_build_order(const LayerArgs &a, int grid, hipStream_t s);

@@ -171,15 +171,26 @@ def test_layer_options_are_checked_per_call():
     for bad in (dict(dispatch=2), dict(dispatch=-1), dict(tile_order=5), dict(tile_order=-1),
                 dict(lead=-1), dict(chunks=-1), dict(chunks=9), dict(wait_timeout_us=-5),
                 dict(trace_records=-1),
-                dict(trace_records=8)):  # records without a buffer
+                dict(trace_records=8),  # records without a buffer
+                dict(schedule=1), dict(schedule=-1)):  # moe_layer is persistent only
         assert lib.moe_layer(*args, opts(**bad), None) == INVALID, bad
-    # the W8A8 layer takes events only
+    # the W8A8 layer: schedule, events, and (persistent only) perturbation and
+    # wait bound; no tile-order or trace fields
     w = (FAKE,) * 9
     need8 = M.moe_layer_fp8_workspace_bytes(D)
-    for bad in (dict(dispatch=1), dict(tile_order=1), dict(chunks=2), dict(perturb_seed=3),
-                dict(wait_timeout_us=10)):
+    for bad in (dict(dispatch=1), dict(tile_order=1), dict(chunks=2), dict(lead=3),
+                dict(trace_records=4), dict(schedule=2), dict(schedule=-1),
+                dict(schedule=M.MOE_SCHEDULE_STAGED, trace_records=4, trace=0x10000),
+                dict(wait_timeout_us=-1),
+                dict(schedule=M.MOE_SCHEDULE_STAGED, perturb_seed=3),
+                dict(schedule=M.MOE_SCHEDULE_STAGED, wait_timeout_us=10)):
         assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need8,
                                  opts(**bad), None) == INVALID, bad
+    # valid options are accepted up to the point of touching the GPU: T = 0
+    # returns before any launch
+    for good in (dict(schedule=M.MOE_SCHEDULE_STAGED), dict(perturb_seed=3, wait_timeout_us=10)):
+        assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0,
+                                 opts(**good), None) == OK, good
     # the old process-wide setters are gone: options travel with the call
     for name in ("moe_set_tile_order", "moe_set_gather_dispatch", "moe_set_trace",
                  "moe_set_wait_timeout_us", "moe_timing_enable", "moe_timing_read"):

@@ -34,6 +34,8 @@ bounds fixed here before any run:
 moe_expert_ffn_fp8 and moe_layer_fp8 must equal the chained halves bit for bit.
 Inputs: the seeded workloads; the permutation is the oracle's own.
 """
+import zlib
+
 import numpy as np
 import pytest
 
@@ -83,6 +85,32 @@ def test_quantizer_bit_exact_on_edge_rows():
     q, s = M.moe_quantize_fp8(dev_bf16(xb))
     torch.cuda.synchronize()
     rq, rs = oracle.quantize_rows_e4m3(xb)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_bit_exact_on_every_bf16_value():
+    """Every finite bf16 value of magnitude at most 448, once each, in rows
+    whose maximum is 448 (scale 1, so each value is encoded as it is): the
+    codes of the whole input domain of the encoder, subnormal codes, ties and
+    signed zeros included, against the oracle bit for bit.  (A row with
+    another power-of-two scale feeds the encoder the same set of floats,
+    shifted exactly; magnitudes below 2^-10 all round to zero.)"""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = W.bf16_bits_to_f32(b)
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    vals = b[keep]
+    cols = 256
+    rows = -(-vals.size // (cols - 1))
+    grid = np.zeros((rows, cols - 1), np.uint16)
+    grid.reshape(-1)[:vals.size] = vals
+    xb = np.concatenate([np.full((rows, 1), W.f32_to_bf16_bits(np.float32([448.0]))[0],
+                                 np.uint16), grid], axis=1)
+    say(f"moe_quantize_fp8 every bf16 value: {vals.size} values in {rows} rows")
+    q, s = M.moe_quantize_fp8(dev_bf16(xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_rows_e4m3(xb)
+    assert np.all(rs == 1.0)
     assert np.array_equal(q.cpu().numpy(), rq)
     assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
 
@@ -200,10 +228,13 @@ LAYER_CASES.update({f"rand{i}": _random_fp8_case(i) for i in range(6)})
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
 def test_fp8_layer_matches_oracle_and_staged_calls(name):
-    """moe_layer_fp8 bit for bit against the staged C-ABI calls (moe_route,
-    moe_permute, moe_gate_up_fp8, moe_down_fp8, moe_combine); routing against
-    the oracle exactly; each GEMM and the combine against the oracle on the
-    GPU's own inputs, on the rows of sampled tokens."""
+    """moe_layer_fp8 (its persistent kernel, its staged schedule, and the
+    persistent kernel under a seeded adversarial schedule: producers delayed
+    before they publish, claims reversed) bit for bit against the staged C-ABI
+    calls (moe_route, moe_permute, moe_gate_up_fp8, moe_down_fp8,
+    moe_combine); routing against the oracle exactly; each GEMM and the
+    combine against the oracle on the GPU's own inputs, on the rows of sampled
+    tokens."""
     from gpu_util import TOL_GATE, sample_tokens
     cfg = LAYER_CASES[name].scaled(name=name)
     arrs = W.generate(cfg)
@@ -220,6 +251,19 @@ def test_fp8_layer_matches_oracle_and_staged_calls(name):
     out = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
                           topk_ids_out=ids, topk_w_out=gates)
     torch.cuda.synchronize()
+    say(f"moe_layer_fp8 staged schedule {name}")
+    out_st = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
+                             opts=M.layer_opts(schedule=M.MOE_SCHEDULE_STAGED))
+    seed = zlib.crc32(name.encode()) | 1
+    say(f"moe_layer_fp8 perturbed schedule {name} seed={seed}")
+    ws = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
+    out_pt = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt, ws=ws,
+                             opts=M.layer_opts(perturb_seed=seed))
+    torch.cuda.synchronize()
+    assert M.moe_device_status(D, ws) == 0, "a flag wait timed out"
+    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
+    assert torch.equal(out.view(bits), out_st.view(bits)), "persistent != staged schedule"
+    assert torch.equal(out.view(bits), out_pt.view(bits)), "perturbed != persistent"
     say(f"staged fp8 calls {name}")
     s_ids, s_gates, _ = M.moe_route(D, x, wr, bias)
     _, offsets, _, inv, xp = M.moe_permute(D, x, s_ids)
@@ -227,7 +271,6 @@ def test_fp8_layer_matches_oracle_and_staged_calls(name):
     y = M.moe_down_fp8(D, h, offsets, dq, ds)
     staged = M.moe_combine(D, y, inv, s_gates, out_dtype=dt)
     torch.cuda.synchronize()
-    bits = torch.int32 if dt == M.MOE_F32 else torch.int16
     assert torch.equal(out.view(bits), staged.view(bits)), "moe_layer_fp8 != staged calls"
     r_ids, r_g = oracle.route(arrs["x"], arrs["w_router"], cfg.k, bias=arrs["bias"])
     _, ro, rp, ri = oracle.permute(r_ids, cfg.E, cfg.e_lo, cfg.E_hi)
@@ -269,8 +312,10 @@ def test_fp8_layer_no_local_rows_gives_exact_zeros():
     (gq, gs), _ = _quant_both("w_gate", arrs["w_gate"])
     (uq, us), _ = _quant_both("w_up", arrs["w_up"])
     (dq, ds), _ = _quant_both("w_down", arrs["w_down"])
-    say("moe_layer_fp8 no local rows")
-    out = M.moe_layer_fp8(D, dev_bf16(arrs["x"]), dev_bf16(arrs["w_router"]), gq, gs, uq, us, dq,
-                          ds, bias=dev(bias), out_dtype=M.MOE_F32)
-    torch.cuda.synchronize()
-    assert torch.count_nonzero(out).item() == 0
+    for sched in (M.MOE_SCHEDULE_PERSISTENT, M.MOE_SCHEDULE_STAGED):
+        say(f"moe_layer_fp8 no local rows, schedule {sched}")
+        out = M.moe_layer_fp8(D, dev_bf16(arrs["x"]), dev_bf16(arrs["w_router"]), gq, gs, uq, us,
+                              dq, ds, bias=dev(bias), out_dtype=M.MOE_F32,
+                              opts=M.layer_opts(schedule=sched))
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(out).item() == 0
