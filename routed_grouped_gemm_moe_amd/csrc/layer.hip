@@ -211,10 +211,20 @@ __device__ __forceinline__ void publish(int32_t *p, bool add, int32_t *xmask, in
 // or atomics: once every wave's writes are performed the counter is raised
 // with a relaxed RMW -- no L2 write-back (which would flush every dirty line
 // of the XCD's L2, other workgroups' included).
-__device__ __forceinline__ void publish_wt(int32_t *p, bool add, int32_t *xmask, int xcd,
-                                           int sleeps) {
+//
+// With resv (a kind's queues), wave 0 also bumps this XCD's counter of that
+// kind before the wait, so the next claim's round trip overlaps the drain of
+// the tile's stores; returns lane 0's pre-op count in wave 0 (-1 otherwise),
+// for own_slot.
+__device__ __forceinline__ int publish_wt(int32_t *p, bool add, int32_t *xmask, int xcd,
+                                          int sleeps, int32_t *resv = nullptr) {
+    int old = -1;
+    if (resv && wave_id() == 0)
+        old = __hip_atomic_fetch_add(resv + xcd * QSTRIDE, lane_id() == 0 ? 1 : 0,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_vmcnt<0>();
     __syncthreads();
+    old = uniform(old);
     if (wave_id() == 0) {
         sleep_units(sleeps);
         const bool l0 = lane_id() == 0;
@@ -226,6 +236,18 @@ __device__ __forceinline__ void publish_wt(int32_t *p, bool add, int32_t *xmask,
         else
             __hip_atomic_store(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    return old;
+}
+
+// The tile of [0, n) in this XCD's range for a count taken by publish_wt's
+// reservation, or -1 once that range is drained (a count past its end is
+// harmless: every claim compares it with the range's length).
+__device__ __forceinline__ int own_slot(int old, int n, int xcd, bool rev) {
+    const int per = (n + NUM_XCD - 1) / NUM_XCD;
+    const int lo = xcd * per;
+    const int len = min(n, lo + per) - lo;
+    if (old < 0 || len <= 0 || old >= len) return -1;
+    return lo + (rev ? len - 1 - old : old);
 }
 
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
@@ -518,7 +540,8 @@ __device__ __forceinline__ void acquire_from(const int32_t *xmask, int xcd) {
         invalidate_l1();
 }
 
-__device__ __forceinline__ void quant_tile_f8(const LayerF8Args &a8, int Lq, int NT1, int xcd) {
+__device__ __forceinline__ int quant_tile_f8(const LayerF8Args &a8, int Lq, int NT1, int xcd,
+                                            int32_t *resv) {
     const LayerArgs &a = a8.b;
     const int64_t f = a.D.f;
     const int qpm = QB_PER_MT / a8.qrb;  // quantisation tiles per m-tile
@@ -569,12 +592,14 @@ __device__ __forceinline__ void quant_tile_f8(const LayerF8Args &a8, int Lq, int
             }
         }
     }
-    publish_wt(a8.q_done + mt, true, a8.q_xcd + mt, xcd, perturb_sleeps(a.perturb, 5, (uint32_t)Lq));
+    const int r = publish_wt(a8.q_done + mt, true, a8.q_xcd + mt, xcd,
+                             perturb_sleeps(a.perturb, 5, (uint32_t)Lq), resv);
     trace_tile(a, 5, Lq, xcd, t0);
+    return r;
 }
 
-__device__ __forceinline__ void down_tile_f8(const LayerF8Args &a8, int L, int MT, int NT2, int xcd,
-                                             char *lds) {
+__device__ __forceinline__ int down_tile_f8(const LayerF8Args &a8, int L, int MT, int NT2, int xcd,
+                                            char *lds, int32_t *resv) {
     const LayerArgs &a = a8.b;
     const int64_t d = a.D.d, f = a.D.f;
     const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
@@ -589,12 +614,13 @@ __device__ __forceinline__ void down_tile_f8(const LayerF8Args &a8, int L, int M
     gemm_tile_f8<F8_BF16, true>(a8.hq + (int64_t)(t.prow0 / 32) * (f / 32) * 1024, f / 32, t.rows,
                           (int)f, a8.sh + t.prow0, a8.wd + wo * f, nullptr, a8.sd + wo, nullptr,
                           a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
-    publish_wt(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
-               perturb_sleeps(a.perturb, 2, (uint32_t)L));
+    const int r = publish_wt(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
+                             perturb_sleeps(a.perturb, 2, (uint32_t)L), resv);
     if (wave_id() == 0)  // after the flag, so a reader that sees the full count sees every y row
         __hip_atomic_fetch_add(a.dn_done, lane_id() == 0 ? 1 : 0, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     trace_tile(a, 2, L, xcd, t0);
+    return r;
 }
 
 template <bool OUT_F32>
@@ -618,17 +644,21 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
     constexpr int KQ = 1 << 28, KD = 1 << 29, KC = 1 << 30;
     bool all_done = false;
     int phase = 1;  // 1 gate/up, 2 quantisation, 3 down, 4 combine
+    int resv = -1;  // wave 0: count reserved on this XCD's queue of the phase by the last publish
     for (;;) {
         if (wave_id() == 0) {
             int v;
             if (phase == 1) {
-                const int c = claim_tile(q1, n1, xcd, rev);
+                int c = own_slot(resv, n1, xcd, rev);
+                if (c < 0) c = claim_tile(q1, n1, xcd, rev);
                 v = c >= 0 ? c : -2;
             } else if (phase == 2) {
-                const int c = claim_tile(qq, nq, xcd, rev);
+                int c = own_slot(resv, nq, xcd, rev);
+                if (c < 0) c = claim_tile(qq, nq, xcd, rev);
                 v = c >= 0 ? (c | KQ) : -2;
             } else if (phase == 3) {
-                const int c = claim_tile(q2, n2, xcd, rev);
+                int c = own_slot(resv, n2, xcd, rev);
+                if (c < 0) c = claim_tile(q2, n2, xcd, rev);
                 v = c >= 0 ? (c | KD) : -2;
             } else {
                 const int c = claim_tile(q3, n3, xcd, rev);
@@ -636,6 +666,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
             }
             s_claim = v;  // every lane stores the same value
         }
+        resv = -1;
         __syncthreads();
         const int v = uniform(s_claim);
         __syncthreads();
@@ -647,9 +678,9 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
         if (v & KC) {
             combine_tile<OUT_F32>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
         } else if (v & KD) {
-            down_tile_f8(a8, v & ~KD, MT, NT2, xcd, lds);
+            resv = down_tile_f8(a8, v & ~KD, MT, NT2, xcd, lds, q2);
         } else if (v & KQ) {
-            quant_tile_f8(a8, v & ~KQ, NT1, xcd);
+            resv = quant_tile_f8(a8, v & ~KQ, NT1, xcd, qq);
         } else {
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             int mt, nt;
@@ -662,8 +693,8 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
                                        a8.wu + wo * d, a8.sg + wo, a8.su + wo,
                                        a8.h + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds,
                                        a8.hmax + t.row0);
-            publish_wt(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
-                       perturb_sleeps(a.perturb, 1, (uint32_t)v));
+            resv = publish_wt(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
+                              perturb_sleeps(a.perturb, 1, (uint32_t)v), q1);
             trace_tile(a, 1, v, xcd, t0);
         }
     }
