@@ -118,14 +118,17 @@ typedef enum {
                                  while chunk c+1's GEMMs do */
 } moe_tile_order;
 
-/* How moe_layer_fp8 runs its expert FFN and combine (moe_layer: persistent
- * only). */
+/* How a layer call runs its expert FFN and combine. */
 typedef enum {
-    MOE_SCHEDULE_PERSISTENT = 0, /* one persistent kernel: gate/up, h
-                                    quantisation, down and combine tiles in
-                                    dependency order with device-side flags
-                                    (default) */
-    MOE_SCHEDULE_STAGED = 1      /* one launch per stage (moe_layer_fp8 only);
+    MOE_SCHEDULE_AUTO = 0,       /* the library's choice (default): moe_layer runs
+                                    its persistent kernel; moe_layer_fp8 its
+                                    staged launches, which measured faster than
+                                    its persistent kernel on every workload shape
+                                    tried on MI355X */
+    MOE_SCHEDULE_PERSISTENT = 1, /* one persistent kernel: gate/up, (W8A8: h
+                                    quantisation,) down and combine tiles in
+                                    dependency order with device-side flags */
+    MOE_SCHEDULE_STAGED = 2      /* one launch per stage (moe_layer_fp8 only);
                                     the same tiles and arithmetic, so the same
                                     bits as the persistent kernel */
 } moe_schedule;
@@ -146,7 +149,7 @@ typedef struct {
                                 claimed in order).  The result bits are
                                 unchanged; only the timing is adversarial.
                                 Also moe_layer_fp8's persistent schedule. */
-    int32_t schedule;        /* moe_schedule; moe_layer requires 0 */
+    int32_t schedule;        /* moe_schedule; moe_layer: AUTO or PERSISTENT */
     int64_t wait_timeout_us; /* bound of each device-side flag
                                 wait; 0 = 2 s.  A wait that times out records
                                 MOE_ERR_DEVICE_TIMEOUT in the workspace and
@@ -322,14 +325,15 @@ moe_status moe_down_fp8(const moe_dims *dims, const void *h, const int32_t *offs
 /* moe_layer_fp8: the whole forward pass with the W8A8 FFN (X-Stage §4.3
  * fuses the MoE block into one kernel, §5.3 evaluates it in W8A8): route (as
  * moe_route), permute, the per-row E4M3 quantisation of the routed rows of
- * x, then by default (opts->schedule = MOE_SCHEDULE_PERSISTENT) one
- * persistent kernel whose workgroups claim gate/up tiles (E4M3 GEMM0 with
- * the SiLU-mul epilogue into bf16 h and each row's max |h|), quantisation
- * tiles (32 rows of h, once their m-tile's gate/up tiles are published),
- * down tiles (once their m-tile's rows are quantised) and combine tiles
- * (once the down tiles holding their rows are published) -- or, with
- * MOE_SCHEDULE_STAGED, moe_expert_ffn_fp8's launches and moe_combine.  Both
- * give the same bits.  One stream, one workspace, no host synchronisation.
+ * x, then either moe_expert_ffn_fp8's launches and moe_combine
+ * (MOE_SCHEDULE_STAGED, and the default MOE_SCHEDULE_AUTO) or, with
+ * MOE_SCHEDULE_PERSISTENT, one persistent kernel whose workgroups claim
+ * gate/up tiles (E4M3 GEMM0 with the SiLU-mul epilogue into bf16 h and each
+ * row's max |h|), quantisation tiles (rows of h, once their m-tile's
+ * gate/up tiles are published), down tiles (once their m-tile's rows are
+ * quantised) and combine tiles (once the down tiles holding their rows are
+ * published).  Both give the same bits.  One stream, one workspace, no host
+ * synchronisation.
  * Arguments as moe_layer, with the E4M3 weights and scales of
  * moe_expert_ffn_fp8 in place of the bf16 weights.  Requires f % 256 == 0.
  * Of opts: events[], schedule, and for the persistent schedule

@@ -38,8 +38,9 @@ MOE_BF16, MOE_F32 = 0, 1
 MOE_DISPATCH_PACKED, MOE_DISPATCH_GATHER = 0, 1
 MOE_ORDER_BY_KIND, MOE_ORDER_READY_DOWN, MOE_ORDER_LEAD, MOE_ORDER_COMBINE_FIRST = 0, 1, 2, 3
 MOE_ORDER_CHUNKED = 4
-MOE_SCHEDULE_PERSISTENT = 0
-MOE_SCHEDULE_STAGED = 1
+MOE_SCHEDULE_AUTO = 0
+MOE_SCHEDULE_PERSISTENT = 1
+MOE_SCHEDULE_STAGED = 2
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_TIMEOUT"}
 
@@ -465,9 +466,9 @@ def moe_layer_fp8_workspace_bytes(dims) -> int:
 def moe_layer_fp8(dims, x, w_router, wq_gate, s_gate, wq_up, s_up, wq_down, s_down, bias=None,
                   out=None, out_dtype: int = MOE_BF16, topk_ids_out=None, topk_w_out=None,
                   ws=None, opts: Optional[MoELayerOpts] = None, stream=None):
-    """Forward pass with the W8A8 expert FFN: one persistent kernel by default,
-    separate launches with opts.schedule = MOE_SCHEDULE_STAGED (same bits).
-    Returns out [T, d]."""
+    """Forward pass with the W8A8 expert FFN: separate launches by default
+    (MOE_SCHEDULE_AUTO / MOE_SCHEDULE_STAGED), one persistent kernel with
+    opts.schedule = MOE_SCHEDULE_PERSISTENT (same bits).  Returns out [T, d]."""
     import torch
     D = _dims(dims)
     dev = x.device

@@ -102,7 +102,8 @@ moe_status check_opts(const moe_layer_opts *o, bool fp8) {
     if (!o) return MOE_OK;
     if (fp8) {
         if (o->dispatch || o->tile_order || o->lead || o->chunks) return MOE_ERR_INVALID_ARG;
-        if (o->schedule == MOE_SCHEDULE_STAGED)  // separate launches: no tiles to perturb or trace
+        if (o->schedule == MOE_SCHEDULE_STAGED || o->schedule == MOE_SCHEDULE_AUTO)
+            // separate launches: no tiles to perturb, bound or trace
             return o->perturb_seed || o->wait_timeout_us || o->trace || o->trace_records
                        ? MOE_ERR_INVALID_ARG
                        : MOE_OK;
@@ -111,7 +112,8 @@ moe_status check_opts(const moe_layer_opts *o, bool fp8) {
             return MOE_ERR_INVALID_ARG;
         return MOE_OK;
     }
-    if (o->schedule != MOE_SCHEDULE_PERSISTENT) return MOE_ERR_INVALID_ARG;
+    if (o->schedule != MOE_SCHEDULE_AUTO && o->schedule != MOE_SCHEDULE_PERSISTENT)
+        return MOE_ERR_INVALID_ARG;
     if (o->dispatch != MOE_DISPATCH_PACKED && o->dispatch != MOE_DISPATCH_GATHER)
         return MOE_ERR_INVALID_ARG;
     if (o->tile_order < MOE_ORDER_BY_KIND || o->tile_order > MOE_ORDER_CHUNKED)

@@ -172,23 +172,27 @@ def test_layer_options_are_checked_per_call():
                 dict(lead=-1), dict(chunks=-1), dict(chunks=9), dict(wait_timeout_us=-5),
                 dict(trace_records=-1),
                 dict(trace_records=8),  # records without a buffer
-                dict(schedule=1), dict(schedule=-1)):  # moe_layer is persistent only
+                dict(schedule=M.MOE_SCHEDULE_STAGED), dict(schedule=3),
+                dict(schedule=-1)):  # moe_layer is persistent only
         assert lib.moe_layer(*args, opts(**bad), None) == INVALID, bad
     # the W8A8 layer: schedule, events, and (persistent only) perturbation and
     # wait bound; no tile-order or trace fields
     w = (FAKE,) * 9
     need8 = M.moe_layer_fp8_workspace_bytes(D)
     for bad in (dict(dispatch=1), dict(tile_order=1), dict(chunks=2), dict(lead=3),
-                dict(trace_records=4), dict(schedule=2), dict(schedule=-1),
+                dict(trace_records=4), dict(schedule=3), dict(schedule=-1),
+                dict(schedule=M.MOE_SCHEDULE_PERSISTENT, wait_timeout_us=-1),
+                # the staged launches (also the default) have no flags or tiles
+                dict(perturb_seed=3), dict(wait_timeout_us=10),
                 dict(schedule=M.MOE_SCHEDULE_STAGED, trace_records=4, trace=0x10000),
-                dict(wait_timeout_us=-1),
                 dict(schedule=M.MOE_SCHEDULE_STAGED, perturb_seed=3),
                 dict(schedule=M.MOE_SCHEDULE_STAGED, wait_timeout_us=10)):
         assert lib.moe_layer_fp8(C.byref(D), *w, FAKE, 0, None, None, FAKE_WS, need8,
                                  opts(**bad), None) == INVALID, bad
     # valid options are accepted up to the point of touching the GPU: T = 0
     # returns before any launch
-    for good in (dict(schedule=M.MOE_SCHEDULE_STAGED), dict(perturb_seed=3, wait_timeout_us=10)):
+    for good in (dict(schedule=M.MOE_SCHEDULE_STAGED),
+                 dict(schedule=M.MOE_SCHEDULE_PERSISTENT, perturb_seed=3, wait_timeout_us=10)):
         assert lib.moe_layer_fp8(C.byref(dims(T=0)), *((None,) * 10), 0, None, None, None, 0,
                                  opts(**good), None) == OK, good
     # the old process-wide setters are gone: options travel with the call

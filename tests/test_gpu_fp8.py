@@ -228,7 +228,7 @@ LAYER_CASES.update({f"rand{i}": _random_fp8_case(i) for i in range(6)})
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
 def test_fp8_layer_matches_oracle_and_staged_calls(name):
-    """moe_layer_fp8 (its persistent kernel, its staged schedule, and the
+    """moe_layer_fp8 (its default schedule, its persistent kernel, and the
     persistent kernel under a seeded adversarial schedule: producers delayed
     before they publish, claims reversed) bit for bit against the staged C-ABI
     calls (moe_route, moe_permute, moe_gate_up_fp8, moe_down_fp8,
@@ -251,19 +251,20 @@ def test_fp8_layer_matches_oracle_and_staged_calls(name):
     out = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
                           topk_ids_out=ids, topk_w_out=gates)
     torch.cuda.synchronize()
-    say(f"moe_layer_fp8 staged schedule {name}")
-    out_st = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
-                             opts=M.layer_opts(schedule=M.MOE_SCHEDULE_STAGED))
+    say(f"moe_layer_fp8 persistent kernel {name}")
+    P = M.MOE_SCHEDULE_PERSISTENT
+    out_ps = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt,
+                             opts=M.layer_opts(schedule=P))
     seed = zlib.crc32(name.encode()) | 1
-    say(f"moe_layer_fp8 perturbed schedule {name} seed={seed}")
+    say(f"moe_layer_fp8 persistent kernel, perturbed schedule {name} seed={seed}")
     ws = torch.empty(M.moe_layer_fp8_workspace_bytes(D), dtype=torch.uint8, device="cuda")
     out_pt = M.moe_layer_fp8(D, x, wr, gq, gs, uq, us, dq, ds, bias=bias, out_dtype=dt, ws=ws,
-                             opts=M.layer_opts(perturb_seed=seed))
+                             opts=M.layer_opts(schedule=P, perturb_seed=seed))
     torch.cuda.synchronize()
     assert M.moe_device_status(D, ws) == 0, "a flag wait timed out"
     bits = torch.int32 if dt == M.MOE_F32 else torch.int16
-    assert torch.equal(out.view(bits), out_st.view(bits)), "persistent != staged schedule"
-    assert torch.equal(out.view(bits), out_pt.view(bits)), "perturbed != persistent"
+    assert torch.equal(out.view(bits), out_ps.view(bits)), "persistent != staged schedule"
+    assert torch.equal(out.view(bits), out_pt.view(bits)), "perturbed != staged schedule"
     say(f"staged fp8 calls {name}")
     s_ids, s_gates, _ = M.moe_route(D, x, wr, bias)
     _, offsets, _, inv, xp = M.moe_permute(D, x, s_ids)
@@ -312,7 +313,7 @@ def test_fp8_layer_no_local_rows_gives_exact_zeros():
     (gq, gs), _ = _quant_both("w_gate", arrs["w_gate"])
     (uq, us), _ = _quant_both("w_up", arrs["w_up"])
     (dq, ds), _ = _quant_both("w_down", arrs["w_down"])
-    for sched in (M.MOE_SCHEDULE_PERSISTENT, M.MOE_SCHEDULE_STAGED):
+    for sched in (M.MOE_SCHEDULE_AUTO, M.MOE_SCHEDULE_PERSISTENT, M.MOE_SCHEDULE_STAGED):
         say(f"moe_layer_fp8 no local rows, schedule {sched}")
         out = M.moe_layer_fp8(D, dev_bf16(arrs["x"]), dev_bf16(arrs["w_router"]), gq, gs, uq, us,
                               dq, ds, bias=dev(bias), out_dtype=M.MOE_F32,
