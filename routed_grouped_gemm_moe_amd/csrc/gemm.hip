@@ -1,12 +1,12 @@
 // Standalone grouped expert GEMMs (the moe_expert_ffn path) over the packed
-// activation layout of gemm_pa.h, and the m-tile table builder.  The tile table is built on the device from
-// the segment offsets that the permute produced, so no count ever returns to
-// the host
-// (Weave §3: the workload is fixed once routing completes; §4: the routing
-// result reaches the kernel as a parameter).
+// activation layout of gemm_pa.h, with the eight-wave tile of gemm_w8.h, and
+// the m-tile table builder.  The tile table is built on the device from the
+// segment offsets that the permute produced, so no count ever returns to
+// the host (Weave §3: the workload is fixed once routing completes; §4: the
+// routing result reaches the kernel as a parameter).
 //
-// Launch shape: one workgroup per (m-tile, n-tile), grid sized for the worst
-// case and surplus workgroups exit at once.  Tiles follow the expert-aligned
+// Launch shape: one workgroup of W8_THREADS per (m-tile, n-tile), grid sized
+// for the worst case and surplus workgroups exit at once.  Tiles follow the expert-aligned
 // blocked order of gemm_tile.h (groups of up to 16 m-tiles of one expert swept
 // n-tile-major, so the tiles in flight share weight and activation tiles --
 // the same order as the persistent kernel, which fixes which down tiles are
@@ -15,7 +15,7 @@
 // dispatch), so the workgroups sharing a tile meet in one XCD's L2.
 #include <algorithm>
 
-#include "gemm_pa.h"
+#include "gemm_w8.h"
 
 namespace moe {
 namespace {
@@ -87,7 +87,7 @@ struct DownSplit {
 };
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(W8_THREADS, 1) void grouped_gemm_kernel(
     int64_t d, int64_t f, int64_t EL, const bf16_t *__restrict__ A,
     const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
     const int32_t *__restrict__ mtile_base, const bf16_t *__restrict__ W0,
@@ -108,14 +108,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_kernel(
     if (GATE_UP) {
         const bf16_t *wg = W0 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
         const bf16_t *wu = W1 + ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
-        gemm_tile_pa<PA_SILU_PACKED>(A + prb * (d / 16) * 512, d / 16, t.rows, (int)d, wg, wu, d,
+        gemm_tile_w8<PA_SILU_PACKED>(A + prb * (d / 16) * 512, d / 16, t.rows, (int)d, wg, wu, d,
                                      out + (prb * (f / 16) + nt * (BN_GU / 16)) * 512, f / 16, lds);
     } else {
         // a cut tile computes K part `part`, starting at k = part * f / S
         const int64_t Kp = part < 0 ? f : f / S, k0 = part < 0 ? 0 : part * Kp;
         const bf16_t *wd = W0 + ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
         const SplitCtl sc{ds.cnt + st, ds.part + (int64_t)st * (CUT_MAX * BM * BN_DN), part, S, 0};
-        gemm_tile_pa<PA_BF16>(A + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, wd,
+        gemm_tile_w8<PA_BF16>(A + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, wd,
                               nullptr, f, out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
                               part < 0 ? nullptr : &sc);
     }
@@ -132,10 +132,10 @@ hipError_t launch_gemm(const Dims &D, const bf16_t *A, const MTile *mtiles, cons
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     if (grid == 0) return hipSuccess;
     hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_kernel<GATE_UP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       GEMM_LDS_BYTES, s, D.d, D.f, D.EL(), A, mtiles, n_mtiles, mtile_base, W0, W1,
+    hipLaunchKernelGGL((grouped_gemm_kernel<GATE_UP>), dim3((unsigned)grid), dim3(W8_THREADS),
+                       W8_LDS_BYTES, s, D.d, D.f, D.EL(), A, mtiles, n_mtiles, mtile_base, W0, W1,
                        out, ds);
     return hipGetLastError();
 }

@@ -210,10 +210,20 @@ struct SplitCtl {
     int sleeps;   // schedule perturbation: s_sleep(127) count before arriving
 };
 
-// Float offset of accumulator vector (wave, i, j, v/4 = g) of lane `lane`:
-// every 16-byte store or load of a wave covers 1 KiB contiguously.
+// Wave grid of a tile of NT threads: 4 waves as 2 x 2 blocks of 128 x 128,
+// 8 waves as 2 x 4 blocks of 128 x 64.  Wave w's accumulator block (i, j)
+// starts at row tile_row0 + 32 i, column tile_col0 + 32 j.
+template <int NT>
+__device__ __forceinline__ int tile_row0(int w) { return (NT == 256 ? w >> 1 : w >> 2) * 128; }
+template <int NT>
+__device__ __forceinline__ int tile_col0(int w) { return NT == 256 ? (w & 1) * 128 : (w & 3) * 64; }
+
+// Float offset of accumulator vector (wave, i, j, v/4 = g) of lane `lane` in
+// an NI x NJ block grid per wave: every 16-byte store or load of a wave
+// covers 1 KiB contiguously.
+template <int NI, int NJ>
 __device__ __forceinline__ int split_slot(int wave, int i, int j, int g, int lane) {
-    return ((((wave * 4 + i) * 4 + j) * 4 + g) * 64 + lane) * 4;
+    return ((((wave * NI + i) * NJ + j) * 4 + g) * 64 + lane) * 4;
 }
 
 // y element (row r, column c) of a 256 x 256 bf16 tile staged in LDS: rows
@@ -227,19 +237,20 @@ __device__ __forceinline__ int y_stage_index(int r, int c) {
 // LDS must be free (the K loop ends with a barrier); the caller copies the
 // tile out.  WT: the partials go out with device-scope stores, so the
 // arrival needs no L2 write-back.
-template <bool WT>
-__device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitCtl &sp, int tid,
+template <bool WT, int NT = GEMM_THREADS, int NI = 4, int NJ = 4>
+__device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[NI][NJ], const SplitCtl &sp, int tid,
                                              int wave, int lane, char *lds) {
+    static_assert(NT / 64 * NI * NJ * 1024 == BM * BN_DN, "the waves' blocks cover the tile");
     float *mine = sp.part + sp.self * (BM * BN_DN);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4_t v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                    acc[i][j][4 * g + 3]};
-                float *dst = mine + split_slot(wave, i, j, g, lane);
+                float *dst = mine + split_slot<NI, NJ>(wave, i, j, g, lane);
                 if (WT) store16_wt(dst, __builtin_bit_cast(u32x4_t, v));
                 else *reinterpret_cast<f32x4_t *>(dst) = v;
             }
@@ -273,38 +284,38 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
     constexpr int PSTRIDE = BM * BN_DN * sizeof(float);  // bytes between partials
     bf16_t *st = reinterpret_cast<bf16_t *>(lds);
     auto put = [&](int idx, const float (&v)[4]) {
-        const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) & 3, i = (idx >> 10) & 3,
-                  w = idx >> 12;
-        const int r = (w >> 1) * 128 + i * 32 + 8 * g + 4 * (l >> 5);
-        const int c = (w & 1) * 128 + j * 32 + (l & 31);
+        const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) % NJ,
+                  i = ((idx >> 8) / NJ) % NI, w = idx / (NI * NJ * 256);
+        const int r = tile_row0<NT>(w) + i * 32 + 8 * g + 4 * (l >> 5);
+        const int c = tile_col0<NT>(w) + j * 32 + (l & 31);
 #pragma unroll
         for (int e = 0; e < 4; ++e) st[y_stage_index(r + e, c)] = f2bf(v[e]);
     };
     if (sp.nparts == 2) {
-        for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 8) {
+        for (int it = 0; it < (BM * BN_DN / 4) / NT; it += 8) {
             i32x4_t p[8][2];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
-                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * GEMM_THREADS + tid) * 16 + q * PSTRIDE,
+                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * NT + tid) * 16 + q * PSTRIDE,
                                                  0, PA_CPOL_SC1);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = __int_as_float(p[u][0][e]) + __int_as_float(p[u][1][e]);
-                put((it + u) * GEMM_THREADS + tid, v);
+                put((it + u) * NT + tid, v);
             }
         }
     } else {
-        for (int it = 0; it < (BM * BN_DN / 4) / GEMM_THREADS; it += 4) {
+        for (int it = 0; it < (BM * BN_DN / 4) / NT; it += 4) {
             i32x4_t p[4][4];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * GEMM_THREADS + tid) * 16 + q * PSTRIDE,
+                    p[u][q] = raw_buffer_load_v4(rs, ((it + u) * NT + tid) * 16 + q * PSTRIDE,
                                                  0, PA_CPOL_SC1);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -314,7 +325,7 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[4][4], const SplitC
                     v[e] = ((__int_as_float(p[u][0][e]) + __int_as_float(p[u][1][e])) +
                             __int_as_float(p[u][2][e])) +
                            __int_as_float(p[u][3][e]);
-                put((it + u) * GEMM_THREADS + tid, v);
+                put((it + u) * NT + tid, v);
             }
         }
     }

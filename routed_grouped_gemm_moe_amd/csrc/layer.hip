@@ -52,6 +52,7 @@
 // then invalid, but the kernel drains).
 #include "combine_tile.h"
 #include "gemm_f8.h"
+#include "gemm_w8.h"
 
 namespace moe {
 namespace {
@@ -276,6 +277,7 @@ __device__ __forceinline__ void trace_tile(const LayerArgs &a, int kind, int L, 
 
 // One down claim LS (a whole tile or a K part of a cut tile): wait until its
 // m-tile's gate/up tiles are published, GEMM1 into y, publish dn_flag.
+template <int NT>
 __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, int nsp, int S,
                                           int MT, int NT1, int NT2, int xcd, char *lds) {
     const Dims &D = a.D;
@@ -300,10 +302,15 @@ __device__ __forceinline__ void down_tile(const LayerArgs &a, int LS, int n2, in
     const int64_t wo = ((int64_t)t.e * d + (int64_t)nt * BN_DN) * f + k0;
     const SplitCtl sc{a.dn_cnt + st, a.dn_part + (int64_t)st * (CUT_MAX * BM * BN_DN), part,
                       S, perturb_sleeps(a.perturb, 4, (uint32_t)LS)};
-    const bool wrote = gemm_tile_pa<PA_BF16, true>(
-        a.h + (prb * (f / 16) + k0 / 16) * 512, f / 16, t.rows, (int)Kp, a.w_down + wo,
-        nullptr, f, a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds,
-        part < 0 ? nullptr : &sc);
+    const bf16_t *hA = a.h + (prb * (f / 16) + k0 / 16) * 512;
+    bf16_t *yo = a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN;
+    bool wrote;
+    if constexpr (NT == W8_THREADS)
+        wrote = gemm_tile_w8<PA_BF16, true>(hA, f / 16, t.rows, (int)Kp, a.w_down + wo, nullptr, f,
+                                            yo, d, lds, part < 0 ? nullptr : &sc);
+    else
+        wrote = gemm_tile_pa<PA_BF16, true>(hA, f / 16, t.rows, (int)Kp, a.w_down + wo, nullptr, f,
+                                            yo, d, lds, part < 0 ? nullptr : &sc);
     if (!wrote) {  // the last part to arrive writes the tile
         trace_tile(a, 4, LS, xcd, t0);
         return;
@@ -352,7 +359,7 @@ __device__ __forceinline__ int claim_ready_combine(const LayerArgs &a, int32_t *
 // One combine tile L (COMB_TOK tokens x up to COMB_CB column blocks of
 // BN_DN): every (token, slot) waits for the down tile holding its row --
 // unless every down tile has already been published -- then the gated sum.
-template <bool OUT_F32>
+template <bool OUT_F32, int NT>
 __device__ __forceinline__ void combine_tile(const LayerArgs &a, int L, int NTB, int NT2, int n2,
                                              int xcd, bool &all_done, char *lds) {
     const Dims &D = a.D;
@@ -363,7 +370,7 @@ __device__ __forceinline__ void combine_tile(const LayerArgs &a, int L, int NTB,
     if (!all_done)  // stays true once seen
         all_done = uniform(__hip_atomic_load(a.dn_done, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT)) >= n2;
-    for (int base = 0; !all_done && base < COMB_TOK * k; base += GEMM_THREADS) {  // uniform
+    for (int base = 0; !all_done && base < COMB_TOK * k; base += NT) {  // uniform
         const int i = base + (int)threadIdx.x;
         const int64_t t = (int64_t)tb * COMB_TOK + i / k;
         const int64_t j = i % k;
@@ -382,16 +389,30 @@ __device__ __forceinline__ void combine_tile(const LayerArgs &a, int L, int NTB,
                           a.status);
     }
     __syncthreads();
-    combine_tile_staged<OUT_F32, COMB_TOK, BN_DN / 8, GEMM_THREADS>(
+    combine_tile_staged<OUT_F32, COMB_TOK, BN_DN / 8, NT>(
         (int64_t)tb * COMB_TOK, D.T, (int64_t)nt0 * (BN_DN / 8), ncb, d, k, a.y, a.inv_perm,
         a.gates, a.out, lds);
     trace_tile(a, 3, L, xcd, t0);
 }
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
+// NT = W8_THREADS: the eight-wave GEMM tiles of gemm_w8.h (packed dispatch);
+// NT = GEMM_THREADS: the four-wave tiles (the gather-on-load dispatch, whose
+// gate/up tile gathers x rows through LDS).
+template <bool OUT_F32, int NT>
+__global__ __launch_bounds__(NT, 1) void layer_kernel(LayerArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ int s_claim;
+    // The claim broadcast slot.  The eight-wave tiles take all 160 KiB of LDS
+    // dynamically, so there it is the last int of that: between tiles no
+    // epilogue or combine tile reaches it, and a K loop starts with a barrier
+    // that every wave passes only after reading the claim.
+    int *s_claim_p;
+    if constexpr (NT == W8_THREADS) {
+        s_claim_p = reinterpret_cast<int *>(lds + W8_LDS_BYTES) - 1;
+    } else {
+        __shared__ int s_claim;
+        s_claim_p = &s_claim;
+    }
+    int &s_claim = *s_claim_p;
     const Dims &D = a.D;
     const int xcd = hw_xcd();
     const int MT = *a.n_mtiles;
@@ -474,11 +495,11 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
                 break;
             }
             if (v & COMB) {
-                combine_tile<OUT_F32>(a, v & ~COMB, NTB, NT2, n2, xcd, all_done, lds);
+                combine_tile<OUT_F32, NT>(a, v & ~COMB, NTB, NT2, n2, xcd, all_done, lds);
                 continue;
             }
             if (v & DOWN) {
-                down_tile(a, v & ~DOWN, n2, nsp, S, MT, NT1, NT2, xcd, lds);
+                down_tile<NT>(a, v & ~DOWN, n2, nsp, S, MT, NT1, NT2, xcd, lds);
                 continue;
             }
             const int L = v;
@@ -489,14 +510,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_kernel(LayerArgs a) {
             const int64_t wo = ((int64_t)t.e * f + (int64_t)nt * BN_GU) * d;
             const int64_t prb = t.prow0 / 32;  // first packed row block
             bf16_t *ho = a.h + (prb * (f / 16) + nt * (BN_GU / 16)) * 512;
-            if (a.gather)  // rows of x fetched through perm_src, both operands via LDS
+            if constexpr (NT == W8_THREADS)
+                gemm_tile_w8<PA_SILU_PACKED, true>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
+                                                   (int)d, a.w_gate + wo, a.w_up + wo, d, ho, f / 16,
+                                                   lds);
+            else  // rows of x fetched through perm_src, both operands via LDS
                 gemm_tile<EPI_SILU_PACKED>(a.x, d, 0, t.rows, a.w_gate + wo, a.w_up + wo, d, BN_GU,
                                            (int)d, ho, f / 16, 0, 0, lds, a.perm_src + t.row0,
                                            D.T);
-            else
-                gemm_tile_pa<PA_SILU_PACKED, true>(a.x_perm + prb * (d / 16) * 512, d / 16, t.rows,
-                                             (int)d, a.w_gate + wo, a.w_up + wo, d, ho, f / 16,
-                                             lds);
             // the gathered tile writes h with ordinary stores: a release
             if (a.gather)
                 publish(a.gu_done + mt, true, a.gu_xcd + mt, xcd,
@@ -676,7 +697,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
         }
         if (v < 0) break;
         if (v & KC) {
-            combine_tile<OUT_F32>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
+            combine_tile<OUT_F32, GEMM_THREADS>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
         } else if (v & KD) {
             resv = down_tile_f8(a8, v & ~KD, MT, NT2, xcd, lds, q2);
         } else if (v & KQ) {
@@ -931,14 +952,24 @@ int layer_grid_size() {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    for (const void *k : {(const void *)layer_kernel<false>, (const void *)layer_kernel<true>,
+    for (const void *k : {(const void *)layer_kernel<false, GEMM_THREADS>,
+                          (const void *)layer_kernel<true, GEMM_THREADS>,
                           (const void *)layer_f8_kernel<false>, (const void *)layer_f8_kernel<true>})
         if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) !=
             hipSuccess)
             return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)layer_kernel<false>,
+    for (const void *k : {(const void *)layer_kernel<false, W8_THREADS>,
+                          (const void *)layer_kernel<true, W8_THREADS>})
+        if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS_BYTES) !=
+            hipSuccess)
+            return 0;
+    // one workgroup per CU for either thread count (the LDS alone sees to it)
+    int occ8 = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)layer_kernel<false, GEMM_THREADS>,
                                                      GEMM_THREADS, GEMM_LDS_BYTES) != hipSuccess ||
-        occ < 1)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ8, (const void *)layer_kernel<false, W8_THREADS>,
+                                                     W8_THREADS, W8_LDS_BYTES) != hipSuccess ||
+        occ < 1 || occ8 != occ)
         occ = 1;
     cached = cus * occ;
     return cached;
@@ -966,11 +997,21 @@ hipError_t launch_layer_f8_persistent(const LayerF8Args &a, int grid, hipStream_
 }
 
 hipError_t launch_layer_persistent(const LayerArgs &a, int grid, hipStream_t s) {
-    if (a.out_f32)
-        hipLaunchKernelGGL(layer_kernel<true>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s, a);
-    else
-        hipLaunchKernelGGL(layer_kernel<false>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
-                           a);
+    if (a.gather) {
+        if (a.out_f32)
+            hipLaunchKernelGGL((layer_kernel<true, GEMM_THREADS>), dim3(grid), dim3(GEMM_THREADS),
+                               GEMM_LDS_BYTES, s, a);
+        else
+            hipLaunchKernelGGL((layer_kernel<false, GEMM_THREADS>), dim3(grid), dim3(GEMM_THREADS),
+                               GEMM_LDS_BYTES, s, a);
+    } else {
+        if (a.out_f32)
+            hipLaunchKernelGGL((layer_kernel<true, W8_THREADS>), dim3(grid), dim3(W8_THREADS),
+                               W8_LDS_BYTES, s, a);
+        else
+            hipLaunchKernelGGL((layer_kernel<false, W8_THREADS>), dim3(grid), dim3(W8_THREADS),
+                               W8_LDS_BYTES, s, a);
+    }
     return hipGetLastError();
 }
 
