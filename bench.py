@@ -23,6 +23,10 @@ Other modes:
   --mode ffn_fp8 / ffn_bf16 / layer_fp8
                      the staged W8A8 or bf16 expert FFN alone, or the W8A8 layer
                      (its default staged launches and its persistent kernel)
+  --mode mfma_rate   the sustained bf16 matrix-core rate of a loop of
+                     independent MFMAs on every CU, with zero and with
+                     random operands (the achievable share of the nominal
+                     peak under the chip's power limit)
   --summarize-trace DIR
                      per-kernel medians of the timed dispatches in the
                      rocprofv3 kernel trace (csv) under DIR, skipping the
@@ -266,6 +270,38 @@ def stage_probes(args, cfg, M, torch, D, x, wr, bias, n_rows, t_local):
                         f"{args.steps} calls after {args.warmup} warm-up"}
 
 
+def mfma_rate_mode(args) -> None:
+    """Sustained matrix-core rate (moe_probe_mfma_rate): one workgroup of 4
+    waves per CU, each wave 16 independent v_mfma_f32_32x32x16_bf16 per
+    iteration; median of `steps` timed launches after `warmup`, for zero and
+    for pseudo-random operands."""
+    import torch
+    import routed_grouped_gemm_moe_amd as M
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    flops = cus * 4 * iters * 16 * 32768.0
+    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, seed in (("zero_operands", 0), ("random_operands", 12345)):
+        for _ in range(max(args.warmup, 1)):
+            M.moe_probe_mfma_rate(cus, iters, seed, sink)
+        ms = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            M.moe_probe_mfma_rate(cus, iters, seed, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = median(ms)
+        res[name] = {"ms_median": round(t, 4), "tflops": round(flops / (t * 1e-3) / 1e12, 1),
+                     "frac_of_peak": round(flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    print(json.dumps({"mode": "mfma_rate", "metric": "sustained bf16 MFMA rate, 1 GPU",
+                      "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "cus": cus,
+                      "flops_per_launch": flops, "steps": args.steps, "warmup": args.warmup,
+                      **res}), flush=True)
+
+
 def ffn_mode(args, cfg, M, torch, D, x, wr, wg, wu, wd, bias) -> None:
     """Time the staged expert FFN (fp8 or bf16) on the workload's routed rows."""
     ids, _, _ = M.moe_route(D, x, wr, bias)
@@ -357,7 +393,7 @@ def main() -> None:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--mode", default="layer",
-                    choices=["layer", "copy", "ffn_fp8", "ffn_bf16", "layer_fp8"])
+                    choices=["layer", "copy", "ffn_fp8", "ffn_bf16", "layer_fp8", "mfma_rate"])
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cpu-per-config", action="store_true",
@@ -392,6 +428,9 @@ def main() -> None:
 
     if args.mode == "copy":
         copy_mode(args)
+        return
+    if args.mode == "mfma_rate":
+        mfma_rate_mode(args)
         return
 
     import moe_workloads as W

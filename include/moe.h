@@ -392,6 +392,18 @@ moe_status moe_layer(const moe_dims *dims, const void *x, const void *w_router, 
 moe_status moe_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
                           const float *c, float *d, void *stream);
 
+/* ---- Matrix-core rate probe (measurement aid).  `workgroups` workgroups of
+ * 256 threads; each of their waves issues iters x 16 independent
+ * v_mfma_f32_32x32x16_bf16 on operands fixed per lane: zero (seed 0) or
+ * pseudo-random values in [-1, 1) drawn from the seed.  Work =
+ * workgroups * 4 * iters * 16 * 32768 FLOP; the caller times it (the sustained
+ * rate with real data is below the nominal peak where the power limit lowers
+ * the clock).  sink: device f32 [workgroups * 256], 16-byte aligned, written
+ * with each thread's sum.  0 <= workgroups <= 65536, 1 <= iters <= 2^20;
+ * MOE_ERR_INVALID_ARG otherwise. */
+moe_status moe_probe_mfma_rate(int64_t workgroups, int iters, uint32_t seed, float *sink,
+                               void *stream);
+
 /* Synchronises `stream`, then reads the device status word at offset 0 of a
  * workspace last used by moe_layer or moe_expert_ffn (MOE_OK, or
  * MOE_ERR_DEVICE_TIMEOUT if a flag wait gave up).  ws_bytes must be >= 256. */

@@ -19,7 +19,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "MoEDims", "lib_path", "load", "exported_abi_names", "header_abi_names",
-    "moe_route", "moe_route_bounds", "moe_probe_mfma", "moe_gate_up_fp8", "moe_down_fp8",
+    "moe_route", "moe_route_bounds", "moe_probe_mfma", "moe_probe_mfma_rate", "moe_gate_up_fp8",
+    "moe_down_fp8",
     "moe_permute", "moe_permute_noalloc", "moe_expert_ffn", "moe_combine", "moe_layer",
     "moe_route_workspace_bytes",
     "moe_permute_workspace_bytes", "moe_expert_ffn_workspace_bytes",
@@ -121,6 +122,7 @@ def load():
         "moe_route": ([dp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_route_bounds": ([dp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_probe_mfma": ([i32, i64, i32, vp, vp, vp, vp, vp], i32),
+        "moe_probe_mfma_rate": ([i64, i32, C.c_uint32, vp, vp], i32),
         "moe_gate_up_fp8": ([dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_down_fp8": ([dp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_permute_workspace_bytes": ([dp], sz),
@@ -293,6 +295,18 @@ def moe_probe_mfma(kind: int, a, b, c, d=None, stream=None):
     _check(load().moe_probe_mfma(int(kind), n, steps, _ptr(a), _ptr(b), _ptr(c), _ptr(d),
                                  _stream(stream)), "moe_probe_mfma")
     return d
+
+
+def moe_probe_mfma_rate(workgroups: int, iters: int, seed: int, sink=None, stream=None):
+    """Matrix-core rate probe: `workgroups` x 4 waves, each iters x 16
+    independent bf16 MFMAs on zero (seed 0) or pseudo-random operands; the
+    caller times it.  Returns the sink tensor (f32 [workgroups * 256])."""
+    import torch
+    if sink is None:
+        sink = torch.empty(max(int(workgroups), 1) * 256, dtype=torch.float32, device="cuda")
+    _check(load().moe_probe_mfma_rate(int(workgroups), int(iters), int(seed) & 0xFFFFFFFF,
+                                      _ptr(sink), _stream(stream)), "moe_probe_mfma_rate")
+    return sink
 
 
 def moe_permute(dims, x, topk_ids, counts=None, offsets=None, perm_src=None, inv_perm=None,

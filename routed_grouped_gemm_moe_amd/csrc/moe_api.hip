@@ -220,6 +220,15 @@ moe_status moe_probe_mfma(int kind, int64_t n, int steps, const void *a, const v
     return hip_status(launch_probe_mfma(kind, n, steps, a, b, c, d, (hipStream_t)stream));
 }
 
+moe_status moe_probe_mfma_rate(int64_t workgroups, int iters, uint32_t seed, float *sink,
+                               void *stream) {
+    if (workgroups < 0 || workgroups > 65536 || iters < 1 || iters > (1 << 20))
+        return MOE_ERR_INVALID_ARG;
+    if (workgroups == 0) return MOE_OK;
+    if (!sink || !aligned16(sink)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_probe_mfma_rate(workgroups, iters, seed, sink, (hipStream_t)stream));
+}
+
 size_t moe_permute_workspace_bytes(const moe_dims *dims) {
     Dims D;
     if (check_dims(dims, &D) != MOE_OK) return 0;

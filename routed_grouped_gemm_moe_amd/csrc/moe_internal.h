@@ -182,6 +182,8 @@ hipError_t launch_route_bounds(const Dims &D, const bf16_t *x, const bf16_t *w_r
                                hipStream_t s);
 
 // Matrix-core probe (probe.hip): kind 0 bf16 32x32x16, kind 1 E4M3 32x32x64.
+hipError_t launch_probe_mfma_rate(int64_t workgroups, int iters, uint32_t seed, float *sink,
+                                  hipStream_t s);
 hipError_t launch_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
                              const float *c, float *d, hipStream_t s);
 

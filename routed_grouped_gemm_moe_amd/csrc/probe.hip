@@ -1,4 +1,4 @@
-// Matrix-core accumulation probe (a measurement aid).  Runs chains of MFMA
+// Matrix-core probes (measurement aids).  The accumulation probe  Runs chains of MFMA
 // instructions on caller-given operands and returns their float32 results, so
 // that the rounding behaviour of gfx950's matrix cores can be measured
 // against exact sums on the host.  Two correctness arguments of this library
@@ -63,7 +63,53 @@ __global__ __launch_bounds__(64) void probe_f8_kernel(int steps, const uint8_t *
     for (int v = 0; v < 16; ++v) d[i * 1024 + acc_row(v, h) * 32 + r] = acc[v];
 }
 
+// Matrix-core rate probe: every wave issues iters x 16 independent
+// v_mfma_f32_32x32x16_bf16 (16 accumulators), operands fixed per lane --
+// zero (seed 0) or pseudo-random values in [-1, 1) from the seed -- so the
+// sustained rate can be compared with the nominal peak: with real data the
+// chip's power limit lowers the clock.  The sums go to sink so the work
+// stays live.
+__global__ __launch_bounds__(256) void probe_rate_kernel(int iters, uint32_t seed,
+                                                         float *__restrict__ sink) {
+    const int tid = threadIdx.x;
+    bf16x8_t a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t h = seed * 0x9E3779B9u ^ ((uint32_t)tid * 8u + (uint32_t)j) * 0x85EBCA6Bu;
+        h ^= h >> 15;
+        h *= 0x2C1B3C6Du;
+        h ^= h >> 12;
+        const float va = seed ? (float)(h & 0xFFFF) / 32768.0f - 1.0f : 0.0f;
+        const float vb = seed ? (float)(h >> 16) / 32768.0f - 1.0f : 0.0f;
+        a[j] = __builtin_bit_cast(__bf16, f2bf(va));
+        b[j] = __builtin_bit_cast(__bf16, f2bf(vb));
+    }
+    f32x16_t acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += acc[i][v];
+    sink[(int64_t)blockIdx.x * 256 + tid] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_probe_mfma_rate(int64_t workgroups, int iters, uint32_t seed, float *sink,
+                                  hipStream_t s) {
+    if (workgroups == 0) return hipSuccess;
+    hipLaunchKernelGGL(probe_rate_kernel, dim3((unsigned)workgroups), dim3(256), 0, s, iters, seed,
+                       sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma(int kind, int64_t n, int steps, const void *a, const void *b,
                              const float *c, float *d, hipStream_t s) {

@@ -212,6 +212,14 @@ def test_verification_entry_points_check_arguments():
     assert lib.moe_probe_mfma(0, 1, 1, C.c_void_p(0x10002), FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_probe_mfma(0, 1, 1, None, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_probe_mfma(0, 0, 1, None, None, None, None, None) == OK
+    # matrix-core rate probe: counts, alignment
+    assert lib.moe_probe_mfma_rate(-1, 1, 0, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma_rate(65537, 1, 0, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma_rate(1, 0, 0, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma_rate(1, (1 << 20) + 1, 0, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma_rate(1, 1, 0, None, None) == INVALID
+    assert lib.moe_probe_mfma_rate(1, 1, 0, C.c_void_p(0x10002), None) == INVALID
+    assert lib.moe_probe_mfma_rate(0, 1, 0, None, None) == OK
     # router bounds: only where the fast path applies (E > 16), workspace required
     D = dims(E=8)
     assert lib.moe_route_bounds(C.byref(D), FAKE, FAKE, None, FAKE, FAKE, FAKE_WS, 1 << 40,
