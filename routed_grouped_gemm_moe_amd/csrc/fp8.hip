@@ -8,7 +8,7 @@
 // with 4 exponent bits (bias 7) and 3 mantissa bits, no infinities.
 #include <algorithm>
 
-#include "gemm_f8.h"
+#include "gemm_f8w8.h"
 
 namespace moe {
 namespace {
@@ -119,7 +119,7 @@ __device__ __forceinline__ int xcd_tile_f8(int n) {
 // packed h codes (K = f), W0 = down codes [E_loc][d][f], out = y rows
 // [cap][d].
 template <bool GATE_UP>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
+__global__ __launch_bounds__(W8_THREADS, 1) void grouped_gemm_f8_kernel(
     int64_t d, int64_t f, int64_t EL, const uint8_t *__restrict__ A, const float *__restrict__ sa,
     const MTile *__restrict__ mtiles, const int32_t *__restrict__ n_mtiles,
     const int32_t *__restrict__ mtile_base,
@@ -136,13 +136,13 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void grouped_gemm_f8_kernel(
     const int64_t prb = t.prow0 / 32;
     if (GATE_UP) {
         const int64_t wo = (int64_t)t.e * f + (int64_t)nt * BN_GU;
-        gemm_tile_f8<F8_SILU_ROWS>(A + prb * (d / 32) * 1024, d / 32, t.rows, (int)d, sa + t.prow0,
+        gemm_tile_f8w8<F8_SILU_ROWS>(A + prb * (d / 32) * 1024, d / 32, t.rows, (int)d, sa + t.prow0,
                                    W0 + wo * d, W1 + wo * d, s0 + wo, s1 + wo,
                                    out + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds,
                                    rowmax + t.row0);
     } else {
         const int64_t wo = (int64_t)t.e * d + (int64_t)nt * BN_DN;
-        gemm_tile_f8<F8_BF16>(A + prb * (f / 32) * 1024, f / 32, t.rows, (int)f, sa + t.prow0,
+        gemm_tile_f8w8<F8_BF16>(A + prb * (f / 32) * 1024, f / 32, t.rows, (int)f, sa + t.prow0,
                               W0 + wo * f, nullptr, s0 + wo, nullptr,
                               out + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
     }
@@ -159,10 +159,10 @@ hipError_t launch_gemm_f8(const Dims &D, const uint8_t *A, const float *sa, cons
     grid = (grid + NUM_XCD - 1) / NUM_XCD * NUM_XCD;
     if (grid == 0) return hipSuccess;
     hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_f8_kernel<GATE_UP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, PA_LDS_BYTES);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((grouped_gemm_f8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(GEMM_THREADS),
-                       PA_LDS_BYTES, s, D.d, D.f, D.EL(), A, sa, mtiles, n_mtiles, mtile_base, W0,
+    hipLaunchKernelGGL((grouped_gemm_f8_kernel<GATE_UP>), dim3((unsigned)grid), dim3(W8_THREADS),
+                       W8_LDS_BYTES, s, D.d, D.f, D.EL(), A, sa, mtiles, n_mtiles, mtile_base, W0,
                        s0, W1, s1, out,
                        rowmax);
     return hipGetLastError();
