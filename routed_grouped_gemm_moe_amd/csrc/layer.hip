@@ -52,7 +52,7 @@
 // then invalid, but the kernel drains).
 #include "combine_tile.h"
 #include "gemm_f8.h"
-#include "gemm_w8.h"
+#include "gemm_f8w8.h"
 
 namespace moe {
 namespace {
@@ -561,6 +561,7 @@ __device__ __forceinline__ void acquire_from(const int32_t *xmask, int xcd) {
         invalidate_l1();
 }
 
+template <int NT>
 __device__ __forceinline__ int quant_tile_f8(const LayerF8Args &a8, int Lq, int NT1, int xcd,
                                             int32_t *resv) {
     const LayerArgs &a = a8.b;
@@ -592,7 +593,7 @@ __device__ __forceinline__ int quant_tile_f8(const LayerF8Args &a8, int Lq, int 
             reinterpret_cast<const u32x4_t *>(a8.h + row * f + (lane >> 5) * 16);
         u32x4_t *o = reinterpret_cast<u32x4_t *>(a8.hq + ((int64_t)t.prow0 / 32 + rb) * (f / 32) * 1024);
         // fragments kk = wave + 4i; QB of them in flight per lane
-        constexpr int QB = 4, NW = GEMM_THREADS / 64;
+        constexpr int QB = 4, NW = NT / 64;
         const int64_t nkk = f / 32;
         for (int64_t kk0 = wave; kk0 < nkk; kk0 += NW * QB) {
             u32x4_t raw[QB][2];
@@ -621,6 +622,7 @@ __device__ __forceinline__ int quant_tile_f8(const LayerF8Args &a8, int Lq, int 
 
 __device__ __forceinline__ int down_tile_f8(const LayerF8Args &a8, int L, int MT, int NT2, int xcd,
                                             char *lds, int32_t *resv) {
+    // (eight-wave tile: the W8A8 persistent kernel runs W8_THREADS threads)
     const LayerArgs &a = a8.b;
     const int64_t d = a.D.d, f = a.D.f;
     const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
@@ -632,9 +634,10 @@ __device__ __forceinline__ int down_tile_f8(const LayerF8Args &a8, int L, int MT
     __syncthreads();
     acquire_from(a8.q_xcd + mt, xcd);
     const int64_t wo = (int64_t)t.e * d + (int64_t)nt * BN_DN;
-    gemm_tile_f8<F8_BF16, true>(a8.hq + (int64_t)(t.prow0 / 32) * (f / 32) * 1024, f / 32, t.rows,
-                          (int)f, a8.sh + t.prow0, a8.wd + wo * f, nullptr, a8.sd + wo, nullptr,
-                          a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
+    gemm_tile_f8w8<F8_BF16, true>(a8.hq + (int64_t)(t.prow0 / 32) * (f / 32) * 1024, f / 32,
+                                  t.rows, (int)f, a8.sh + t.prow0, a8.wd + wo * f, nullptr,
+                                  a8.sd + wo, nullptr,
+                                  a.y + (int64_t)t.row0 * d + (int64_t)nt * BN_DN, d, lds);
     const int r = publish_wt(a.dn_flag + (int64_t)mt * NT2 + nt, false, nullptr, xcd,
                              perturb_sleeps(a.perturb, 2, (uint32_t)L), resv);
     if (wave_id() == 0)  // after the flag, so a reader that sees the full count sees every y row
@@ -645,9 +648,10 @@ __device__ __forceinline__ int down_tile_f8(const LayerF8Args &a8, int L, int MT
 }
 
 template <bool OUT_F32>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a8) {
+__global__ __launch_bounds__(W8_THREADS, 1) void layer_f8_kernel(LayerF8Args a8) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    __shared__ int s_claim;
+    // claim broadcast slot: the last int of the dynamic LDS, as in layer_kernel
+    int &s_claim = *(reinterpret_cast<int *>(lds + W8_LDS_BYTES) - 1);
     const LayerArgs &a = a8.b;
     const Dims &D = a.D;
     const int xcd = hw_xcd();
@@ -697,19 +701,19 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void layer_f8_kernel(LayerF8Args a
         }
         if (v < 0) break;
         if (v & KC) {
-            combine_tile<OUT_F32, GEMM_THREADS>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
+            combine_tile<OUT_F32, W8_THREADS>(a, v & ~KC, NTB, NT2, n2, xcd, all_done, lds);
         } else if (v & KD) {
             resv = down_tile_f8(a8, v & ~KD, MT, NT2, xcd, lds, q2);
         } else if (v & KQ) {
-            resv = quant_tile_f8(a8, v & ~KQ, NT1, xcd, qq);
+            resv = quant_tile_f8<W8_THREADS>(a8, v & ~KQ, NT1, xcd, qq);
         } else {
             const int64_t t0 = a.trace ? (int64_t)wall_clock64() : 0;
             int mt, nt;
             expert_tile(v, MT, NT1, (int)D.EL(), a.mtiles, a.mtile_base, &mt, &nt);
             const MTile t = a.mtiles[mt];
             const int64_t wo = (int64_t)t.e * f + (int64_t)nt * BN_GU;
-            gemm_tile_f8<F8_SILU_ROWS, true>(a8.xq + (int64_t)(t.prow0 / 32) * (d / 32) * 1024,
-                                             d / 32,
+            gemm_tile_f8w8<F8_SILU_ROWS, true>(a8.xq + (int64_t)(t.prow0 / 32) * (d / 32) * 1024,
+                                               d / 32,
                                        t.rows, (int)d, a8.sx + t.prow0, a8.wg + wo * d,
                                        a8.wu + wo * d, a8.sg + wo, a8.su + wo,
                                        a8.h + (int64_t)t.row0 * f + (int64_t)nt * BN_GU, f, lds,
@@ -953,13 +957,13 @@ int layer_grid_size() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     for (const void *k : {(const void *)layer_kernel<false, GEMM_THREADS>,
-                          (const void *)layer_kernel<true, GEMM_THREADS>,
-                          (const void *)layer_f8_kernel<false>, (const void *)layer_f8_kernel<true>})
+                          (const void *)layer_kernel<true, GEMM_THREADS>})
         if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS_BYTES) !=
             hipSuccess)
             return 0;
     for (const void *k : {(const void *)layer_kernel<false, W8_THREADS>,
-                          (const void *)layer_kernel<true, W8_THREADS>})
+                          (const void *)layer_kernel<true, W8_THREADS>,
+                          (const void *)layer_f8_kernel<false>, (const void *)layer_f8_kernel<true>})
         if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, W8_LDS_BYTES) !=
             hipSuccess)
             return 0;
@@ -988,10 +992,10 @@ int64_t wall_clock_hz() {
 
 hipError_t launch_layer_f8_persistent(const LayerF8Args &a, int grid, hipStream_t s) {
     if (a.b.out_f32)
-        hipLaunchKernelGGL(layer_f8_kernel<true>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
+        hipLaunchKernelGGL(layer_f8_kernel<true>, dim3(grid), dim3(W8_THREADS), W8_LDS_BYTES, s,
                            a);
     else
-        hipLaunchKernelGGL(layer_f8_kernel<false>, dim3(grid), dim3(GEMM_THREADS), GEMM_LDS_BYTES, s,
+        hipLaunchKernelGGL(layer_f8_kernel<false>, dim3(grid), dim3(W8_THREADS), W8_LDS_BYTES, s,
                            a);
     return hipGetLastError();
 }
