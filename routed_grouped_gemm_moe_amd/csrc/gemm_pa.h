@@ -420,7 +420,7 @@ __device__ __forceinline__ bool gemm_tile_pa(const bf16_t *__restrict__ Ap, int6
                     const int r32 = 8 * (v >> 2) + 4 * half + (v & 3);
                     const float g = acc[i][j][v];
                     const float u = acc[i][j + 2][v];
-                    st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g / (1.0f + __expf(-g)) * u);
+                    st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
                 }
             }
         __syncthreads();

@@ -281,7 +281,7 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
                     const int r32 = 8 * (v >> 2) + 4 * khalf + (v & 3);
                     const float g = acc[i][j][v];
                     const float u = acc[i][j + 2][v];
-                    st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g / (1.0f + __expf(-g)) * u);
+                    st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
                 }
             }
         __syncthreads();
@@ -307,7 +307,7 @@ __device__ __forceinline__ void gemm_tile(const bf16_t *__restrict__ A, int64_t 
                 for (int j = 0; j < 2; ++j) {
                     const float g = acc[i][j][v];
                     const float u = acc[i][j + 2][v];
-                    const float h = g / (1.0f + __expf(-g)) * u;
+                    const float h = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
                     o[wn * 64 + j * 32 + l32] = f2bf(h);
                 }
             } else if (EPI == EPI_BF16) {
