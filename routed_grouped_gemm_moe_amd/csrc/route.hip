@@ -896,30 +896,48 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // exact logits of the candidates, four at a time: lane = (u, chunk c)
+    // exact logits of the candidates, up to sixteen per pass: lane = (group
+    // g, chunk c) runs the chunk-c chains of the pass's candidates g, g + 4,
+    // g + 8, g + 12, so each staged x element is widened once for all of
+    // them; every chain is the defined sequential order over its chunk, and
+    // the 16 chunk sums of a candidate meet in the balanced tree
     const int c = lane & 15;
-    const int u = lane >> 4;
+    const int g = lane >> 4;
     const char *xc = xs + c * cbs;
-    for (int b = 0; b < ns; b += 4) {
-        const int ci = b + u;
-        const int e = cand[ci < ns ? ci : b];
-        const u32x4_t *wp = reinterpret_cast<const u32x4_t *>(wt + (int64_t)e * d) + c;
-        float acc = 0.0f;
-        constexpr int PG = 8;   // vectors per prefetch group
-        u32x4_t wa[PG], wb[PG];
-        auto load = [&](u32x4_t (&r)[PG], int64_t i0) {
+    for (int b = 0; b < ns; b += 16) {
+        const int nj = min(4, (ns - b + 3) >> 2);  // candidate slots per lane in use (uniform)
+        const u32x4_t *wp[4];
 #pragma unroll
-            for (int q = 0; q < PG; ++q)
-                r[q] = (i0 + q < ppc) ? wp[(i0 + q) * 16] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j) {
+            const int ci = b + g + 4 * j;
+            const int e = cand[ci < ns ? ci : b];
+            wp[j] = reinterpret_cast<const u32x4_t *>(wt + (int64_t)e * d) + c;
+        }
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        constexpr int PG = 2;  // vectors per candidate and prefetch group
+        u32x4_t wa[4][PG], wb[4][PG];
+        auto load = [&](u32x4_t (&r)[4][PG], int64_t i0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j < nj)
+#pragma unroll
+                    for (int q = 0; q < PG; ++q)
+                        r[j][q] = (i0 + q < ppc) ? wp[j][(i0 + q) * 16] : u32x4_t{0u, 0u, 0u, 0u};
         };
-        auto compute = [&](const u32x4_t (&r)[PG], int64_t i0) {
+        auto compute = [&](const u32x4_t (&r)[4][PG], int64_t i0) {
 #pragma unroll
             for (int q = 0; q < PG; ++q) {
                 if (i0 + q >= ppc) break;
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xc + (i0 + q) * 16);
+                float xf[8];
 #pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    acc = __builtin_fmaf(bf16x8_elem(xv, h), bf16x8_elem(r[q], h), acc);
+                for (int h = 0; h < 8; ++h) xf[h] = bf16x8_elem(xv, h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j < nj)
+#pragma unroll
+                        for (int h = 0; h < 8; ++h)
+                            acc[j] = __builtin_fmaf(xf[h], bf16x8_elem(r[j][q], h), acc[j]);
             }
         };
         load(wa, 0);
@@ -930,11 +948,15 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
             if (i0 + PG < ppc) compute(wb, i0 + PG);
         }
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) acc = acc + __shfl_xor(acc, m, 64);
-        if (c == 0 && ci < ns) {
-            float l = acc;
-            if (bias) l = l + bias[e];
-            exact[ci] = l;
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) acc[j] = acc[j] + __shfl_xor(acc[j], m, 64);
+            const int ci = b + g + 4 * j;
+            if (c == 0 && j < nj && ci < ns) {
+                float l = acc[j];
+                if (bias) l = l + bias[cand[ci]];
+                exact[ci] = l;
+            }
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
