@@ -62,7 +62,7 @@ __device__ __forceinline__ void combine_vec(int64_t t, int64_t v, int64_t d, int
         u32x4_t r;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            r[q] = (uint32_t)f2bf(acc[2 * q]) | ((uint32_t)f2bf(acc[2 * q + 1]) << 16);
+            r[q] = pk_bf16(acc[2 * q], acc[2 * q + 1]);
         reinterpret_cast<u32x4_t *>(reinterpret_cast<bf16_t *>(out) + t * d)[v] = r;
     }
 }
@@ -169,7 +169,7 @@ __device__ __forceinline__ void combine_tile_staged(int64_t t0, int64_t T, int64
             u32x4_t r;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                r[q] = (uint32_t)f2bf(acc[n][2 * q]) | ((uint32_t)f2bf(acc[n][2 * q + 1]) << 16);
+                r[q] = pk_bf16(acc[n][2 * q], acc[n][2 * q + 1]);
             reinterpret_cast<u32x4_t *>(reinterpret_cast<bf16_t *>(out) + t * d)[v] = r;
         }
     }

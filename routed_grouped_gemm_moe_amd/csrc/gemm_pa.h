@@ -227,17 +227,21 @@ __device__ __forceinline__ int split_slot(int wave, int i, int j, int g, int lan
 }
 
 // y element (row r, column c) of a 256 x 256 bf16 tile staged in LDS: rows
-// of 256, 16-byte chunk index xor-ed with r & 7.
+// of 256, 16-byte chunk index xor-ed with r & RM (7 for tiles that write one
+// element per lane along a row, 31 for tiles that write four columns of 32
+// consecutive rows per instruction).
+template <int RM = 7>
 __device__ __forceinline__ int y_stage_index(int r, int c) {
-    return r * 256 + (((c >> 3) ^ (r & 7)) << 3) + (c & 7);
+    return r * 256 + (((c >> 3) ^ (r & RM)) << 3) + (c & 7);
 }
 
 // Returns false in all but the last-arriving workgroup.  In the last, the
-// bf16 tile of the part-ordered sum is left in LDS (y_stage_index layout).
+// bf16 tile of the part-ordered sum is left in LDS (y_stage_index layout;
+// SWAP: accumulators of transposed blocks, staged with y_stage_index<31>).
 // LDS must be free (the K loop ends with a barrier); the caller copies the
 // tile out.  WT: the partials go out with device-scope stores, so the
 // arrival needs no L2 write-back.
-template <bool WT, int NT = GEMM_THREADS, int NI = 4, int NJ = 4>
+template <bool WT, int NT = GEMM_THREADS, int NI = 4, int NJ = 4, bool SWAP = false>
 __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[NI][NJ], const SplitCtl &sp, int tid,
                                              int wave, int lane, char *lds) {
     static_assert(NT / 64 * NI * NJ * 1024 == BM * BN_DN, "the waves' blocks cover the tile");
@@ -286,10 +290,17 @@ __device__ __forceinline__ bool split_reduce(f32x16_t (&acc)[NI][NJ], const Spli
     auto put = [&](int idx, const float (&v)[4]) {
         const int l = idx & 63, g = (idx >> 6) & 3, j = (idx >> 8) % NJ,
                   i = ((idx >> 8) / NJ) % NI, w = idx / (NI * NJ * 256);
-        const int r = tile_row0<NT>(w) + i * 32 + 8 * g + 4 * (l >> 5);
-        const int c = tile_col0<NT>(w) + j * 32 + (l & 31);
+        if (SWAP) {  // v: four consecutive columns of one row
+            const int r = tile_row0<NT>(w) + i * 32 + (l & 31);
+            const int c = tile_col0<NT>(w) + j * 32 + 8 * g + 4 * (l >> 5);
+            *reinterpret_cast<u32x2_t *>(st + y_stage_index<31>(r, c)) =
+u32x2_t{pk_bf16_sw(v[0], v[1]), pk_bf16_sw(v[2], v[3])};
+        } else {  // v: four consecutive rows of one column
+            const int r = tile_row0<NT>(w) + i * 32 + 8 * g + 4 * (l >> 5);
+            const int c = tile_col0<NT>(w) + j * 32 + (l & 31);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st[y_stage_index(r + e, c)] = f2bf(v[e]);
+            for (int e = 0; e < 4; ++e) st[y_stage_index(r + e, c)] = f2bf(v[e]);
+        }
     };
     if (sp.nparts == 2) {
         for (int it = 0; it < (BM * BN_DN / 4) / NT; it += 8) {

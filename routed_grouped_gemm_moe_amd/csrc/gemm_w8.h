@@ -24,6 +24,15 @@
 // barrier of half-stage h, B(s + 3) right after the last barrier of stage s,
 // so each DMA has about three (A) or four (B) half-stages to land.
 //
+// The MFMAs take the weight fragment as their first operand and the
+// activation fragment as their second, so each accumulator block is the
+// transpose of the output block: lane l holds output row l % 32 and, in
+// accumulators 4g .. 4g + 3, the four consecutive output columns
+// 8g + 4 (l / 32) .. + 3.  Every output element is still the same sum of
+// the same products in the same k order (only the roles of the two
+// operands in the instruction change), and the epilogues stage four
+// columns per 8-byte LDS write instead of one per 2-byte write.
+//
 // Per half-stage (two k-steps of 16) and wave: 16 MFMAs, 12 fragment reads
 // (4 A + 2 B per k-step, one k-step ahead), 2 A DMA instructions (plus 4 B
 // in every second half-stage) and one wait + barrier, placed by a fixed
@@ -142,7 +151,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
         for (int k = 0; k < 8; ++k) {
             const int i = k >> 1, j = k & 1;
             if (FULL || i < nblk)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][i], b[0][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][j], a[0][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (k < 2) readB(b[1][k], bs, 2 * P + 1, k);
             if (k >= 2 && k < 6) readA(a[1][k - 2], as, k - 2, 1);
@@ -160,7 +169,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
         for (int k = 0; k < 8; ++k) {
             const int i = k >> 1, j = k & 1;
             if (FULL || i < nblk)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[1][j], a[1][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (k == 1) {
                 wait_vmcnt_lgkm0<8>();
@@ -246,22 +255,32 @@ __device__ __forceinline__ bool gemm_tile_w8(const bf16_t *__restrict__ Ap, int6
     else
         w8_kloop<GATE_UP, false>(acc, rsA, voffA, rsB, voffB, lds_base, KS, nblk, wave, lane, lds);
 
-    // Epilogue through LDS (the rings are free): accumulator v of lane l sits
-    // at row 8*(v/4) + 4*(l/32) + v%4, column l%32 of its 32x32 block.
+    // Epilogue through LDS (the rings are free): accumulator 4g + e of lane l
+    // sits at row l % 32, column 8g + 4 (l / 32) + e of its 32x32 block.
     bf16_t *st = reinterpret_cast<bf16_t *>(lds);
     if (GATE_UP) {
         // h tile: 256 rows x 128 columns as 8 row blocks x 8 packed fragments;
-        // this wave holds h columns 32 wn .. 32 wn + 31 of 4 row blocks.
-        const int col = wn * 32 + l32;
-        const int fo = ((col >> 4) * 64 + 32 * ((col >> 3) & 1)) * 8 + (col & 7);
+        // this wave holds h columns 32 wn .. 32 wn + 31 of 4 row blocks, four
+        // consecutive columns (8 bytes of one packed 16-byte slot) at a time.
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r32 = 8 * (v >> 2) + 4 * half + (v & 3);
-                const float g = acc[i][0][v];
-                const float u = acc[i][1][v];
-                st[(wm * 4 + i) * 4096 + fo + r32 * 8] = f2bf(g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u);
+            for (int g = 0; g < 4; ++g) {
+                const int col = wn * 32 + 8 * g + 4 * half;
+                const int fo = ((col >> 4) * 64 + 32 * ((col >> 3) & 1) + l32) * 8 + (col & 7);
+                uint32_t w[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float hv[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const float gv = acc[i][0][4 * g + 2 * e + q];
+                        const float uv = acc[i][1][4 * g + 2 * e + q];
+                        hv[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+                    }
+                    w[e] = pk_bf16(hv[0], hv[1]);
+                }
+                *reinterpret_cast<u32x2_t *>(st + (wm * 4 + i) * 4096 + fo) = u32x2_t{w[0], w[1]};
             }
         __syncthreads();
         // 8 row blocks x 8 KiB, each contiguous in h; blocks past the tile's
@@ -275,25 +294,29 @@ __device__ __forceinline__ bool gemm_tile_w8(const bf16_t *__restrict__ Ap, int6
         }
     } else {
         if (sp) {
-            if (!split_reduce<WT, W8_THREADS>(acc, *sp, tid, wave, lane, lds)) return false;
+            if (!split_reduce<WT, W8_THREADS, 4, 2, true>(acc, *sp, tid, wave, lane, lds))
+                return false;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        st[y_stage_index(r, wn * 64 + j * 32 + l32)] = f2bf(acc[i][j][v]);
-                }
+                    for (int g = 0; g < 4; ++g) {
+                        const int r = wm * 128 + i * 32 + l32;
+                        const int c = wn * 64 + j * 32 + 8 * g + 4 * half;
+                        const uint32_t w0 = pk_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+                        const uint32_t w1 = pk_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                        *reinterpret_cast<u32x2_t *>(st + y_stage_index<31>(r, c)) = u32x2_t{w0, w1};
+                    }
         }
         __syncthreads();
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
         for (int g = tid; g < a_rows * 32; g += W8_THREADS) {
             const int r = g >> 5, c = g & 31;
             u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + (int64_t)r * o_ld) + c;
-            if (WT) store16_wt(dst, src[r * 32 + (c ^ (r & 7))]);
-            else *dst = src[r * 32 + (c ^ (r & 7))];
+            if (WT) store16_wt(dst, src[r * 32 + (c ^ (r & 31))]);
+            else *dst = src[r * 32 + (c ^ (r & 31))];
         }
     }
     return true;

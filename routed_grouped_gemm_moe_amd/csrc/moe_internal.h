@@ -89,6 +89,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // Native 16-byte vector (HIP's uint4 is a union-based struct, which keeps
 // arrays of it out of registers).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 element q (0..7) of a 16-byte vector, widened exactly to float.
 __device__ __forceinline__ float bf16x8_elem(const u32x4_t &v, int q) {
@@ -99,11 +100,24 @@ __device__ __forceinline__ float bf16x8_elem(const u32x4_t &v, int q) {
 __device__ __forceinline__ float bf2f(bf16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
-// float -> bf16, round to nearest, ties to even (inputs are finite).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+// float -> bf16, round to nearest, ties to even: gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32), which rounds finite values exactly as
+// IEEE round-to-nearest-even and keeps NaN a NaN.
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// Two floats -> two bf16 in one 32-bit word (lo in the low half), one
+// conversion instruction.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{lo, hi}, bf16x2v_t));
+}
+// The same pair by integer arithmetic (where the conversion instruction's
+// scheduling would raise register pressure past the budget).
+__device__ __forceinline__ uint32_t pk_bf16_sw(float lo, float hi) {
+    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    a += 0x7FFFu + ((a >> 16) & 1u);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (a >> 16) | (b & 0xFFFF0000u);
 }
 
 // ---------------------------------------------------------------- sizes
