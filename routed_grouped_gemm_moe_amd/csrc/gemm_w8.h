@@ -64,13 +64,17 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
-// The K loop over KS stages of 64 (KH = 2 KS half-stages).  FULL: all four
-// of the wave's row blocks valid; otherwise MFMAs of row blocks past the
-// tile's last valid row are skipped (nblk = valid blocks of this wave).
-template <bool GATE_UP, bool FULL>
+// The K loop over KS stages of 64 (KH = 2 KS half-stages).  NB: this wave's
+// row blocks holding valid rows (4 in every full tile; fewer in the last,
+// partly filled m-tile of an expert).  The MFMAs and A fragment reads of the
+// other blocks are left out at compile time (a wave with none also skips its
+// B fragment reads), so no loop carries a branch between its MFMAs; every
+// wave still issues all its DMAs and passes every barrier, so waves running
+// different NB stay in step.
+template <bool GATE_UP, int NB>
 __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &rsA,
                                          const int (&voffA)[2], const i32x4_t &rsB,
-                                         const int (&voffB)[4], uint32_t lds_base, int KS, int nblk,
+                                         const int (&voffB)[4], uint32_t lds_base, int KS,
                                          int wave, int lane, const char *lds) {
     const int KH = 2 * KS;
     const int wm = wave >> 2, wn = wave & 3;
@@ -104,9 +108,11 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
                      :: "s"(m), "v"(voffB[n] + so), "s"(rsB) : "memory", "m0");
     };
     auto readA = [&](bf16x8_t &dst, uint32_t as, int i, int kk) {
+        if (i >= NB) return;
         dst = *reinterpret_cast<const bf16x8_t *>(lds + as * W8_A_SLOT + aoff + i * 2048 + kk * 1024);
     };
     auto readB = [&](bf16x8_t &dst, uint32_t bs, int q, int j) {
+        if (NB == 0) return;
         dst = *reinterpret_cast<const bf16x8_t *>(lds + W8_B_BASE + bs * W8_B_SLOT + boff[q] + brow[j]);
     };
 
@@ -150,7 +156,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = k >> 1, j = k & 1;
-            if (FULL || i < nblk)
+            if (i < NB)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][j], a[0][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (k < 2) readB(b[1][k], bs, 2 * P + 1, k);
@@ -168,7 +174,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = k >> 1, j = k & 1;
-            if (FULL || i < nblk)
+            if (i < NB)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[1][j], a[1][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (k == 1) {
@@ -250,10 +256,13 @@ __device__ __forceinline__ bool gemm_tile_w8(const bf16_t *__restrict__ Ap, int6
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     __syncthreads();  // the previous user of the LDS is done with it
-    if (a_rows == BM)
-        w8_kloop<GATE_UP, true>(acc, rsA, voffA, rsB, voffB, lds_base, KS, 4, wave, lane, lds);
-    else
-        w8_kloop<GATE_UP, false>(acc, rsA, voffA, rsB, voffB, lds_base, KS, nblk, wave, lane, lds);
+    switch (nblk) {  // wave-uniform
+    case 4: w8_kloop<GATE_UP, 4>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 3: w8_kloop<GATE_UP, 3>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 2: w8_kloop<GATE_UP, 2>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 1: w8_kloop<GATE_UP, 1>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    default: w8_kloop<GATE_UP, 0>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    }
 
     // Epilogue through LDS (the rings are free): accumulator 4g + e of lane l
     // sits at row l % 32, column 8g + 4 (l / 32) + e of its 32x32 block.
