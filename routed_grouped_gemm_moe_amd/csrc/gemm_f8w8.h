@@ -23,13 +23,15 @@ namespace moe {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
-// KS stages of 128 bytes (KH = 2 KS fp8 k-steps).  FULL: all four of the
-// wave's row blocks valid.
-template <bool GATE_UP, bool FULL>
+// KS stages of 128 bytes (KH = 2 KS fp8 k-steps).  NB: this wave's row
+// blocks holding valid rows; the MFMAs and A fragment reads of the others
+// are left out at compile time (no branch between MFMAs), every DMA and
+// barrier stays, as in gemm_w8.h.
+template <bool GATE_UP, int NB>
 __device__ __forceinline__ void f8w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &rsA,
                                            const int (&voffA)[2], const i32x4_t &rsB,
                                            const int (&voffB)[4], uint32_t lds_base, int KS,
-                                           int nblk, int wave, int lane, const char *lds) {
+                                           int wave, int lane, const char *lds) {
     const int KH = 2 * KS;
     const int wm = wave >> 2, wn = wave & 3;
     const int l32 = lane & 31, half = lane >> 5;
@@ -59,9 +61,11 @@ __device__ __forceinline__ void f8w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t 
                      :: "s"(m), "v"(voffB[n] + so), "s"(rsB) : "memory", "m0");
     };
     auto readA = [&](bf16x8_t &dst, uint32_t as, int i, int kk) {
+        if (i >= NB) return;
         dst = *reinterpret_cast<const bf16x8_t *>(lds + as * W8_A_SLOT + aoff + i * 2048 + kk * 1024);
     };
     auto readB = [&](bf16x8_t &dst, uint32_t bs, int q, int j) {
+        if (NB == 0) return;
         dst = *reinterpret_cast<const bf16x8_t *>(lds + W8_B_BASE + bs * W8_B_SLOT + boff[q] + brow[j]);
     };
 
@@ -108,7 +112,7 @@ __device__ __forceinline__ void f8w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t 
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = k >> 1, j = k & 1;
-            if (FULL || i < nblk)
+            if (i < NB)
                 acc[i][j] = mfma_f8(f8_join(a[P][i][0], a[P][i][1]), f8_join(b[P][j][0], b[P][j][1]),
                                     acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
@@ -194,10 +198,13 @@ __device__ __forceinline__ void gemm_tile_f8w8(const uint8_t *__restrict__ Ap, i
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     __syncthreads();  // the previous user of the LDS is done with it
-    if (a_rows == BM)
-        f8w8_kloop<GATE_UP, true>(acc, rsA, voffA, rsB, voffB, lds_base, KS, 4, wave, lane, lds);
-    else
-        f8w8_kloop<GATE_UP, false>(acc, rsA, voffA, rsB, voffB, lds_base, KS, nblk, wave, lane, lds);
+    switch (nblk) {  // wave-uniform
+    case 4: f8w8_kloop<GATE_UP, 4>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 3: f8w8_kloop<GATE_UP, 3>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 2: f8w8_kloop<GATE_UP, 2>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    case 1: f8w8_kloop<GATE_UP, 1>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    default: f8w8_kloop<GATE_UP, 0>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
+    }
 
     // Epilogue through LDS, the arithmetic of gemm_tile_f8: accumulator v of
     // lane l sits at row 8*(v/4) + 4*(l/32) + v%4, column l%32 of its block.
