@@ -169,9 +169,25 @@ def _check_gemm_halves(cfg, xrows, eor, h_dev, y_dev, rows, ref_w):
 def test_fp8_ffn_matches_oracle(name):
     cfg = FP8_CASES[name].scaled(name=name)
     arrs = W.generate(cfg)
-    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
     r_ids, _ = oracle.route(arrs["x"], arrs["w_router"], cfg.k, bias=arrs["bias"])
     _, ro, rp, _ = oracle.permute(r_ids, cfg.E, cfg.e_lo, cfg.E_hi)
+    _fp8_ffn_case(name, cfg, arrs, ro, rp)
+
+
+def test_fp8_ffn_partly_filled_m_tiles_every_row_block_count():
+    # the row counts of the bf16 test of the same name: every pair of valid
+    # 32-row blocks in the two halves of an expert's last m-tile
+    counts = np.array([1, 31, 32, 33, 64, 80, 97, 128, 129, 160, 180, 224, 255, 256, 257, 300,
+                       513])
+    E, N = len(counts), int(counts.sum())
+    cfg = W.CONFIGS["tiny"].scaled(name="partial_tiles", T=N, d=256, f=512, E=E, k=1, seed=22)
+    arrs = W.generate(cfg)
+    ro = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    _fp8_ffn_case("partial_tiles", cfg, arrs, ro, np.arange(N), all_rows=True)
+
+
+def _fp8_ffn_case(name, cfg, arrs, ro, rp, all_rows=False):
+    D = M.MoEDims.make(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k, cfg.e_lo, cfg.E_hi)
     N = int(ro[-1])
     (gq, gs), (rgq, rgs) = _quant_both("w_gate", arrs["w_gate"])
     (uq, us), (ruq, rus) = _quant_both("w_up", arrs["w_up"])
@@ -191,7 +207,7 @@ def test_fp8_ffn_matches_oracle(name):
         return
     assert torch.equal(y_all[:N].view(torch.int16), y[:N].view(torch.int16)), \
         "moe_expert_ffn_fp8 != moe_down_fp8(moe_gate_up_fp8)"
-    rows = np.arange(N) if N <= 1200 else np.unique(
+    rows = np.arange(N) if N <= 1200 or all_rows else np.unique(
         np.concatenate([[0, N - 1], ro[1:-1].clip(0, N - 1),
                         np.random.default_rng(1).choice(N, 40, replace=False)]))
     eor = (np.searchsorted(ro, rows, side="right") - 1).astype(np.int32)

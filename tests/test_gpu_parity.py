@@ -223,6 +223,34 @@ def test_expert_with_more_m_tiles_than_one_group():
     _check_layer(cfg, t, arrs, staged_out=staged, tokens=sample_tokens(cfg.T, 40, seed=6))
 
 
+# Row counts per expert whose last m-tile (count % 256 rows, 256 when that
+# is 0) gives the two halves of the eight-wave tile every pair of valid
+# 32-row blocks a last m-tile can have -- (1,0) (2,0) (3,0) (4,0) (4,1)
+# (4,2) (4,3) (4,4) and full -- plus experts of several m-tiles.  Each wave
+# runs a K loop specialised on its half's count, so each one is exercised.
+PARTIAL_TILE_COUNTS = np.array([1, 31, 32, 33, 64, 80, 97, 128, 129, 160, 180, 224, 255, 256,
+                                257, 300, 513])
+
+
+def test_partly_filled_m_tiles_every_row_block_count():
+    counts = PARTIAL_TILE_COUNTS
+    E, N = len(counts), int(counts.sum())
+    cfg = W.CONFIGS["tiny"].scaled(name="partial_tiles", T=N, d=256, f=384, E=E, k=1, seed=21)
+    arrs = W.generate(cfg)
+    t = upload(cfg, arrs)
+    D = _dims(cfg)
+    ro = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    say(f"moe_expert_ffn partly filled m-tiles E={E} N={N}")
+    y = M.moe_expert_ffn(D, t["x"], torch.as_tensor(ro, device="cuda"), t["w_gate"], t["w_up"],
+                         t["w_down"])
+    torch.cuda.synchronize()
+    eor = np.repeat(np.arange(E, dtype=np.int32), counts)
+    ref = oracle.expert_rows(arrs["x"], eor, arrs["w_gate"], arrs["w_up"], arrs["w_down"])
+    err = rel_err(host_f32(y[:N]), ref)
+    say(f"  ffn rel err {err:.3e}")
+    assert err <= TOL_LAYER
+
+
 def test_no_local_rows_gives_zero_output():
     # every token routes only to experts outside the local range
     cfg = W.CONFIGS["tiny"].scaled(name="nolocal", T=50, d=256, f=128, E=8, k=1, e_lo=0, e_hi=2,
