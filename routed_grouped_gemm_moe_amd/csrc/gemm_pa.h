@@ -65,6 +65,9 @@ constexpr int PA_CPOL_SC1 = 16;
 __device__ __forceinline__ void store16_wt(void *p, const u32x4_t &v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
+__device__ __forceinline__ void store8_wt(void *p, const u32x2_t &v) {
+    asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 #pragma clang diagnostic pop
 
 // Memory instruction issued after MFMA k (0..15) of sub-step q (0..3):

@@ -264,15 +264,21 @@ __device__ __forceinline__ bool gemm_tile_w8(const bf16_t *__restrict__ Ap, int6
     default: w8_kloop<GATE_UP, 0>(acc, rsA, voffA, rsB, voffB, lds_base, KS, wave, lane, lds); break;
     }
 
-    // Epilogue through LDS (the rings are free): accumulator 4g + e of lane l
-    // sits at row l % 32, column 8g + 4 (l / 32) + e of its 32x32 block.
+    // Epilogues: accumulator 4g + e of lane l sits at row l % 32, column
+    // 8g + 4 (l / 32) + e of its 32x32 block.  h goes out from the registers,
+    // y through LDS (the rings are free).
     bf16_t *st = reinterpret_cast<bf16_t *>(lds);
     if (GATE_UP) {
         // h tile: 256 rows x 128 columns as 8 row blocks x 8 packed fragments;
         // this wave holds h columns 32 wn .. 32 wn + 31 of 4 row blocks, four
         // consecutive columns (8 bytes of one packed 16-byte slot) at a time.
+        // For one (row block, g) the wave's 64 lanes fill 32 whole slots of
+        // one fragment, 512 contiguous bytes, so h goes out straight from the
+        // registers.  Row blocks past the tile's last valid row belong to the
+        // next segment and are not written.
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            if (i >= nblk) break;  // wave-uniform
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int col = wn * 32 + 8 * g + 4 * half;
@@ -289,17 +295,10 @@ __device__ __forceinline__ bool gemm_tile_w8(const bf16_t *__restrict__ Ap, int6
                     }
                     w[e] = pk_bf16(hv[0], hv[1]);
                 }
-                *reinterpret_cast<u32x2_t *>(st + (wm * 4 + i) * 4096 + fo) = u32x2_t{w[0], w[1]};
+                bf16_t *dst = out + (int64_t)(wm * 4 + i) * o_ld * 512 + fo;
+                if (WT) store8_wt(dst, u32x2_t{w[0], w[1]});
+                else *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{w[0], w[1]};
             }
-        __syncthreads();
-        // 8 row blocks x 8 KiB, each contiguous in h; blocks past the tile's
-        // last valid row belong to the next segment and are not written.
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(lds);
-        for (int g = tid; g < nb_all * 512; g += W8_THREADS) {
-            const int rb = g >> 9;
-            u32x4_t *dst = reinterpret_cast<u32x4_t *>(out + rb * o_ld * 512) + (g & 511);
-            if (WT) store16_wt(dst, src[g]);
-            else *dst = src[g];
         }
     } else {
         if (sp) {
