@@ -16,7 +16,9 @@
 // side flag as soon as it is written (the producer-consumer tile signaling of
 // Cui et al., abstract), not at a kernel boundary.
 //
-// GEMM tiles are those of gemm_pa.h: x_perm and h are in its packed layout
+// GEMM tiles: the eight-wave tiles of gemm_w8.h (packed dispatch, 512
+// threads) or the four-wave tiles of gemm_pa.h / gemm_tile.h (gather-on-load
+// dispatch, 256 threads).  x_perm and h are in the packed layout of gemm_pa.h
 // (h written by the gate/up epilogue, read as the down tiles' A operand).
 //
 // Interleaved order (MOE_ORDER_READY_DOWN): before each gate/up claim a
@@ -38,8 +40,12 @@
 //
 // Memory ordering (MI355X: one L2 per XCD; an agent-scope release writes the
 // issuing XCD's L2 back, an agent-scope acquire invalidates it):
-//  - producers: each wave waits for its stores, the workgroup meets at a
-//    barrier, then one wave publishes with a single agent-scope release RMW;
+//  - producers write their outputs with device-scope (write-through)
+//    stores; each wave waits until its stores are performed, the workgroup
+//    meets at a barrier, then one wave publishes with a relaxed agent-scope
+//    RMW, so no XCD's L2 is written back.  (The gathered gate/up tile of the
+//    gather-on-load dispatch writes h with ordinary stores and publishes with
+//    an agent-scope release instead.)
 //  - gate/up producers also OR their XCD into gu_xcd[m-tile].  A down tile
 //    whose producers all ran on its own XCD reads h through the shared L2 and
 //    only invalidates the CU's L1; otherwise it takes the agent-scope acquire.
