@@ -60,10 +60,16 @@ constexpr int PA_CPOL_SC1 = 16;
 // point of coherence rather than held dirty in this XCD's L2, so a producer
 // whose outputs all go out this way publishes them without an L2 write-back
 // (it waits for the stores, then raises its flag).
+//
+// The compiler does not look inside the asm, so the hazard a store of more
+// than 64 bits has on this chip -- a VALU write to its data registers in the
+// next cycle can change the data still being read -- is covered by the
+// asm's own wait states (without them, y stored straight from freshly
+// converted registers came out wrong now and then).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void store16_wt(void *p, const u32x4_t &v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store8_wt(void *p, const u32x2_t &v) {
     asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
