@@ -138,7 +138,7 @@ __device__ __forceinline__ void f8_kloop(f32x16_t (&acc)[4][4], const i32x4_t &r
         const uint32_t so = s < KT ? (uint32_t)s * PA_ROWB : PA_OOB;
         const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base + (s & (PA_NST - 1)) * PA_STAGE +
                                                           wave * 8192 + n * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :: "s"(m), "v"(voffB[n] + so), "s"(rsB) : "memory", "m0");
     };
     auto loadA = [&](bf16x8_t &dst, int s, int q, int i) {

@@ -103,7 +103,10 @@ __host__ __device__ constexpr PaSlot pa_slot(int q, int k) {
 enum { PA_SILU_PACKED = 0, PA_BF16 = 1 };
 
 // The DMA below names M0 (the LDS-DMA destination register) as clobbered; no
-// other code of these kernels keeps a value in M0.
+// other code of these kernels keeps a value in M0.  Every LDS-DMA asm of the
+// library puts one wait state between its M0 write and the load that reads
+// M0, the distance this chip generation asks for and which the compiler
+// cannot add to asm it does not look into.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -132,7 +135,7 @@ __device__ __forceinline__ void pa_kloop(f32x16_t (&acc)[4][4], const i32x4_t &r
         const uint32_t so = s < KT ? (uint32_t)s * PA_ROWB : PA_OOB;
         const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base + (s & (PA_NST - 1)) * PA_STAGE +
                                                           wave * 8192 + n * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :: "s"(m), "v"(voffB[n] + so), "s"(rsB) : "memory", "m0");
     };
     auto loadA = [&](bf16x8_t &dst, int s, int q, int i) {

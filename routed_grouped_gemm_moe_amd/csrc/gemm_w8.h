@@ -96,7 +96,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
         const uint32_t so = h < KH ? (uint32_t)h * 2048u : PA_OOB;
         const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base + (h & (W8_A_SLOTS - 1)) * W8_A_SLOT +
                                                           (wave * 2 + n) * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :: "s"(m), "v"(voffA[n] + so), "s"(rsA) : "memory", "m0");
     };
     // B DMA n of stage s into slot bs: B rows (4 wave + n) * 8 .. + 7
@@ -104,7 +104,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
         const uint32_t so = s < KS ? (uint32_t)s * PA_ROWB : PA_OOB;
         const uint32_t m = __builtin_amdgcn_readfirstlane(lds_base + W8_B_BASE + bs * W8_B_SLOT +
                                                           (wave * 4 + n) * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :: "s"(m), "v"(voffB[n] + so), "s"(rsB) : "memory", "m0");
     };
     auto readA = [&](bf16x8_t &dst, uint32_t as, int i, int kk) {

@@ -538,11 +538,11 @@ __global__ __launch_bounds__(64 * (RtlGeom<EP, EG>::WAVES)) void route_tok_lds_k
 #pragma unroll
         for (int r = 0; r < DPW; ++r) {
             const uint32_t m = __builtin_amdgcn_readfirstlane(sb + (wave * DPW + r) * 1024);
-            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+            asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                          :: "s"(m), "v"(voff[r] + (uint32_t)s * 128u), "s"(rx) : "memory", "m0");
         }
         const uint32_t m = __builtin_amdgcn_readfirstlane(sb + G::X_BYTES + wave * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                      :: "s"(m), "v"(woff + (uint32_t)s * 128u), "s"(rw) : "memory", "m0");
     };
     for (int s = 0; s < NSL; ++s) issue(s);
