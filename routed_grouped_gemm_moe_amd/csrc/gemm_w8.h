@@ -34,7 +34,8 @@
 // columns per 8-byte LDS write instead of one per 2-byte write.
 //
 // Per half-stage (two k-steps of 16) and wave: 16 MFMAs, 12 fragment reads
-// (4 A + 2 B per k-step, one k-step ahead), 2 A DMA instructions (plus 4 B
+// (4 A + 2 B per k-step, one k-step ahead, each issued as early as its
+// buffer and, after the barrier, its slot allow), 2 A DMA instructions (plus 4 B
 // in every second half-stage) and one wait + barrier, placed by a fixed
 // slot table.  For a gate/up tile the
 // wave's two column blocks are 32 gate columns and the 32 matching up
@@ -160,7 +161,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[0][j], a[0][i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (k < 2) readB(b[1][k], bs, 2 * P + 1, k);
-            if (k >= 2 && k < 6) readA(a[1][k - 2], as, k - 2, 1);
+            if (k < 4) readA(a[1][k], as, k, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         // k-step 2h + 1: MFMAs on a[1], b[1].  After two of them, the wait +
@@ -182,7 +183,7 @@ __device__ __forceinline__ void w8_kloop(f32x16_t (&acc)[4][2], const i32x4_t &r
                 __syncthreads();
             }
             if (k == 2 || k == 3) readB(b[0][k - 2], bs_n, (2 * P + 2) & 3, k - 2);
-            if (k >= 4) readA(a[0][k - 4], as_n, k - 4, 0);
+            if (k >= 2 && k < 6) readA(a[0][k - 2], as_n, k - 2, 0);
             if (P == 1 && k >= 2 && k < 6) dmaB(s + 3, bs, k - 2);
             if (k == 6) dmaA(h + 4, 0);
             if (k == 7) dmaA(h + 4, 1);
