@@ -51,8 +51,6 @@ __host__ __device__ __forceinline__ int64_t packed_chunk(int64_t row, int64_t c,
     return (((row >> 5) * kb + (c >> 1)) << 6) + (row & 31) + ((c & 1) << 5);
 }
 
-__device__ i32x4_t raw_buffer_load_v4(i32x4_t rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 // Cache-policy operand of a buffer load: sc1 (bit 4).
 constexpr int PA_CPOL_SC1 = 16;
 

@@ -46,6 +46,9 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 __device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) void *lds,
                                     int size, int voffset, int soffset, int offset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.lds");
+// LLVM intrinsic: raw buffer load of 16 bytes into VGPRs.
+__device__ i32x4_t raw_buffer_load_v4(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
 // Buffer descriptor over [p, p + bytes): raw (stride 0); lanes whose offset
 // is out of range read zeros.

@@ -200,6 +200,24 @@ __host__ __device__ __forceinline__ int64_t stag_pitch(int64_t d) { return 16 * 
 __host__ __device__ __forceinline__ int64_t refine_per_wave(int64_t d, int64_t E) {
     return stag_pitch(d) + ((E * 8 + 15) & ~(int64_t)15);
 }
+// A refine wave stages x_t in one window (all ppc = d/128 16-byte pieces of
+// each chunk) when that leaves LDS for 16 waves per CU, else in two: pieces
+// [0, h) of every chunk, then [h, ppc), h even.  Returns h.
+__host__ __device__ __forceinline__ int64_t refine_split(int64_t d, int64_t E) {
+    const int64_t ppc = d / 128;
+    if (refine_per_wave(d, E) * 16 <= 160 * 1024 || ppc < 4) return ppc;
+    return (ppc / 2) & ~(int64_t)1;
+}
+// Byte pitch of one chunk in the staging window (16-byte stagger as above).
+__host__ __device__ __forceinline__ int64_t refine_chunk_pitch(int64_t d, int64_t E) {
+    const int64_t ppc = d / 128, h = refine_split(d, E);
+    return (h > ppc - h ? h : ppc - h) * 16 + 16;
+}
+// LDS of one refine wave as launched: the staging window, then candidate ids
+// and exact logits.
+__host__ __device__ __forceinline__ int64_t refine_lds_per_wave(int64_t d, int64_t E) {
+    return 16 * refine_chunk_pitch(d, E) + ((E * 8 + 15) & ~(int64_t)15);
+}
 
 template <int EP>
 __global__ __launch_bounds__(RT_THREADS) void route_small_kernel(
@@ -752,6 +770,62 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void route_gemm_kernel(
                        part + (int64_t)s * T * E, E, n0, b_rows, lds);
 }
 
+// The chunk chains of NJ candidates over pieces lo .. lo + n - 1 of this
+// lane's chunk (acc[j] += x_i * w_j,i, i ascending).  rw = buffer over the
+// re-laid-out W_r; vo[j] = byte offset of candidate j's first 16-byte piece
+// of the chunk, successive pieces 256 bytes apart; xc = the staged window of
+// the chunk (piece lo first); n is even (d is a multiple of 256 and the
+// windows split at an even piece).  NJ is a template parameter so every group
+// of loads is unconditional: the pieces of RF_RING - 1 groups ahead are in
+// flight while a group is summed, and each wait leaves exactly those
+// outstanding.  A group's position is one wave-uniform scalar offset (the
+// pieces within it are immediate offsets), so the loads cost no vector
+// address arithmetic; positions past the window's end re-load its last group.
+constexpr int RF_PG = 2;    // 16-byte pieces per candidate and group (divides n)
+constexpr int RF_RING = 2;  // groups in the register ring
+template <int NJ>
+__device__ __forceinline__ void refine_chains(i32x4_t rw, const int (&vo)[4], const char *xc,
+                                              int lo, int n, float (&acc)[4]) {
+    u32x4_t r[RF_RING][NJ][RF_PG];
+    auto load = [&](u32x4_t (&dst)[NJ][RF_PG], int i0) {
+        const int so = __builtin_amdgcn_readfirstlane((lo + min(i0, n - RF_PG)) * 256);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < RF_PG; ++q)
+                dst[j][q] = __builtin_bit_cast(u32x4_t, raw_buffer_load_v4(rw, vo[j] + q * 256, so, 0));
+    };
+    auto sum = [&](const u32x4_t (&src)[NJ][RF_PG], int i0) {
+#pragma unroll
+        for (int q = 0; q < RF_PG; ++q) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xc + (i0 + q) * 16);
+            float xf[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h) xf[h] = bf16x8_elem(xv, h);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int h = 0; h < 8; ++h)
+                    acc[j] = __builtin_fmaf(xf[h], bf16x8_elem(src[j][q], h), acc[j]);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < RF_RING - 1; ++u) {
+        load(r[u], u * RF_PG);
+        __builtin_amdgcn_sched_barrier(0);  // groups issued in ring order
+    }
+    for (int i0 = 0; i0 < n; i0 += RF_RING * RF_PG) {
+#pragma unroll
+        for (int u = 0; u < RF_RING; ++u) {
+            load(r[(u + RF_RING - 1) % RF_RING], i0 + (u + RF_RING - 1) * RF_PG);
+            if (i0 + u * RF_PG < n) sum(r[u], i0 + u * RF_PG);  // whole groups (uniform)
+            // keep the next step's loads after this sum (hoisted, they would
+            // all wait at the turn's last sum)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // One wave per token: bounds, candidates, exact logits of the candidates in
 // the defined order, selection and gates.
 constexpr int RF_WAVES = 4;
@@ -773,13 +847,13 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     if (t >= T) return;  // wave-uniform; the kernel has no workgroup barrier
 
     const int64_t dc = d / 16, ppc = dc / 8;
-    const int64_t cbs = dc * 2 + 16;
-    const int64_t per_wave = refine_per_wave(d, E);
-    char *xs = smem + wave * per_wave;                          // staged x_t
-    int32_t *cand = reinterpret_cast<int32_t *>(xs + stag_pitch(d));  // [E]
-    float *exact = reinterpret_cast<float *>(cand + E);                // [E]
+    const int64_t h = refine_split(d, E);         // pieces of chunk in window 0
+    const int64_t cbs = refine_chunk_pitch(d, E);  // chunk pitch in the window
+    char *xs = smem + wave * refine_lds_per_wave(d, E);         // staged x_t window
+    int32_t *cand = reinterpret_cast<int32_t *>(xs + 16 * cbs);  // [E]
+    float *exact = reinterpret_cast<float *>(cand + E);          // [E]
 
-    // stage x_t (coalesced) and ||x_t||
+    // ||x_t|| over the whole row (coalesced), staging window 0
     float ss = 0.0f;
     for (int64_t p0 = lane; p0 < d / 8; p0 += 8 * 64) {
         u32x4_t v[8];
@@ -797,7 +871,8 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
                 const float f = bf16x8_elem(v[u], q);
                 ss = __builtin_fmaf(f, f, ss);
             }
-            *reinterpret_cast<u32x4_t *>(xs + (p / ppc) * cbs + (p % ppc) * 16) = v[u];
+            if (p % ppc < h)
+                *reinterpret_cast<u32x4_t *>(xs + (p / ppc) * cbs + (p % ppc) * 16) = v[u];
         }
     }
 #pragma unroll
@@ -904,48 +979,51 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     const int c = lane & 15;
     const int g = lane >> 4;
     const char *xc = xs + c * cbs;
+    const i32x4_t rw = make_rsrc(wt, (uint32_t)(E * d * 2));
+    // window w holds pieces [lo, lo + n) of every chunk
+    auto stage = [&](int64_t lo, int64_t n) {
+        for (int64_t q0 = lane; q0 < 16 * n; q0 += 8 * 64) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t q = q0 + u * 64;
+                if (q < 16 * n)
+                    v[u] = reinterpret_cast<const u32x4_t *>(x + t * d)[(q / n) * ppc + lo + q % n];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t q = q0 + u * 64;
+                if (q >= 16 * n) break;
+                *reinterpret_cast<u32x4_t *>(xs + (q / n) * cbs + (q % n) * 16) = v[u];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    int staged = 0;  // window in LDS
     for (int b = 0; b < ns; b += 16) {
         const int nj = min(4, (ns - b + 3) >> 2);  // candidate slots per lane in use (uniform)
-        const u32x4_t *wp[4];
+        int vo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int ci = b + g + 4 * j;
             const int e = cand[ci < ns ? ci : b];
-            wp[j] = reinterpret_cast<const u32x4_t *>(wt + (int64_t)e * d) + c;
+            vo[j] = (e * (int)d + c * 8) * 2;
         }
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        constexpr int PG = 2;  // vectors per candidate and prefetch group
-        u32x4_t wa[4][PG], wb[4][PG];
-        auto load = [&](u32x4_t (&r)[4][PG], int64_t i0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (j < nj)
-#pragma unroll
-                    for (int q = 0; q < PG; ++q)
-                        r[j][q] = (i0 + q < ppc) ? wp[j][(i0 + q) * 16] : u32x4_t{0u, 0u, 0u, 0u};
-        };
-        auto compute = [&](const u32x4_t (&r)[4][PG], int64_t i0) {
-#pragma unroll
-            for (int q = 0; q < PG; ++q) {
-                if (i0 + q >= ppc) break;
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(xc + (i0 + q) * 16);
-                float xf[8];
-#pragma unroll
-                for (int h = 0; h < 8; ++h) xf[h] = bf16x8_elem(xv, h);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (j < nj)
-#pragma unroll
-                        for (int h = 0; h < 8; ++h)
-                            acc[j] = __builtin_fmaf(xf[h], bf16x8_elem(r[j][q], h), acc[j]);
+        for (int w = 0; w < (h < ppc ? 2 : 1); ++w) {  // the chains go on across windows
+            const int64_t lo = w ? h : 0, n = w ? ppc - h : h;
+            if (staged != w) {
+                stage(lo, n);
+                staged = w;
             }
-        };
-        load(wa, 0);
-        for (int64_t i0 = 0; i0 < ppc; i0 += 2 * PG) {
-            if (i0 + PG < ppc) load(wb, i0 + PG);
-            compute(wa, i0);
-            if (i0 + 2 * PG < ppc) load(wa, i0 + 2 * PG);
-            if (i0 + PG < ppc) compute(wb, i0 + PG);
+            switch (nj) {  // wave-uniform
+            case 4: refine_chains<4>(rw, vo, xc, (int)lo, (int)n, acc); break;
+            case 3: refine_chains<3>(rw, vo, xc, (int)lo, (int)n, acc); break;
+            case 2: refine_chains<2>(rw, vo, xc, (int)lo, (int)n, acc); break;
+            default: refine_chains<1>(rw, vo, xc, (int)lo, (int)n, acc); break;
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1075,7 +1153,7 @@ static hipError_t launch_route_fast(const Dims &D, const bf16_t *x, const bf16_t
     hipLaunchKernelGGL(route_gemm_kernel, dim3((unsigned)tiles), dim3(GEMM_THREADS), GEMM_LDS_BYTES,
                        s, D.T, D.d, D.E, S, x, w_router, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds = (size_t)RF_WAVES * refine_per_wave(D.d, D.E);
+    const size_t lds = (size_t)RF_WAVES * refine_lds_per_wave(D.d, D.E);
     const dim3 grid((unsigned)((D.T + RF_WAVES - 1) / RF_WAVES));
     auto refine = [&](auto rk) -> hipError_t {
         constexpr int R = decltype(rk)::value;

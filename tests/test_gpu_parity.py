@@ -380,6 +380,39 @@ def test_router_fast_path_on_constructed_ties(pattern):
         assert np.array_equal(r_ids[0], np.arange(cfg.k))
 
 
+# With E > 16 and a wide hidden dimension, a refine wave stages its token row
+# in two windows of pieces per chunk (the row would otherwise leave LDS for
+# fewer than 16 waves per CU): windows of 16 and 18 pieces (d = 4352), of 16
+# (d = 4096, duplicated expert rows: exact ties), and every expert a
+# candidate at d = 7168 (all rows equal), so each batch of 16 candidates
+# stages both windows again.
+TWO_WINDOW_ROUTER = {
+    "d4352_e256": dict(T=300, d=4352, E=256, k=8, pattern=None),
+    "d4096_e256_duplicated": dict(T=200, d=4096, E=256, k=6, pattern="duplicated_rows"),
+    "d7168_e256_all_equal": dict(T=129, d=7168, E=256, k=8, pattern="all_equal"),
+}
+
+
+@pytest.mark.parametrize("name", list(TWO_WINDOW_ROUTER))
+def test_router_two_window_staging(name):
+    spec = dict(TWO_WINDOW_ROUTER[name])
+    pattern = spec.pop("pattern")
+    cfg = W.CONFIGS["tiny"].scaled(name=name, f=128, seed=60 + list(TWO_WINDOW_ROUTER).index(name),
+                                   **spec)
+    arrs = W.generate(cfg)
+    if pattern is not None:
+        wr = W.bf16_bits_to_f32(arrs["w_router"]).reshape(cfg.E, cfg.d)
+        if pattern == "duplicated_rows":
+            wr[1::2] = wr[0::2]
+        else:
+            wr[:] = wr[0]
+        arrs["w_router"] = W.f32_to_bf16_bits(wr.astype(np.float32))
+    t = upload(cfg, arrs)
+    ids, gates, r_ids, r_g = _check_route(cfg, t, arrs)
+    if pattern == "all_equal":
+        assert np.array_equal(r_ids[0], np.arange(cfg.k))
+
+
 # The E <= 16 router stages the activations through LDS when d is a multiple
 # of 1024 (up to four 32 KiB steps in flight, a ring beyond that): step
 # counts 1, 2, 3, 5 and 8, ragged and single-token blocks, E below 8 and
