@@ -770,6 +770,75 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void route_gemm_kernel(
                        part + (int64_t)s * T * E, E, n0, b_rows, lds);
 }
 
+// Cross-lane steps by DPP (register moves, no LDS round trip); the whole
+// wave must be active.  Controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1]
+// (partners xor 1, xor 2), row_half_mirror (lane i <-> 7 - i of each 8),
+// row_mirror (i <-> 15 - i of each 16), row_bcast15 / row_bcast31 (lane 15 of
+// a row to the next row, lane 31 to rows 2 and 3; rows outside ROWS keep
+// their own value).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// Sum of each 16-lane row in the balanced pairwise order (partners xor 1, 2,
+// 4, 8).  After the first two steps the four lanes of a quad hold the same
+// bits (a + b == b + a exactly), so the half-mirror and mirror partners hold
+// the values the xor-4 and xor-8 partners would: every lane of the row ends
+// with ((s0 + s1) + (s2 + s3)) + ... bit for bit.
+__device__ __forceinline__ float row16_tree_sum(float a) {
+    a = a + dpp_f32<0xB1>(a);
+    a = a + dpp_f32<0x4E>(a);
+    a = a + dpp_f32<0x141>(a);
+    a = a + dpp_f32<0x140>(a);
+    return a;
+}
+
+// Maximum over the wave (every lane receives it).
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    v = fmaxf(v, dpp_f32<0x142, 0xA>(v));
+    v = fmaxf(v, dpp_f32<0x143, 0xC>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// wave_topk_gates for n <= 64 entries (entry i in lane i), without LDS round
+// trips: each entry's rank under (value desc, id asc) is the count of
+// entries ahead of it, from wave-uniform reads of every entry; the entries
+// of rank 0 .. k-1 are the selection in order, and the gates take the same
+// float32 operations in the same order (the denominator summed over ranks
+// 0 .. k-1).  The whole wave must be active; k <= n.
+__device__ __forceinline__ void wave_topk_gates_small(const float *vals, const int32_t *idmap,
+                                                      int n, int64_t k, int lane,
+                                                      int32_t *ids_row, float *gates_row) {
+    const bool have = lane < n;
+    const float v = have ? vals[lane] : -__builtin_inff();
+    const int32_t e = have ? (idmap ? idmap[lane] : lane) : 0x7FFFFFFF;
+    int rank = 0;
+    for (int i = 0; i < n; ++i) {
+        const float vi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), i));
+        const int32_t ei = __builtin_amdgcn_readlane(e, i);
+        rank += (vi > v || (vi == v && ei < e)) ? 1 : 0;
+    }
+    const bool sel = have && rank < k;
+    const int l0 = __builtin_ctzll(__ballot(have && rank == 0));
+    const float first = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l0));
+    const float ej = sel ? expf(v - first) : 0.0f;
+    float denom = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        const int lj = __builtin_ctzll(__ballot(have && rank == (int)j));
+        denom += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), lj));
+    }
+    if (sel) {
+        ids_row[rank] = e;
+        gates_row[rank] = ej / denom;
+    }
+}
+
 // The chunk chains of NJ candidates over pieces lo .. lo + n - 1 of this
 // lane's chunk (acc[j] += x_i * w_j,i, i ascending).  rw = buffer over the
 // re-laid-out W_r; vo[j] = byte offset of candidate j's first 16-byte piece
@@ -933,29 +1002,27 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
         }
     }
     if (BOUNDS) return;
-    // Lk = k-th largest lower bound (k rounds of a wave max)
+    // Lk = k-th largest lower bound: k rounds of a wave max, each removing one
+    // instance of the maximum (the value does not depend on which)
     uint32_t taken = 0;
     float Lk = -__builtin_inff();
     for (int64_t j = 0; j < k; ++j) {
         float bv = -__builtin_inff();
-        int bs = -1;
 #pragma unroll
         for (int r2 = 0; r2 < RMAX; ++r2)
-            if (!(taken & (1u << r2)) && r2 * 64 + lane < E && (bs < 0 || lo[r2] > bv)) {
-                bv = lo[r2];
-                bs = r2 * 64 + lane;
-            }
+            if (!(taken & (1u << r2)) && r2 * 64 + lane < E) bv = fmaxf(bv, lo[r2]);
+        const float m = wave_max_f32(bv);
+        const int owner = __builtin_ctzll(__ballot(bv == m));
+        if (lane == owner) {
+            bool done = false;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(bv, m, 64);
-            const int os = __shfl_xor(bs, m, 64);
-            if (os >= 0 && (bs < 0 || ov > bv || (ov == bv && os < bs))) {
-                bv = ov;
-                bs = os;
-            }
+            for (int r2 = 0; r2 < RMAX; ++r2)
+                if (!done && !(taken & (1u << r2)) && r2 * 64 + lane < E && lo[r2] == m) {
+                    taken |= 1u << r2;
+                    done = true;
+                }
         }
-        if (bs >= 0 && (bs & 63) == lane) taken |= 1u << (bs >> 6);
-        Lk = bv;
+        Lk = m;
     }
     // candidates: upper bound >= Lk, compacted in ascending expert order
     int ns = 0;
@@ -1027,8 +1094,7 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) acc[j] = acc[j] + __shfl_xor(acc[j], m, 64);
+            if (j < nj) acc[j] = row16_tree_sum(acc[j]);  // nj wave-uniform
             const int ci = b + g + 4 * j;
             if (c == 0 && j < nj && ci < ns) {
                 float l = acc[j];
@@ -1040,7 +1106,10 @@ __global__ __launch_bounds__(64 * RF_WAVES) void route_refine_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    wave_topk_gates(exact, cand, ns, k, lane, ids + t * k, gates + t * k);
+    if (ns <= 64)
+        wave_topk_gates_small(exact, cand, ns, k, lane, ids + t * k, gates + t * k);
+    else
+        wave_topk_gates(exact, cand, ns, k, lane, ids + t * k, gates + t * k);
 }
 
 template <int TPT, int EPT>
