@@ -357,11 +357,14 @@ def test_fused_visibility_poisoned_workspace_alternating_inputs(name, hot):
         assert torch.equal(out.view(torch.int16), staged.view(torch.int16)), "fused != staged"
 
 
-@pytest.mark.parametrize("pattern", ["duplicated_rows", "all_equal", "scaled_copies"])
+@pytest.mark.parametrize("pattern", ["duplicated_rows", "all_equal", "scaled_copies",
+                                     "block_equal"])
 def test_router_fast_path_on_constructed_ties(pattern):
     # Router weights built so that logits tie exactly (duplicated expert rows),
-    # all tie (identical rows: every expert is a candidate), or sit at the
-    # tolerance edge (rows that are exact power-of-two multiples of others):
+    # all tie (identical rows: every expert is a candidate), sit at the
+    # tolerance edge (rows that are exact power-of-two multiples of others),
+    # or tie in a block of 40 (a token that ranks that row among its top k has
+    # 40 or more candidates: several candidate batches, selected by rank):
     # the fast path must still return the exact-order selection and gates.
     cfg = W.CONFIGS["tiny"].scaled(name=f"ties_{pattern}", T=257, d=512, f=128, E=96, k=6,
                                    seed=16)
@@ -371,6 +374,8 @@ def test_router_fast_path_on_constructed_ties(pattern):
         wr[1::2] = wr[0::2]
     elif pattern == "all_equal":
         wr[:] = wr[0]
+    elif pattern == "block_equal":
+        wr[:40] = wr[0]
     else:
         wr[48:] = wr[:48] * 2.0
     arrs["w_router"] = W.f32_to_bf16_bits(wr.astype(np.float32))
@@ -385,11 +390,14 @@ def test_router_fast_path_on_constructed_ties(pattern):
 # fewer than 16 waves per CU): windows of 16 and 18 pieces (d = 4352), of 16
 # (d = 4096, duplicated expert rows: exact ties), and every expert a
 # candidate at d = 7168 (all rows equal), so each batch of 16 candidates
-# stages both windows again.
+# stages both windows again; and a block of 40 equal rows at d = 7168 (40 to
+# 64 candidates where the block ranks high: several batches, each staging
+# both windows, selected by rank).
 TWO_WINDOW_ROUTER = {
     "d4352_e256": dict(T=300, d=4352, E=256, k=8, pattern=None),
     "d4096_e256_duplicated": dict(T=200, d=4096, E=256, k=6, pattern="duplicated_rows"),
     "d7168_e256_all_equal": dict(T=129, d=7168, E=256, k=8, pattern="all_equal"),
+    "d7168_e256_block_equal": dict(T=257, d=7168, E=256, k=8, pattern="block_equal"),
 }
 
 
@@ -404,6 +412,8 @@ def test_router_two_window_staging(name):
         wr = W.bf16_bits_to_f32(arrs["w_router"]).reshape(cfg.E, cfg.d)
         if pattern == "duplicated_rows":
             wr[1::2] = wr[0::2]
+        elif pattern == "block_equal":
+            wr[:40] = wr[0]
         else:
             wr[:] = wr[0]
         arrs["w_router"] = W.f32_to_bf16_bits(wr.astype(np.float32))
